@@ -1,0 +1,161 @@
+"""Checks that tie the oracle to facts outside itself.
+
+Each ``pin_*`` takes the attention (or re-root) function under test and returns
+the worst deviation from something the oracle did not compute: torch's CPU
+``scaled_dot_product_attention`` in the causal and decode special cases,
+hand-derived golden sets, closed forms. ``test_oracle_pins.py`` runs them on the
+oracle; ``test_oracle_mutations.py`` runs them on oracles with a planted
+mistake and expects them to fail.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def load_golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def rand(rng, *shape):
+    return rng.standard_normal(shape)
+
+
+def sdpa_causal(q_seq, k_seq, v_seq):
+    """Causal self-attention over a whole sequence, by torch (fp64, CPU).
+
+    q_seq: [L, Hq, d]; k_seq, v_seq: [L, Hkv, d]. Returns [L, Hq, d].
+    """
+    q = torch.from_numpy(q_seq).permute(1, 0, 2)[None]
+    k = torch.from_numpy(k_seq).permute(1, 0, 2)[None]
+    v = torch.from_numpy(v_seq).permute(1, 0, 2)[None]
+    o = F.scaled_dot_product_attention(q, k, v, is_causal=True, enable_gqa=True)
+    return o[0].permute(1, 0, 2).numpy()
+
+
+def sdpa_full(q_rows, k_seq, v_seq):
+    """Unmasked attention of a few query rows over a key sequence, by torch.
+
+    q_rows: [n, Hq, d]; k_seq, v_seq: [L, Hkv, d].
+    """
+    q = torch.from_numpy(q_rows).permute(1, 0, 2)[None]
+    k = torch.from_numpy(k_seq).permute(1, 0, 2)[None]
+    v = torch.from_numpy(v_seq).permute(1, 0, 2)[None]
+    o = F.scaled_dot_product_attention(q, k, v, enable_gqa=True)
+    return o[0].permute(1, 0, 2).numpy()
+
+
+def chain_parent(n):
+    return [-1] + list(range(n - 1))
+
+
+def pin_chain_causal(attn, rng, prefix_len=37, n=9, hq=8, hkv=2, d=16):
+    """A chain tree is the tail of an ordinary causal sequence.
+
+    The tree tokens are the last ``n`` tokens of a sequence of length
+    ``prefix_len + n``; their outputs must equal torch's causal attention there.
+    """
+    L = prefix_len + n
+    q_seq = rand(rng, L, hq, d)
+    k_seq = rand(rng, L, hkv, d)
+    v_seq = rand(rng, L, hkv, d)
+    want = sdpa_causal(q_seq, k_seq, v_seq)[prefix_len:]
+    cap = L + 5
+    k = np.full((hkv, cap, d), np.nan)
+    v = np.full((hkv, cap, d), np.nan)
+    k[:, :L] = k_seq.transpose(1, 0, 2)
+    v[:, :L] = v_seq.transpose(1, 0, 2)
+    got = attn(q_seq[prefix_len:], k, v, prefix_len, chain_parent(n), hkv)
+    return float(np.abs(got - want).max())
+
+
+def pin_root_only_decode(attn, rng, prefix_len=50, hq=4, hkv=4, d=32):
+    """A single node under the virtual root is plain one-token decode attention."""
+    L = prefix_len + 1
+    q = rand(rng, 1, hq, d)
+    k_seq = rand(rng, L, hkv, d)
+    v_seq = rand(rng, L, hkv, d)
+    want = sdpa_full(q, k_seq, v_seq)
+    got = attn(q, k_seq.transpose(1, 0, 2).copy(), v_seq.transpose(1, 0, 2).copy(),
+               prefix_len, [-1], hkv)
+    return float(np.abs(got - want).max())
+
+
+def pin_golden_uniform(attn, rng, prefix_len=6, hq=2, hkv=1, d=8):
+    """With zero queries every visible key weighs the same, so each output is the
+    plain mean of the visible value rows; the visible sets come from the
+    hand-derived golden file."""
+    worst = 0.0
+    for case in load_golden("mask_visible_sets.json")["cases"]:
+        parent = case["parent"]
+        n = len(parent)
+        cap = prefix_len + n + 3
+        k = rand(rng, hkv, cap, d)
+        v = rand(rng, hkv, cap, d)
+        k[:, prefix_len + n:] = np.nan
+        v[:, prefix_len + n:] = np.nan
+        q = np.zeros((n, hq, d))
+        got = attn(q, k, v, prefix_len, parent, hkv)
+        for i, vis in enumerate(case["visible"]):
+            rows = list(range(prefix_len)) + [prefix_len + j for j in vis]
+            for h in range(hq):
+                want = v[h // (hq // hkv), rows].mean(axis=0)
+                worst = max(worst, float(np.abs(got[i, h] - want).max()))
+    return worst
+
+
+def pin_path_reroot_causal(attn, reroot, parent, x, rng, prefix_len=5, hq=4, hkv=2, d=8):
+    """Node ``x`` of any tree sees exactly what the last token of a causal
+    sequence sees once its root path has been moved into the prefix.
+
+    The root path of ``x`` is found here by its own walk; the re-root (a pure
+    gather) lays the path out as prefix rows; torch's causal attention over that
+    new prefix then gives ``x``'s output at the last position.
+    """
+    n = len(parent)
+    path = [x]
+    while parent[path[-1]] != -1:
+        path.append(parent[path[-1]])
+    path.reverse()
+    cap = prefix_len + n + 2
+    k = rand(rng, 1, hkv, cap, d)
+    v = rand(rng, 1, hkv, cap, d)
+    q = rand(rng, n, hq, d)
+    got = attn(q, k[0], v[0], prefix_len, parent, hkv)[x]
+    k2, v2, new_p, _ = reroot(k, v, prefix_len, parent, path, [])
+    L = new_p
+    q_seq = np.zeros((L, hq, d))
+    q_seq[-1] = q[x]
+    want = sdpa_causal(q_seq, k2[0, :, :L].transpose(1, 0, 2).copy(),
+                       v2[0, :, :L].transpose(1, 0, 2).copy())[-1]
+    return float(np.abs(got - want).max())
+
+
+def pin_reroot_golden(plan):
+    """Hand-worked re-root cases: returns the number of mismatching cases.
+
+    ``plan(prefix_len, parent, path, survivors, capacity)`` returns
+    ``(order, new_prefix_len, new_parent)``.
+    """
+    bad = 0
+    for case in load_golden("reroot_cases.json")["cases"]:
+        cap = case["prefix_len"] + len(case["parent"])
+        order, new_p, new_par = plan(case["prefix_len"], case["parent"], case["path"],
+                                     case["survivors"], cap)
+        src = [case["prefix_len"] + o for o in order]
+        dst = [case["prefix_len"] + k for k in range(len(order))]
+        if (list(order) != case["order"] or src != case["src_slots"] or dst != case["dst_slots"]
+                or new_p != case["new_prefix_len"] or list(new_par) != case["new_parent"]):
+            bad += 1
+    return bad
+
+
+def scale_of(d):
+    return 1.0 / math.sqrt(d)

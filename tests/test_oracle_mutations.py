@@ -1,0 +1,156 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check a pin catches each.
+
+A pin that cannot tell a correct oracle from a broken one pins nothing. Each
+mutant below is the oracle with one realistic slip; the test asserts that at
+least one pin reports an error far above its tolerance.
+"""
+
+import importlib
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from tests import pins
+
+attn_mod = importlib.import_module("oracle.tree_attn_ref")
+reroot_mod = importlib.import_module("oracle.kv_reroot_ref")
+
+
+def attention_pins(attn):
+    rng = np.random.default_rng(5)
+    errs = [
+        pins.pin_chain_causal(attn, rng),
+        pins.pin_root_only_decode(attn, rng),
+        pins.pin_golden_uniform(attn, rng),
+    ]
+    for parent in ([-1, 0, 0, 1, -1, 4, 3], [-1, -1, 1, 2]):
+        for x in range(len(parent)):
+            errs.append(pins.pin_path_reroot_causal(attn, oracle.kv_reroot_ref, parent, x, rng))
+    return max(errs)
+
+
+def test_unmutated_oracle_passes_every_pin():
+    assert attention_pins(oracle.tree_attn_ref) < 1e-12
+    assert attention_pins(oracle.tree_attn_dense_ref) < 1e-12
+
+
+def _no_self(parent, i):
+    return [a for a in _orig_anc(parent, i) if a != i]
+
+
+def _stop_below_root(parent, i):
+    chain = _orig_anc(parent, i)
+    return chain[1:] if len(chain) > 1 else chain
+
+
+def _with_parent_of_parent_only(parent, i):
+    # skips every other ancestor
+    return [a for k, a in enumerate(reversed(_orig_anc(parent, i))) if k % 2 == 0]
+
+
+_orig_anc = attn_mod.ancestors_inclusive
+
+
+@pytest.mark.parametrize("bad", [_no_self, _stop_below_root, _with_parent_of_parent_only])
+def test_wrong_ancestor_walk_is_caught(monkeypatch, bad):
+    monkeypatch.setattr(attn_mod, "ancestors_inclusive", bad)
+    assert attention_pins(oracle.tree_attn_ref) > 1e-3
+
+
+def test_visibility_without_diagonal_is_caught(monkeypatch):
+    orig = attn_mod.visibility_matrix
+
+    def bad(parent):
+        m = orig(parent).copy()
+        np.fill_diagonal(m, False)
+        return m
+    monkeypatch.setattr(attn_mod, "visibility_matrix", bad)
+    with np.errstate(invalid="ignore"):
+        err = attention_pins(oracle.tree_attn_dense_ref)
+    assert not err < 1e-3
+
+
+def test_visibility_one_step_only_is_caught(monkeypatch):
+    """Forgetting the transitive closure leaves only parent and self visible."""
+    def bad(parent):
+        n = len(parent)
+        m = np.eye(n, dtype=bool)
+        for i, p in enumerate(parent):
+            if p >= 0:
+                m[i, p] = True
+        return m
+    monkeypatch.setattr(attn_mod, "visibility_matrix", bad)
+    assert attention_pins(oracle.tree_attn_dense_ref) > 1e-3
+
+
+def test_missing_score_scale_is_caught():
+    def bad(q, k, v, P, parent, hkv):
+        return oracle.tree_attn_ref(np.asarray(q) * math.sqrt(np.shape(q)[-1]), k, v, P, parent, hkv)
+    assert attention_pins(bad) > 1e-3
+
+
+def test_wrong_gqa_head_mapping_is_caught():
+    def bad(q, k, v, P, parent, hkv):
+        hq = np.shape(q)[1]
+        idx = [h % hkv for h in range(hq)]
+        return oracle.tree_attn_ref(q, np.asarray(k)[idx], np.asarray(v)[idx], P, parent, hq)
+    assert attention_pins(bad) > 1e-3
+
+
+def test_swapped_key_and_value_is_caught():
+    def bad(q, k, v, P, parent, hkv):
+        return oracle.tree_attn_ref(q, v, k, P, parent, hkv)
+    assert attention_pins(bad) > 1e-3
+
+
+def test_prefix_off_by_one_is_caught():
+    """Dropping the last prefix key (a range bound slip)."""
+    def bad(q, k, v, P, parent, hkv):
+        q = np.asarray(q, dtype=np.float64)
+        n, hq, d = q.shape
+        out = np.empty_like(q)
+        for i in range(n):
+            keys = list(range(max(P - 1, 0))) + [P + j for j in oracle.ancestors_inclusive(parent, i)]
+            for h in range(hq):
+                g = h // (hq // hkv)
+                s = np.asarray(k)[g, keys] @ q[i, h] / math.sqrt(d)
+                w = np.exp(s - s.max())
+                out[i, h] = w @ np.asarray(v)[g, keys] / w.sum()
+        return out
+    assert attention_pins(bad) > 1e-3
+
+
+def test_reroot_plan_slips_are_caught(monkeypatch):
+    assert pins.pin_reroot_golden(oracle.reroot_plan_ref) == 0
+    orig = reroot_mod.reroot_plan_ref
+
+    def parent_off_by_one(*a):
+        order, p, par = orig(*a)
+        return order, p, [x + 1 if x >= 0 else x for x in par]
+
+    def survivors_reversed(*a):
+        order, p, par = orig(*a)
+        m = p - a[0]
+        return order[:m] + order[m:][::-1], p, par
+
+    def path_not_in_prefix(*a):
+        order, p, par = orig(*a)
+        return order, a[0], par
+
+    for bad in (parent_off_by_one, survivors_reversed, path_not_in_prefix):
+        assert pins.pin_reroot_golden(bad) > 0
+
+
+def test_reroot_gather_slip_is_caught(monkeypatch):
+    """A gather that leaves the accepted path where it was breaks the causal pin."""
+    def bad_reroot(k, v, P, parent, path, surv):
+        k2, v2, new_p, new_par = oracle.kv_reroot_ref(k, v, P, parent, path, surv)
+        k2[:, :, P] = k[:, :, P]
+        v2[:, :, P] = v[:, :, P]
+        return k2, v2, new_p, new_par
+    rng = np.random.default_rng(9)
+    parent = [-1, -1, 1, 2]
+    errs = [pins.pin_path_reroot_causal(oracle.tree_attn_ref, bad_reroot, parent, x, rng) for x in range(4)]
+    assert max(errs) > 1e-3
