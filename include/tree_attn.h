@@ -1,0 +1,162 @@
+/*
+ * tree_attn.h — C ABI of the MI355X (gfx950) tree-attention library.
+ *
+ * Two device operations sit behind this header:
+ *
+ *   ta_tree_attn  tree-masked attention of a token tree against a KV cache
+ *                 laid out as [verified prefix | tree tokens];
+ *   ta_kv_reroot  re-root of that cache after verification: the accepted
+ *                 path joins the prefix and the surviving subtree is packed
+ *                 contiguously right after it.
+ *
+ * Source: SwiftSpec (arXiv 2506.11309), Pith review page, sections
+ * "What carries the argument" (prefix/tree cache invariant, re-root at the
+ * last verified token, mask attention kernel without explicit barriers) and
+ * "Core claim" (verified tokens move into the prefix cache; surviving tree
+ * states are reorganised contiguously after it).
+ *
+ * Conventions shared by every entry point:
+ *  - Plain C types only. No exception crosses this boundary.
+ *  - Device buffers are owned by the caller. The library never allocates,
+ *    frees or retains device memory, and never synchronises a stream.
+ *  - Host arrays are read only during the call.
+ *  - Every argument is validated before anything is enqueued. On error the
+ *    call enqueues nothing, leaves every output untouched, returns a status
+ *    and records a message readable through ta_last_error() (per thread).
+ *  - Launch failures return TA_ERR_DEVICE. A fault inside a kernel surfaces,
+ *    as usual for HIP, at the caller's next synchronisation.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ */
+#ifndef TREE_ATTN_H
+#define TREE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TA_ABI_VERSION 1
+#define TA_MAX_TREE 64 /* nodes per call: one 64-bit ancestor word per node */
+
+typedef enum {
+  TA_OK = 0,
+  TA_ERR_ARG = 1,         /* null pointer, negative size, misalignment, bad workspace */
+  TA_ERR_UNSUPPORTED = 2, /* dtype/head_dim/head ratio/tree size outside the built kernels */
+  TA_ERR_CAPACITY = 3,    /* prefix_len + n_tree exceeds the cache capacity */
+  TA_ERR_TREE = 4,        /* malformed parent array, path or survivor list */
+  TA_ERR_DEVICE = 5       /* a HIP runtime call failed */
+} ta_status;
+
+typedef enum { TA_F32 = 0, TA_BF16 = 1 } ta_dtype;
+
+/*
+ * One model's KV cache (caller-owned device memory).
+ * k and v are each dense [n_layers][n_kv_heads][capacity][head_dim] arrays of
+ * `dtype`, 16-byte aligned. Slot t < prefix_len holds verified token t; slot
+ * prefix_len + j holds tree node j.
+ */
+typedef struct {
+  void* k;
+  void* v;
+  int32_t n_layers;
+  int32_t n_kv_heads;
+  int32_t capacity;
+  int32_t head_dim; /* 64 or 128 */
+  int32_t dtype;    /* ta_dtype */
+} ta_kv_cache;
+
+/*
+ * Bytes of device workspace ta_tree_attn needs for this shape (0 if none).
+ * The workspace carries split-softmax partial results and the hand-off
+ * counters of the cross-workgroup combine. The counters always occupy the
+ * first 16 KiB, whatever the shape; that region must be zero-filled once
+ * before the first use, and every completed call leaves it zero again, so one
+ * workspace can serve calls of any shapes in sequence with no clearing. One
+ * workspace must not be used by two calls that can run at the same time (two
+ * streams, or graph replays that overlap). Returns 0 and records an error
+ * message if the shape is invalid.
+ */
+size_t ta_tree_attn_workspace_bytes(const ta_kv_cache* cache, int32_t n_q_heads,
+                                    int32_t prefix_len, int32_t n_tree);
+
+/*
+ * Tree-masked attention of one layer.
+ *
+ * For tree node i and query head h (KV head g = h / (n_q_heads/n_kv_heads)):
+ *   s_t = <q[i][h], K[layer][g][t]> / sqrt(head_dim)
+ * over the visible slots t: every prefix slot 0..prefix_len-1 and the slots
+ * prefix_len + j of every tree node j that is i itself or an ancestor of i
+ * (parent[j] = -1 hangs j off the last prefix token). out[i][h] is the
+ * softmax(s)-weighted sum of V[layer][g][t], accumulated in fp32. Slots at or
+ * beyond prefix_len + n_tree are never read.
+ *
+ *  q       device, [n_tree][n_q_heads][head_dim] of cache->dtype, 16-B aligned
+ *  parent  host, n_tree entries, parent[i] in {-1} U [0, i)
+ *  out     device, like q (bf16 results are rounded to nearest even)
+ *  workspace / workspace_bytes: device, >= ta_tree_attn_workspace_bytes(..)
+ *          (may be NULL when that is 0); see above for its contract.
+ * Limits: 1 <= n_tree <= TA_MAX_TREE (n_tree == 0 is a no-op returning TA_OK),
+ * head_dim in {64, 128}, n_q_heads a multiple of n_kv_heads with ratio <= 16,
+ * prefix_len >= 0, prefix_len + n_tree <= capacity.
+ */
+ta_status ta_tree_attn(const void* q, const ta_kv_cache* cache, int32_t layer,
+                       int32_t prefix_len, const int32_t* parent, int32_t n_tree,
+                       int32_t n_q_heads, void* out, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/*
+ * Re-root every layer of the cache after a verification step.
+ *
+ *  accepted_path    host, n_accepted >= 0 nodes from a first-level node
+ *                   (parent -1) downward: parent[a_k] = a_{k-1}
+ *  surviving_nodes  host, n_surviving >= 0 nodes, strictly ascending, disjoint
+ *                   from the path, closed under parent, with tops hanging off
+ *                   the last accepted node (off -1 when n_accepted == 0)
+ *  new_parent       host out, n_surviving entries: the survivors' tree in its
+ *                   new numbering (-1 under the new last prefix token)
+ *  new_prefix_len   host out: prefix_len + n_accepted
+ *
+ * Row prefix_len + k of every layer, KV head, K and V receives old row
+ * prefix_len + order[k], order = accepted_path ++ surviving_nodes; all other
+ * rows keep their bytes. The host outputs are final on return; the row moves
+ * are enqueued on `stream` and are bit-exact.
+ */
+ta_status ta_kv_reroot(const ta_kv_cache* cache, int32_t prefix_len,
+                       const int32_t* parent, int32_t n_tree,
+                       const int32_t* accepted_path, int32_t n_accepted,
+                       const int32_t* surviving_nodes, int32_t n_surviving,
+                       int32_t* new_parent, int32_t* new_prefix_len, void* stream);
+
+/*
+ * Host-only planning steps of the two calls above (no device work; usable
+ * without a GPU).
+ *
+ * ta_tree_ancestor_bits: bits_out[i] has bit j set iff node j is i itself or
+ * an ancestor of i. Validates parent like ta_tree_attn.
+ *
+ * ta_kv_reroot_plan: validates a re-root request exactly like ta_kv_reroot and
+ * writes src_rows_out[k] = prefix_len + order[k] for k < n_accepted +
+ * n_surviving (the source slot of destination slot prefix_len + k), plus
+ * new_parent and new_prefix_len as ta_kv_reroot would.
+ */
+ta_status ta_tree_ancestor_bits(const int32_t* parent, int32_t n_tree, uint64_t* bits_out);
+ta_status ta_kv_reroot_plan(int32_t prefix_len, int32_t capacity, const int32_t* parent,
+                            int32_t n_tree, const int32_t* accepted_path, int32_t n_accepted,
+                            const int32_t* surviving_nodes, int32_t n_surviving,
+                            int32_t* src_rows_out, int32_t* new_parent, int32_t* new_prefix_len);
+
+/* Number of prefix splits ta_tree_attn uses for this shape (>= 1); 0 on invalid shape. */
+int32_t ta_tree_attn_num_splits(const ta_kv_cache* cache, int32_t n_q_heads,
+                                int32_t prefix_len, int32_t n_tree);
+
+const char* ta_status_string(ta_status status);
+const char* ta_last_error(void);
+int32_t ta_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TREE_ATTN_H */

@@ -1,0 +1,227 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU fp64 oracle.
+
+Tolerances: fp32 max-abs <= 1e-5; bf16 (bf16 in, fp32 accumulate) max-abs <=
+1e-2 and, because those inputs give |out| of only ~1e-3, also
+max|out - ref| <= 2^-7 * max|ref| + 1e-6 (bf16 output rounding alone is
+2^-9 relative). Re-root must be byte-identical over the whole cache.
+"""
+
+import sys
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tree_masked_attention_attn_amd as ta
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def say(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def check_close(got, ref, dtype, what=""):
+    err = float(np.abs(got - ref).max())
+    scale = float(np.abs(ref).max())
+    if dtype == "f32":
+        assert err <= 1e-5, f"{what}: max-abs {err:.3g}"
+    else:
+        assert err <= 1e-2, f"{what}: max-abs {err:.3g}"
+        assert err <= 2.0 ** -7 * scale + 1e-6, f"{what}: max-abs {err:.3g} vs max|ref| {scale:.3g}"
+    assert np.isfinite(got).all()
+    return err
+
+
+def gpu_attn(x, layer=0):
+    q, k, v = x["q"].to(DEV), x["k"].to(DEV), x["v"].to(DEV)
+    out = ta.tree_attn(q, k, v, x["prefix_len"], x["parent"], layer=layer)
+    torch.cuda.synchronize()
+    return W.to_f64(out)
+
+
+def ref_attn(x, hkv, layer=0, dense=True):
+    f = oracle.tree_attn_dense_ref if dense else oracle.tree_attn_ref
+    return f(W.to_f64(x["q"]), W.to_f64(x["k"][layer]), W.to_f64(x["v"][layer]),
+             x["prefix_len"], x["parent"], hkv)
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "llama3_8b_verify", "llama3_70b_verify", "qwen2_72b_32k_verify"])
+def test_config_parity(name):
+    cfg = W.config(name)
+    say(f"[parity] {name} seed={cfg['seed']} P={cfg['prefix']} n={cfg['n_tree']} "
+        f"heads={cfg['n_q_heads']}/{cfg['n_kv_heads']} d={cfg['head_dim']} {cfg['dtype']}")
+    x = W.make_inputs(cfg)
+    got = gpu_attn(x)
+    ref = ref_attn(x, cfg["n_kv_heads"])
+    check_close(got, ref, cfg["dtype"], name)
+    # A few whole nodes once more through the one-(node, head)-at-a-time oracle.
+    n = cfg["n_tree"]
+    for i in sorted({0, 1, n // 2, n - 1}):
+        sub = dict(x, q=x["q"][: i + 1], parent=x["parent"][: i + 1])
+        one = ref_attn(sub, cfg["n_kv_heads"], dense=False)[i]
+        check_close(got[i], one, cfg["dtype"], f"{name} node {i}")
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "llama3_8b_verify", "llama3_70b_verify", "draft_loop_1b"])
+def test_mask_probe(name):
+    """Outputs that spell the visible set of every node: 1/|A| on A, ~0 elsewhere."""
+    cfg = W.config(name)
+    parent, _ = W.make_tree(cfg, np.random.default_rng(cfg["seed"]))
+    say(f"[mask-probe] {name}")
+    x = W.mask_probe_inputs(cfg, parent)
+    got = gpu_attn(x)
+    ref = ref_attn(x, cfg["n_kv_heads"])
+    check_close(got, ref, cfg["dtype"], name)
+    for i in range(len(parent)):
+        vis = oracle.ancestors_inclusive(parent, i)
+        want = np.zeros(cfg["head_dim"])
+        want[vis] = 1.0 / len(vis)
+        assert np.abs(got[i, :, :] - want).max() < 2e-2, i
+
+
+def test_peaked_softmax_unscaled_inputs():
+    cfg = W.config("llama3_8b_verify")
+    say("[peaked] 8B shape with N(0,1) inputs")
+    x = W.make_inputs(cfg, np.random.default_rng(77), value_scale=1.0)
+    check_close(gpu_attn(x), ref_attn(x, cfg["n_kv_heads"]), "bf16", "peaked")
+
+
+def edge_cases():
+    rng = np.random.default_rng(5)
+    rnd = lambda n: [-1] + [int(rng.integers(-1, i)) for i in range(1, n)]  # noqa: E731
+    return {
+        "root_only": (dict(n_q_heads=8, n_kv_heads=2, head_dim=128, dtype="bf16", prefix=100), [-1]),
+        "chain64_ragged": (dict(n_q_heads=8, n_kv_heads=2, head_dim=64, dtype="bf16", prefix=37),
+                           [-1] + list(range(63))),
+        "forest64_no_prefix": (dict(n_q_heads=8, n_kv_heads=2, head_dim=128, dtype="bf16", prefix=0), [-1] * 64),
+        "random_no_prefix": (dict(n_q_heads=4, n_kv_heads=4, head_dim=64, dtype="bf16", prefix=0), rnd(64)),
+        "prefix_one": (dict(n_q_heads=4, n_kv_heads=1, head_dim=128, dtype="bf16", prefix=1), rnd(40)),
+        "ragged_gqa3": (dict(n_q_heads=12, n_kv_heads=4, head_dim=128, dtype="bf16", prefix=1000), rnd(37)),
+        "gqa16": (dict(n_q_heads=16, n_kv_heads=1, head_dim=64, dtype="bf16", prefix=3000), rnd(64)),
+        "mha": (dict(n_q_heads=4, n_kv_heads=4, head_dim=128, dtype="bf16", prefix=5000), rnd(33)),
+        "f32_d128": (dict(n_q_heads=4, n_kv_heads=2, head_dim=128, dtype="f32", prefix=300), rnd(20)),
+        "f32_split": (dict(n_q_heads=8, n_kv_heads=1, head_dim=64, dtype="f32", prefix=5000), rnd(50)),
+        "f32_no_prefix": (dict(n_q_heads=2, n_kv_heads=1, head_dim=64, dtype="f32", prefix=0), rnd(64)),
+        "long_small_tree": (dict(n_q_heads=8, n_kv_heads=8, head_dim=64, dtype="bf16", prefix=60000), rnd(3)),
+    }
+
+
+@pytest.mark.parametrize("case", list(edge_cases()))
+def test_edge_shapes(case):
+    shape, parent = edge_cases()[case]
+    n = len(parent)
+    cfg = dict(shape, n_tree=n, capacity=shape["prefix"] + n + 40, seed=0,
+               value_scale=1.0 if shape["dtype"] == "f32" else 0.5, tree="given")
+    rng = np.random.default_rng(zlib.crc32(case.encode()))
+    say(f"[edge] {case} {shape} n={n}")
+    x = W.make_inputs(dict(cfg, tree="random"), rng)
+    x["parent"] = parent
+    check_close(gpu_attn(x), ref_attn(x, shape["n_kv_heads"]), shape["dtype"], case)
+
+
+def test_layer_selection_in_multilayer_cache():
+    cfg = W.config("llama3_8b_verify", prefix=700)
+    say("[layers] 3-layer cache, layer 2")
+    x = W.make_inputs(cfg, n_layers=3)
+    check_close(gpu_attn(x, layer=2), ref_attn(x, cfg["n_kv_heads"], layer=2), "bf16", "layer2")
+
+
+def test_repeat_calls_are_bitwise_identical_and_workspace_reusable():
+    cfg = W.config("llama3_70b_verify")
+    say("[determinism] 70B shape x3, then 8B shape, then 70B again")
+    x = W.make_inputs(cfg)
+    q, k, v = x["q"].to(DEV), x["k"].to(DEV), x["v"].to(DEV)
+    outs = [ta.tree_attn(q, k, v, x["prefix_len"], x["parent"]).clone() for _ in range(3)]
+    y = W.make_inputs(W.config("llama3_8b_verify"))
+    ta.tree_attn(y["q"].to(DEV), y["k"].to(DEV), y["v"].to(DEV), y["prefix_len"], y["parent"])
+    outs.append(ta.tree_attn(q, k, v, x["prefix_len"], x["parent"]))
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+
+
+def test_bad_calls_raise_and_touch_nothing():
+    cfg = W.config("tiny_fp32")
+    x = W.make_inputs(cfg)
+    q, k, v = x["q"].to(DEV), x["k"].to(DEV), x["v"].to(DEV)
+    out = torch.full_like(q, 7.0)
+    with pytest.raises(ta.TreeAttnError):
+        ta.tree_attn(q, k, v, 250, x["parent"], out=out)            # capacity
+    with pytest.raises(ta.TreeAttnError):
+        ta.tree_attn(q, k, v, 128, [-1, 5] + [0] * 13, out=out)     # bad parent
+    torch.cuda.synchronize()
+    assert (out == 7.0).all()
+
+
+# ----------------------------------------------------------------------------- re-root
+
+def reroot_case(cfg, n_layers, rng, path, surv, parent):
+    x = W.make_inputs(cfg, rng, n_layers=n_layers, poison=False)
+    k, v = x["k"].to(DEV), x["v"].to(DEV)
+    k_bits, v_bits = W.raw_bits(x["k"]), W.raw_bits(x["v"])
+    say(f"[reroot] {cfg['name']} layers={n_layers} path={path} survivors={len(surv)}")
+    new_par, new_p = ta.kv_reroot(k, v, x["prefix_len"], parent, path, surv)
+    torch.cuda.synchronize()
+    k2, v2, want_p, want_par = oracle.kv_reroot_ref(k_bits, v_bits, x["prefix_len"], parent, path, surv)
+    assert new_p == want_p and new_par == want_par
+    assert np.array_equal(W.raw_bits(k), k2) and np.array_equal(W.raw_bits(v), v2)
+
+
+@pytest.mark.parametrize("n_layers", [1, 4])
+def test_reroot_tiny_root_to_leaf(n_layers):
+    cfg = W.config("tiny_fp32")
+    rng = np.random.default_rng(cfg["seed"])
+    parent = W.random_parent(rng, cfg["n_tree"])
+    path = W.random_path_from(rng, parent, 0)
+    reroot_case(cfg, n_layers, rng, path, [], parent)
+
+
+@pytest.mark.parametrize("name,n_layers", [("draft_loop_1b", 1), ("draft_loop_1b", 16),
+                                           ("llama3_8b_verify", 2), ("tiny_fp32", 3)])
+def test_reroot_random_paths_bit_exact(name, n_layers):
+    cfg = W.config(name)
+    rng = np.random.default_rng(1234 + n_layers)
+    for trial in range(4):
+        if cfg["tree"] == "top8":
+            parent, _ = W.top8_tree(rng)
+            path = W.draft_path(rng, parent)
+        else:
+            parent = W.random_parent(rng, cfg["n_tree"])
+            path = W.random_path_from(rng, parent, 0, max_len=int(rng.integers(1, 6)))
+        surv = W.descendants(parent, path[-1])
+        if trial == 3:
+            surv = [s for s in surv if parent[s] == path[-1]]  # prune to the first level
+        reroot_case(cfg, n_layers, rng, path, surv, parent)
+
+
+def test_reroot_nothing_accepted_and_target_side():
+    cfg = W.config("llama3_8b_verify")
+    rng = np.random.default_rng(8)
+    parent, _ = W.top8_tree(rng)
+    root = 3  # nothing accepted: keep the subtree of one first-level node
+    reroot_case(cfg, 1, rng, [], sorted([root] + W.descendants(parent, root)), parent)
+    path = W.draft_path(rng, parent)
+    reroot_case(cfg, 1, rng, path, [], parent)  # target side: accepted rows only
+
+
+def test_reroot_then_attend_equals_attend_on_gpu():
+    """The re-root invariant, measured on the GPU path itself."""
+    cfg = W.config("draft_loop_1b")
+    rng = np.random.default_rng(21)
+    x = W.make_inputs(cfg, rng, poison=False)
+    q, k, v = x["q"].to(DEV), x["k"].to(DEV), x["v"].to(DEV)
+    parent, P = x["parent"], x["prefix_len"]
+    before = ta.tree_attn(q, k, v, P, parent).clone()
+    path = W.draft_path(rng, parent)
+    surv = W.descendants(parent, path[-1])
+    say(f"[invariant] path={path} survivors={len(surv)}")
+    new_par, new_p = ta.kv_reroot(k, v, P, parent, path, surv)
+    if surv:
+        after = ta.tree_attn(q[surv].contiguous(), k, v, new_p, new_par)
+        torch.cuda.synchronize()
+        check_close(W.to_f64(after), W.to_f64(before[surv]), "bf16", "re-rooted survivors")

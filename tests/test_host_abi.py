@@ -1,0 +1,176 @@
+"""The C-ABI library on the CPU: exports, host planning, validation errors.
+
+No test here launches a kernel: every call either runs host-only code or fails
+validation before anything would be enqueued (fake device addresses below are
+never dereferenced).
+"""
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+import pytest
+from hypothesis import given, settings
+
+import oracle
+import tree_masked_attention_attn_amd as ta
+from tests import pins
+from tests.test_oracle_pins import reroot_requests
+
+FAKE = 1 << 40  # 16-byte aligned, never dereferenced
+
+
+def test_library_exports_every_declared_symbol():
+    names = ta.header_symbols()
+    assert len(names) >= 9
+    lib = ta.lib()
+    for name in names:
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", ta.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert set(names) <= exported
+    assert ta.lib().ta_abi_version() == 1
+
+
+def test_status_strings():
+    for s in range(6):
+        assert ta.lib().ta_status_string(s)
+
+
+def test_ancestor_bits_match_oracle_walk():
+    rng = np.random.default_rng(0)
+    trees = [c["parent"] for c in pins.load_golden("mask_visible_sets.json")["cases"]]
+    trees += [[-1] + [int(rng.integers(-1, i)) for i in range(1, n)] for n in (1, 2, 17, 63, 64)]
+    for parent in trees:
+        bits = ta.tree_ancestor_bits(parent)
+        for i, b in enumerate(bits):
+            assert [j for j in range(64) if (b >> j) & 1] == oracle.ancestors_inclusive(parent, i)
+
+
+def test_ancestor_bits_reject_bad_trees():
+    for bad, status in (([0], ta.TA_ERR_TREE), ([-1, 1], ta.TA_ERR_TREE), ([-1, 0, 5], ta.TA_ERR_TREE),
+                        ([-1] * 65, ta.TA_ERR_UNSUPPORTED)):
+        with pytest.raises(ta.TreeAttnError) as e:
+            ta.tree_ancestor_bits(bad)
+        assert e.value.status == status
+
+
+def test_reroot_plan_hand_worked_cases():
+    def plan(P, parent, path, surv, cap):
+        src, new_par, new_p = ta.kv_reroot_plan(P, cap, parent, path, surv)
+        return [s - P for s in src], new_p, new_par
+    assert pins.pin_reroot_golden(plan) == 0
+
+
+def test_reroot_plan_rejects_invalid_requests():
+    for case in pins.load_golden("reroot_cases.json")["invalid"]:
+        cap = case["prefix_len"] + len(case["parent"])
+        with pytest.raises(ta.TreeAttnError) as e:
+            ta.kv_reroot_plan(case["prefix_len"], cap, case["parent"], case["path"], case["survivors"])
+        assert e.value.status == ta.TA_ERR_TREE, case["name"]
+    with pytest.raises(ta.TreeAttnError) as e:
+        ta.kv_reroot_plan(10, 11, [-1, 0], [0], [1])
+    assert e.value.status == ta.TA_ERR_CAPACITY
+
+
+@settings(max_examples=300, deadline=None)
+@given(reroot_requests())
+def test_reroot_plan_matches_oracle(req):
+    P, parent, path, surv = req
+    cap = P + len(parent) + 1
+    order, new_p, new_par = oracle.reroot_plan_ref(P, parent, path, surv, cap)
+    src, new_par2, new_p2 = ta.kv_reroot_plan(P, cap, parent, path, surv)
+    assert src == [P + o for o in order] and new_par2 == new_par and new_p2 == new_p
+    # the properties the in-place copy relies on
+    assert all(s >= P + k for k, s in enumerate(src))
+    assert all(b > a for a, b in zip(src, src[1:]))
+
+
+def _desc(L=1, H=8, C=8448, D=128, dtype=ta.TA_BF16, k=FAKE, v=FAKE + (1 << 30)):
+    return ta.ta_kv_cache(k, v, L, H, C, D, dtype)
+
+
+def _attn(desc, n_q_heads=64, prefix=8192, parent=None, q=FAKE, out=FAKE, ws=None, ws_len=0, layer=0):
+    parent = [-1] * 8 if parent is None else parent
+    par, n = ta._i32(parent)
+    return ta.lib().ta_tree_attn(q, ctypes.byref(desc), layer, prefix, par, n, n_q_heads, out, ws, ws_len, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(desc=_desc(D=96)), ta.TA_ERR_UNSUPPORTED),
+    (dict(desc=_desc(dtype=7)), ta.TA_ERR_UNSUPPORTED),
+    (dict(desc=_desc(), n_q_heads=60), ta.TA_ERR_UNSUPPORTED),
+    (dict(desc=_desc(H=2), n_q_heads=64), ta.TA_ERR_UNSUPPORTED),   # 32 q heads per KV head
+    (dict(desc=_desc(), parent=[-1] * 65), ta.TA_ERR_UNSUPPORTED),
+    (dict(desc=_desc(), prefix=8448 - 7), ta.TA_ERR_CAPACITY),
+    (dict(desc=_desc(), prefix=-1), ta.TA_ERR_ARG),
+    (dict(desc=_desc(), parent=[-1, 1]), ta.TA_ERR_TREE),
+    (dict(desc=_desc(k=FAKE + 8)), ta.TA_ERR_ARG),
+    (dict(desc=_desc(k=0)), ta.TA_ERR_ARG),
+    (dict(desc=_desc(), q=FAKE + 4), ta.TA_ERR_ARG),
+    (dict(desc=_desc(), out=0), ta.TA_ERR_ARG),
+    (dict(desc=_desc(), layer=1), ta.TA_ERR_ARG),
+    (dict(desc=_desc(L=0)), ta.TA_ERR_ARG),
+    (dict(desc=_desc()), ta.TA_ERR_ARG),                 # needs a workspace, none given
+    (dict(desc=_desc(), ws=FAKE, ws_len=1024), ta.TA_ERR_ARG),
+])
+def test_tree_attn_rejects_before_enqueueing(kwargs, status):
+    assert _attn(**kwargs) == status
+    assert ta.lib().ta_last_error()
+
+
+def test_empty_tree_is_a_no_op():
+    assert _attn(_desc(), parent=[]) == ta.TA_OK
+
+
+def test_workspace_and_split_plan():
+    lib = ta.lib()
+    d = _desc()
+    assert lib.ta_tree_attn_num_splits(ctypes.byref(d), 64, 8192, 64) > 1
+    ws = lib.ta_tree_attn_workspace_bytes(ctypes.byref(d), 64, 8192, 64)
+    assert ws > 0 and ws % 256 == 0
+    tiny = _desc(H=1, C=256, D=64, dtype=ta.TA_F32)
+    assert lib.ta_tree_attn_num_splits(ctypes.byref(tiny), 2, 128, 15) == 1
+    assert lib.ta_tree_attn_workspace_bytes(ctypes.byref(tiny), 2, 128, 15) == 0
+    assert lib.ta_tree_attn_workspace_bytes(ctypes.byref(d), 60, 8192, 64) == 0  # invalid -> 0
+
+
+def test_kv_reroot_rejects_before_enqueueing():
+    lib = ta.lib()
+    np_out = (ctypes.c_int32 * 64)()
+    npl = ctypes.c_int32(-7)
+
+    def call(desc, P, parent, path, surv, new_parent=np_out, new_prefix=ctypes.byref(npl)):
+        par, n = ta._i32(parent)
+        a, m = ta._i32(path)
+        s, k = ta._i32(surv)
+        return lib.ta_kv_reroot(ctypes.byref(desc), P, par, n, a, m, s, k, new_parent, new_prefix, None)
+
+    d = _desc(C=100)
+    assert call(d, 0, [-1, 0, 0, 1], [0, 2, 3], []) == ta.TA_ERR_TREE
+    assert call(d, 0, [-1, 0, 0, 1], [0, 1], [2]) == ta.TA_ERR_TREE
+    assert call(d, 99, [-1, 0], [0], [1]) == ta.TA_ERR_CAPACITY
+    assert call(_desc(D=80), 0, [-1], [0], []) == ta.TA_ERR_UNSUPPORTED
+    assert call(_desc(v=0), 0, [-1], [0], []) == ta.TA_ERR_ARG
+    assert call(d, 0, [-1, 0], [0], [1], new_prefix=None) == ta.TA_ERR_ARG
+    assert npl.value == -7  # outputs untouched on error
+    # A valid request whose rows are already in place moves nothing: host-only.
+    assert call(d, 5, [-1, 0, 1], [0, 1], [2]) == ta.TA_OK
+    assert npl.value == 7 and np_out[0] == -1
+
+
+def test_package_refuses_to_run_without_the_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(ta, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(ta, "_lib", None)
+    with pytest.raises(RuntimeError, match="no CPU fallback"):
+        ta.tree_ancestor_bits([-1])
+
+
+def test_package_does_not_import_the_oracle():
+    pkg = os.path.dirname(ta.__file__)
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text

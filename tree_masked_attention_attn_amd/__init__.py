@@ -1,0 +1,223 @@
+"""Python binding of the MI355X tree-attention library (ctypes, no compute here).
+
+Every function marshals arguments and calls the C ABI in ``libtree_attn.so``
+(declared in ``include/tree_attn.h``). torch tensors are used only as device
+memory and for the current HIP stream. There is no CPU fallback: if the
+library has not been built, importing works but every call raises.
+
+    tree_attn(q, k_cache, v_cache, prefix_len, parent, layer=0, out=None)
+    kv_reroot(k_cache, v_cache, prefix_len, parent, accepted_path, surviving_nodes)
+    tree_attn_workspace_bytes / tree_attn_num_splits / tree_ancestor_bits / kv_reroot_plan
+
+Layouts: q and out ``[n_tree, n_q_heads, head_dim]``; caches
+``[n_layers, n_kv_heads, capacity, head_dim]``; all contiguous, same dtype
+(float32 or bfloat16), on the same GPU.
+"""
+
+import ctypes
+import os
+import re
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtree_attn.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "tree_attn.h")
+
+TA_OK, TA_ERR_ARG, TA_ERR_UNSUPPORTED, TA_ERR_CAPACITY, TA_ERR_TREE, TA_ERR_DEVICE = range(6)
+TA_F32, TA_BF16 = 0, 1
+MAX_TREE = 64
+
+
+class TreeAttnError(RuntimeError):
+    """A call into the library returned a non-OK status."""
+
+    def __init__(self, status, message):
+        super().__init__(f"[{status}] {message}")
+        self.status = status
+
+
+class ta_kv_cache(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("n_layers", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("capacity", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+_lib = None
+_lib_lock = threading.Lock()
+_I32P = ctypes.POINTER(ctypes.c_int32)
+_U64P = ctypes.POINTER(ctypes.c_uint64)
+_CP = ctypes.POINTER(ta_kv_cache)
+
+
+def lib():
+    """The loaded shared library; raises if it was never built."""
+    global _lib
+    with _lib_lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                                   "(there is no CPU fallback)")
+            L = ctypes.CDLL(LIB_PATH)
+            L.ta_abi_version.restype = ctypes.c_int32
+            L.ta_last_error.restype = ctypes.c_char_p
+            L.ta_status_string.restype = ctypes.c_char_p
+            L.ta_status_string.argtypes = [ctypes.c_int]
+            L.ta_tree_attn_workspace_bytes.restype = ctypes.c_size_t
+            L.ta_tree_attn_workspace_bytes.argtypes = [_CP, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+            L.ta_tree_attn_num_splits.restype = ctypes.c_int32
+            L.ta_tree_attn_num_splits.argtypes = [_CP, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+            L.ta_tree_attn.restype = ctypes.c_int
+            L.ta_tree_attn.argtypes = [ctypes.c_void_p, _CP, ctypes.c_int32, ctypes.c_int32, _I32P,
+                                       ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_size_t, ctypes.c_void_p]
+            L.ta_kv_reroot.restype = ctypes.c_int
+            L.ta_kv_reroot.argtypes = [_CP, ctypes.c_int32, _I32P, ctypes.c_int32, _I32P, ctypes.c_int32,
+                                       _I32P, ctypes.c_int32, _I32P, _I32P, ctypes.c_void_p]
+            L.ta_tree_ancestor_bits.restype = ctypes.c_int
+            L.ta_tree_ancestor_bits.argtypes = [_I32P, ctypes.c_int32, _U64P]
+            L.ta_kv_reroot_plan.restype = ctypes.c_int
+            L.ta_kv_reroot_plan.argtypes = [ctypes.c_int32, ctypes.c_int32, _I32P, ctypes.c_int32, _I32P,
+                                            ctypes.c_int32, _I32P, ctypes.c_int32, _I32P, _I32P, _I32P]
+            if L.ta_abi_version() != 1:
+                raise RuntimeError("libtree_attn.so ABI version mismatch")
+            _lib = L
+    return _lib
+
+
+def header_symbols():
+    """Names of the functions ``include/tree_attn.h`` declares."""
+    with open(HEADER) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"\b(ta_[a-z_]+)\s*\(", text)))
+
+
+def _check(status):
+    if status != TA_OK:
+        L = lib()
+        raise TreeAttnError(status, f"{L.ta_status_string(status).decode()}: {L.ta_last_error().decode()}")
+
+
+def _i32(seq):
+    seq = [int(x) for x in seq]
+    arr = (ctypes.c_int32 * max(len(seq), 1))(*seq)
+    return arr, len(seq)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return TA_F32
+    if t.dtype == torch.bfloat16:
+        return TA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _cache_desc(k_cache, v_cache, need_device=True):
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        if t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [n_layers, n_kv_heads, capacity, head_dim] tensor")
+        if need_device and not t.is_cuda:
+            raise ValueError(f"{name} must be on the GPU")
+    if k_cache.shape != v_cache.shape or k_cache.dtype != v_cache.dtype:
+        raise ValueError("k_cache and v_cache must match in shape and dtype")
+    L, H, C, D = k_cache.shape
+    return ta_kv_cache(k_cache.data_ptr(), v_cache.data_ptr(), L, H, C, D, _dtype_code(k_cache))
+
+
+def _stream_ptr(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+_workspaces = {}
+_ws_lock = threading.Lock()
+
+
+def _workspace(device, nbytes):
+    """A zero-filled workspace per device, grown on demand and kept for reuse.
+
+    The kernel leaves its counters at zero after every call, so reuse needs no
+    clearing; it does assume calls on one device are ordered (one stream).
+    """
+    if nbytes == 0:
+        return None
+    key = torch.device(device).index
+    with _ws_lock:
+        ws = _workspaces.get(key)
+        if ws is None or ws.numel() < nbytes:
+            ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+            _workspaces[key] = ws
+    return ws
+
+
+def tree_attn_workspace_bytes(k_cache, v_cache, n_q_heads, prefix_len, n_tree):
+    desc = _cache_desc(k_cache, v_cache, need_device=False)
+    return lib().ta_tree_attn_workspace_bytes(ctypes.byref(desc), n_q_heads, prefix_len, n_tree)
+
+
+def tree_attn_num_splits(k_cache, v_cache, n_q_heads, prefix_len, n_tree):
+    desc = _cache_desc(k_cache, v_cache, need_device=False)
+    return lib().ta_tree_attn_num_splits(ctypes.byref(desc), n_q_heads, prefix_len, n_tree)
+
+
+def tree_attn(q, k_cache, v_cache, prefix_len, parent, layer=0, out=None, workspace=None):
+    """Tree-masked attention of one layer; returns ``out`` (allocated if None).
+
+    ``parent`` is a host sequence of ints. The launch goes on torch's current
+    stream of q's device; nothing is synchronised.
+    """
+    if q.dim() != 3 or not q.is_contiguous() or not q.is_cuda:
+        raise ValueError("q must be a contiguous [n_tree, n_q_heads, head_dim] GPU tensor")
+    desc = _cache_desc(k_cache, v_cache)
+    if q.dtype != k_cache.dtype or q.device != k_cache.device:
+        raise ValueError("q must match the cache in dtype and device")
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() or out.device != q.device:
+        raise ValueError("out must be a contiguous tensor like q")
+    par, n = _i32(parent)
+    nbytes = lib().ta_tree_attn_workspace_bytes(ctypes.byref(desc), q.shape[1], prefix_len, n)
+    if workspace is None:
+        workspace = _workspace(q.device, nbytes)
+    ws_ptr = None if workspace is None else workspace.data_ptr()
+    ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().ta_tree_attn(q.data_ptr(), ctypes.byref(desc), layer, prefix_len, par, n, q.shape[1],
+                              out.data_ptr(), ws_ptr, ws_len, _stream_ptr(q.device)))
+    return out
+
+
+def kv_reroot(k_cache, v_cache, prefix_len, parent, accepted_path, surviving_nodes):
+    """Re-root every layer in place; returns ``(new_parent, new_prefix_len)``.
+
+    The row moves are enqueued on torch's current stream of the cache's device.
+    """
+    desc = _cache_desc(k_cache, v_cache)
+    par, n = _i32(parent)
+    path, m = _i32(accepted_path)
+    surv, ns = _i32(surviving_nodes)
+    new_par = (ctypes.c_int32 * max(ns, 1))()
+    new_p = ctypes.c_int32(0)
+    _check(lib().ta_kv_reroot(ctypes.byref(desc), prefix_len, par, n, path, m, surv, ns, new_par,
+                              ctypes.byref(new_p), _stream_ptr(k_cache.device)))
+    return [new_par[i] for i in range(ns)], new_p.value
+
+
+def tree_ancestor_bits(parent):
+    """Host-only: bit j of entry i is set iff node j is i or an ancestor of i."""
+    par, n = _i32(parent)
+    bits = (ctypes.c_uint64 * max(n, 1))()
+    _check(lib().ta_tree_ancestor_bits(par, n, bits))
+    return [bits[i] for i in range(n)]
+
+
+def kv_reroot_plan(prefix_len, capacity, parent, accepted_path, surviving_nodes):
+    """Host-only re-root plan: ``(src_rows, new_parent, new_prefix_len)``."""
+    par, n = _i32(parent)
+    path, m = _i32(accepted_path)
+    surv, ns = _i32(surviving_nodes)
+    src = (ctypes.c_int32 * max(m + ns, 1))()
+    new_par = (ctypes.c_int32 * max(ns, 1))()
+    new_p = ctypes.c_int32(0)
+    _check(lib().ta_kv_reroot_plan(prefix_len, capacity, par, n, path, m, surv, ns, src, new_par,
+                                   ctypes.byref(new_p)))
+    return [src[i] for i in range(m + ns)], [new_par[i] for i in range(ns)], new_p.value

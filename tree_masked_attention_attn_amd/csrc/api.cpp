@@ -1,0 +1,168 @@
+// extern "C" entry points declared in include/tree_attn.h.
+//
+// Each call validates everything on the host first (plan.cpp), so an invalid
+// call enqueues nothing and leaves its outputs untouched; only then are the
+// kernel arguments packed and the kernel launched on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <string>
+
+#include "launch.h"
+#include "plan.h"
+
+using namespace ta;
+
+namespace {
+
+ta_status device_error(hipError_t e, const char* what) {
+  return fail(TA_ERR_DEVICE, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t ta_abi_version(void) { return TA_ABI_VERSION; }
+
+const char* ta_last_error(void) { return last_error(); }
+
+const char* ta_status_string(ta_status s) {
+  switch (s) {
+    case TA_OK: return "ok";
+    case TA_ERR_ARG: return "invalid argument";
+    case TA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case TA_ERR_CAPACITY: return "cache capacity exceeded";
+    case TA_ERR_TREE: return "malformed tree, path or survivor list";
+    case TA_ERR_DEVICE: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+ta_status ta_tree_ancestor_bits(const int32_t* parent, int32_t n_tree, uint64_t* bits_out) {
+  clear_error();
+  return ancestor_bits(parent, n_tree, bits_out);
+}
+
+ta_status ta_kv_reroot_plan(int32_t prefix_len, int32_t capacity, const int32_t* parent,
+                            int32_t n_tree, const int32_t* accepted_path, int32_t n_accepted,
+                            const int32_t* surviving_nodes, int32_t n_surviving,
+                            int32_t* src_rows_out, int32_t* new_parent, int32_t* new_prefix_len) {
+  clear_error();
+  return plan_kv_reroot(prefix_len, capacity, parent, n_tree, accepted_path, n_accepted,
+                        surviving_nodes, n_surviving, src_rows_out, new_parent, new_prefix_len);
+}
+
+size_t ta_tree_attn_workspace_bytes(const ta_kv_cache* cache, int32_t n_q_heads,
+                                    int32_t prefix_len, int32_t n_tree) {
+  clear_error();
+  AttnPlan p;
+  if (plan_tree_attn(cache, n_q_heads, prefix_len, n_tree, &p) != TA_OK) return 0;
+  return p.ws_bytes;
+}
+
+int32_t ta_tree_attn_num_splits(const ta_kv_cache* cache, int32_t n_q_heads, int32_t prefix_len,
+                                int32_t n_tree) {
+  clear_error();
+  AttnPlan p;
+  if (plan_tree_attn(cache, n_q_heads, prefix_len, n_tree, &p) != TA_OK) return 0;
+  return p.splits > 0 ? p.splits : 1;
+}
+
+ta_status ta_tree_attn(const void* q, const ta_kv_cache* cache, int32_t layer,
+                       int32_t prefix_len, const int32_t* parent, int32_t n_tree,
+                       int32_t n_q_heads, void* out, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  clear_error();
+  ta_status st = check_cache(cache, true);
+  if (st != TA_OK) return st;
+  AttnPlan plan;
+  st = plan_tree_attn(cache, n_q_heads, prefix_len, n_tree, &plan);
+  if (st != TA_OK) return st;
+  if (layer < 0 || layer >= cache->n_layers) return fail(TA_ERR_ARG, "layer out of range");
+  TreeAttnArgs a;
+  std::memset(&a, 0, sizeof(a));
+  st = ancestor_bits(parent, n_tree, a.anc);
+  if (st != TA_OK) return st;
+  if (n_tree == 0) return TA_OK;
+  if (q == nullptr || out == nullptr) return fail(TA_ERR_ARG, "q or out is null");
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(out)) & 15)
+    return fail(TA_ERR_ARG, "q and out must be 16-byte aligned");
+  if (plan.ws_bytes > 0) {
+    if (workspace == nullptr || workspace_bytes < plan.ws_bytes)
+      return fail(TA_ERR_ARG, "workspace too small: need " + std::to_string(plan.ws_bytes) +
+                                  " bytes, got " + std::to_string(workspace_bytes));
+    if (reinterpret_cast<uintptr_t>(workspace) & 255)
+      return fail(TA_ERR_ARG, "workspace must be 256-byte aligned");
+  }
+  const size_t es = dtype_bytes(cache->dtype);
+  const int64_t head_stride = static_cast<int64_t>(cache->capacity) * cache->head_dim;
+  const size_t layer_bytes = static_cast<size_t>(cache->n_kv_heads) * head_stride * es;
+  char* ws = static_cast<char*>(workspace);
+  a.q = q;
+  a.k = static_cast<const char*>(cache->k) + layer * layer_bytes;
+  a.v = static_cast<const char*>(cache->v) + layer * layer_bytes;
+  a.out = out;
+  a.ws_o = plan.ws_bytes ? reinterpret_cast<float*>(ws + plan.ws_o_offset) : nullptr;
+  a.ws_ml = plan.ws_bytes ? reinterpret_cast<float2*>(ws + plan.ws_ml_offset) : nullptr;
+  a.ws_cnt = plan.ws_bytes ? reinterpret_cast<int32_t*>(ws + plan.ws_cnt_offset) : nullptr;
+  a.kv_head_stride = head_stride;
+  a.n_q_heads = n_q_heads;
+  a.group = plan.group;
+  a.n_tree = n_tree;
+  a.prefix_len = prefix_len;
+  a.total_keys = plan.total_keys;
+  a.rows_per_head = plan.rows_per_head;
+  a.row_blocks = plan.row_blocks;
+  a.splits = plan.splits;
+  a.n_tiles = plan.n_tiles;
+  a.n_units = plan.n_units;
+  a.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(cache->head_dim)));
+  hipError_t e = launch_tree_attn(a, cache->dtype, cache->head_dim, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_error(e, "tree_attn launch");
+  return TA_OK;
+}
+
+ta_status ta_kv_reroot(const ta_kv_cache* cache, int32_t prefix_len, const int32_t* parent,
+                       int32_t n_tree, const int32_t* accepted_path, int32_t n_accepted,
+                       const int32_t* surviving_nodes, int32_t n_surviving, int32_t* new_parent,
+                       int32_t* new_prefix_len, void* stream) {
+  clear_error();
+  ta_status st = check_cache(cache, true);
+  if (st != TA_OK) return st;
+  RerootArgs a;
+  std::memset(&a, 0, sizeof(a));
+  int32_t np_tmp[TA_MAX_TREE];
+  int32_t npl_tmp = 0;
+  st = plan_kv_reroot(prefix_len, cache->capacity, parent, n_tree, accepted_path, n_accepted,
+                      surviving_nodes, n_surviving, a.src, np_tmp, &npl_tmp);
+  if (st != TA_OK) return st;
+  if (new_prefix_len == nullptr || (n_surviving > 0 && new_parent == nullptr))
+    return fail(TA_ERR_ARG, "output pointer is null");
+  const int32_t rows = n_accepted + n_surviving;
+  bool moves = false;
+  for (int32_t k = 0; k < rows; ++k) moves |= a.src[k] != prefix_len + k;
+  if (moves) {
+    const size_t es = dtype_bytes(cache->dtype);
+    a.k = static_cast<char*>(cache->k);
+    a.v = static_cast<char*>(cache->v);
+    a.row_bytes = static_cast<int32_t>(cache->head_dim * es);
+    a.plane_bytes = static_cast<int64_t>(cache->capacity) * a.row_bytes;
+    a.n_planes = cache->n_layers * cache->n_kv_heads;
+    a.n_rows = rows;
+    a.dst0 = prefix_len;
+    // Columns per workgroup: enough that every thread has about one item.
+    const int32_t cols = a.row_bytes / 16;
+    int32_t gcols = cols;
+    while (gcols > 1 && rows * gcols > 256) gcols /= 2;
+    a.col_groups = cols / gcols;
+    hipError_t e = launch_kv_reroot(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return device_error(e, "kv_reroot launch");
+  }
+  for (int32_t k = 0; k < n_surviving; ++k) new_parent[k] = np_tmp[k];
+  *new_prefix_len = npl_tmp;
+  return TA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,51 @@
+// Kernel argument blocks and launchers shared by the C ABI (api.cpp) and the
+// HIP kernels. Everything here is passed to the device by value.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace ta {
+
+struct TreeAttnArgs {
+  const void* q;            // [n_tree][n_q_heads][D]
+  const void* k;            // layer base: [n_kv_heads][capacity][D]
+  const void* v;
+  void* out;                // like q
+  float* ws_o;              // split partials, see AttnPlan
+  float2* ws_ml;
+  int32_t* ws_cnt;
+  int64_t kv_head_stride;   // elements from one KV head to the next (capacity * D)
+  int32_t n_q_heads;
+  int32_t group;            // query heads per KV head
+  int32_t n_tree;
+  int32_t prefix_len;
+  int32_t total_keys;       // prefix_len + n_tree
+  int32_t rows_per_head;    // group * n_tree
+  int32_t row_blocks;
+  int32_t splits;
+  int32_t n_tiles;
+  int32_t n_units;
+  float scale_log2;         // log2(e) / sqrt(D)
+  uint64_t anc[64];         // ancestor-or-self bitset per tree node
+};
+
+hipError_t launch_tree_attn(const TreeAttnArgs& a, int32_t dtype, int32_t head_dim,
+                            hipStream_t stream);
+
+struct RerootArgs {
+  char* k;                  // cache base (all layers)
+  char* v;
+  int64_t plane_bytes;      // capacity * row_bytes: one (layer, KV head) plane
+  int32_t row_bytes;        // head_dim * element size
+  int32_t n_planes;         // n_layers * n_kv_heads
+  int32_t n_rows;           // rows to place: n_accepted + n_surviving
+  int32_t dst0;             // first destination slot (= prefix_len)
+  int32_t col_groups;       // column groups per plane (grid.y)
+  int32_t src[64];          // source slot of destination slot dst0 + k
+};
+
+hipError_t launch_kv_reroot(const RerootArgs& a, hipStream_t stream);
+
+}  // namespace ta

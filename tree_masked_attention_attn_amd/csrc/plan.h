@@ -1,0 +1,69 @@
+// Host-side validation and planning for the tree-attention library.
+// Plain C++ (no HIP): it is compiled into the library and also builds on its
+// own with g++ for sanitizer runs.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+
+#include "../../include/tree_attn.h"
+
+namespace ta {
+
+// Records `msg` as the calling thread's last error and returns `st`.
+ta_status fail(ta_status st, const std::string& msg);
+void clear_error();
+const char* last_error();
+
+// parent[i] in {-1} U [0, i) for every i < n.
+ta_status check_parent(const int32_t* parent, int32_t n);
+
+// bits[i] = bit i | bits[parent[i]] (root path of i, self included).
+ta_status ancestor_bits(const int32_t* parent, int32_t n, uint64_t* bits);
+
+// Validates a KV-cache descriptor (pointers may be null when `need_ptrs` is false).
+ta_status check_cache(const ta_kv_cache* c, bool need_ptrs);
+
+// Tiling of one ta_tree_attn call. A "work unit" is one workgroup:
+// (KV head g, block of kRowsPerBlock query rows, prefix split s).
+struct AttnPlan {
+  int32_t head_dim = 0;
+  int32_t group = 0;           // query heads per KV head
+  int32_t rows_per_head = 0;   // group * n_tree
+  int32_t row_blocks = 0;      // ceil(rows_per_head / kRowsPerBlock)
+  int32_t total_keys = 0;      // prefix_len + n_tree
+  int32_t n_tiles = 0;         // ceil(total_keys / kKeyTile)
+  int32_t splits = 0;          // key-range splits per row block
+  int32_t n_units = 0;         // n_kv_heads * row_blocks * splits
+  // Workspace layout (only when splits > 1). The arrival counters always sit
+  // at offset 0 in a fixed-size region, whatever the shape, so a workspace
+  // that calls of different shapes share never finds partial data of an
+  // earlier call where it expects a counter.
+  size_t ws_cnt_offset = 0;    // int32 arrival counters [n_kv_heads * row_blocks]
+  size_t ws_ml_offset = 0;     // fp32 (max, sum) pairs [units][kRowsPerBlock][2]
+  size_t ws_o_offset = 0;      // fp32 partial outputs [units][kRowsPerBlock][head_dim]
+  size_t ws_bytes = 0;
+};
+
+constexpr int32_t kKeyTile = 32;       // keys per staged K/V tile
+constexpr int32_t kWaves = 4;          // waves per workgroup
+constexpr int32_t kRowsPerWave = 32;   // query rows per wave (one 32-wide MFMA N tile)
+constexpr int32_t kRowsPerBlock = kWaves * kRowsPerWave;
+constexpr int32_t kTargetUnits = 512;  // 2 workgroups per CU on a 256-CU part
+constexpr int32_t kMinTilesPerSplit = 4;
+constexpr int32_t kMaxGroups = 4096;   // counters in the fixed region: n_kv_heads * row_blocks
+constexpr size_t kCounterBytes = kMaxGroups * sizeof(int32_t);
+
+ta_status plan_tree_attn(const ta_kv_cache* cache, int32_t n_q_heads, int32_t prefix_len,
+                         int32_t n_tree, AttnPlan* plan);
+
+// Re-root plan: src_rows[k] = prefix_len + order[k], order = path ++ survivors.
+ta_status plan_kv_reroot(int32_t prefix_len, int32_t capacity, const int32_t* parent,
+                         int32_t n_tree, const int32_t* path, int32_t n_path,
+                         const int32_t* surv, int32_t n_surv, int32_t* src_rows,
+                         int32_t* new_parent, int32_t* new_prefix_len);
+
+size_t dtype_bytes(int32_t dtype);
+
+}  // namespace ta

@@ -231,6 +231,14 @@ def to_f64(t):
     return t.detach().to("cpu", torch.float64).numpy()
 
 
+def bits_to_f64(bits):
+    """float64 values of stored words (uint16 = bf16, uint32 = fp32); exact."""
+    bits = np.asarray(bits)
+    if bits.dtype == np.uint16:
+        return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return bits.view(np.float32).astype(np.float64)
+
+
 def raw_bits(t):
     """The stored words of a cache tensor (uint16 for bf16, uint32 for fp32)."""
     t = t.detach().to("cpu").contiguous()
