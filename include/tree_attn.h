@@ -71,7 +71,7 @@ typedef struct {
  * Bytes of device workspace ta_tree_attn needs for this shape (0 if none).
  * The workspace carries split-softmax partial results and the hand-off
  * counters of the cross-workgroup combine. The counters always occupy the
- * first 16 KiB, whatever the shape; that region must be zero-filled once
+ * first 64 KiB, whatever the shape; that region must be zero-filled once
  * before the first use, and every completed call leaves it zero again, so one
  * workspace can serve calls of any shapes in sequence with no clearing. One
  * workspace must not be used by two calls that can run at the same time (two
@@ -146,6 +146,17 @@ ta_status ta_kv_reroot_plan(int32_t prefix_len, int32_t capacity, const int32_t*
                             int32_t n_tree, const int32_t* accepted_path, int32_t n_accepted,
                             const int32_t* surviving_nodes, int32_t n_surviving,
                             int32_t* src_rows_out, int32_t* new_parent, int32_t* new_prefix_len);
+
+/*
+ * How long a prefix split of ta_tree_attn waits for the other splits of its
+ * row block before leaving its share of the merge to the last split to
+ * arrive: `polls` polls of about 128 GPU cycles each (default 20000, about
+ * 1 ms). Results do not depend on it: when every split of a row block runs at
+ * once (the normal case on an otherwise idle GPU) each merges 1/splits of the
+ * rows; a split that stops waiting leaves its rows to the last arrival, which
+ * never waits. 0 disables waiting. Process-wide; applies to later calls.
+ */
+void ta_set_split_wait_limit(int32_t polls);
 
 /* Number of prefix splits ta_tree_attn uses for this shape (>= 1); 0 on invalid shape. */
 int32_t ta_tree_attn_num_splits(const ta_kv_cache* cache, int32_t n_q_heads,

@@ -75,6 +75,8 @@ def lib():
             L.ta_kv_reroot.restype = ctypes.c_int
             L.ta_kv_reroot.argtypes = [_CP, ctypes.c_int32, _I32P, ctypes.c_int32, _I32P, ctypes.c_int32,
                                        _I32P, ctypes.c_int32, _I32P, _I32P, ctypes.c_void_p]
+            L.ta_set_split_wait_limit.restype = None
+            L.ta_set_split_wait_limit.argtypes = [ctypes.c_int32]
             L.ta_tree_ancestor_bits.restype = ctypes.c_int
             L.ta_tree_ancestor_bits.argtypes = [_I32P, ctypes.c_int32, _U64P]
             L.ta_kv_reroot_plan.restype = ctypes.c_int
@@ -200,6 +202,11 @@ def kv_reroot(k_cache, v_cache, prefix_len, parent, accepted_path, surviving_nod
     _check(lib().ta_kv_reroot(ctypes.byref(desc), prefix_len, par, n, path, m, surv, ns, new_par,
                               ctypes.byref(new_p), _stream_ptr(k_cache.device)))
     return [new_par[i] for i in range(ns)], new_p.value
+
+
+def set_split_wait_limit(polls):
+    """Bound (in polls of ~128 GPU cycles) of the wait between prefix splits."""
+    lib().ta_set_split_wait_limit(int(polls))
 
 
 def tree_ancestor_bits(parent):

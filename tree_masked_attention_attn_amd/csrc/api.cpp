@@ -5,6 +5,7 @@
 // kernel arguments packed and the kernel launched on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstring>
 #include <string>
@@ -16,6 +17,10 @@ using namespace ta;
 
 namespace {
 
+// Polls (of about 128 cycles each) a split waits for the other splits of its
+// row block before leaving its rows to the last arrival.
+std::atomic<int32_t> g_wait_polls{20000};
+
 ta_status device_error(hipError_t e, const char* what) {
   return fail(TA_ERR_DEVICE, std::string(what) + ": " + hipGetErrorString(e));
 }
@@ -25,6 +30,8 @@ ta_status device_error(hipError_t e, const char* what) {
 extern "C" {
 
 int32_t ta_abi_version(void) { return TA_ABI_VERSION; }
+
+void ta_set_split_wait_limit(int32_t polls) { g_wait_polls.store(polls < 0 ? 0 : polls); }
 
 const char* ta_last_error(void) { return last_error(); }
 
@@ -118,6 +125,7 @@ ta_status ta_tree_attn(const void* q, const ta_kv_cache* cache, int32_t layer,
   a.splits = plan.splits;
   a.n_tiles = plan.n_tiles;
   a.n_units = plan.n_units;
+  a.wait_polls = g_wait_polls.load();
   a.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(cache->head_dim)));
   hipError_t e = launch_tree_attn(a, cache->dtype, cache->head_dim, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return device_error(e, "tree_attn launch");

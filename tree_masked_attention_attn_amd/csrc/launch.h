@@ -15,7 +15,7 @@ struct TreeAttnArgs {
   void* out;                // like q
   float* ws_o;              // split partials, see AttnPlan
   float2* ws_ml;
-  int32_t* ws_cnt;
+  int32_t* ws_cnt;          // kGroupWords words per (KV head, row block) group
   int64_t kv_head_stride;   // elements from one KV head to the next (capacity * D)
   int32_t n_q_heads;
   int32_t group;            // query heads per KV head
@@ -27,6 +27,7 @@ struct TreeAttnArgs {
   int32_t splits;
   int32_t n_tiles;
   int32_t n_units;
+  int32_t wait_polls;       // bound of the wait for the other splits of a group
   float scale_log2;         // log2(e) / sqrt(D)
   uint64_t anc[64];         // ancestor-or-self bitset per tree node
 };

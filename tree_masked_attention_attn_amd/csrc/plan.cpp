@@ -98,9 +98,14 @@ ta_status plan_tree_attn(const ta_kv_cache* cache, int32_t n_q_heads, int32_t pr
     return TA_OK;
   }
   const int32_t base_units = cache->n_kv_heads * p.row_blocks;
-  int32_t want = (kTargetUnits + base_units - 1) / base_units;
+  // Aim for every CU busy with all splits resident at once (the split merge
+  // waits for its partners): the bf16 kernel runs one workgroup per CU, the
+  // fp32 one two (one for head_dim 128).
+  const bool one_per_cu = cache->dtype == TA_BF16 || cache->head_dim == 128;
+  const int32_t target = one_per_cu ? kTargetUnits / 2 : kTargetUnits;
+  int32_t want = (target + base_units - 1) / base_units;
   int32_t cap = std::max(1, p.n_tiles / kMinTilesPerSplit);
-  p.splits = std::max(1, std::min(want, cap));
+  p.splits = std::max(1, std::min(std::min(want, cap), kMaxSplits));
   p.n_units = base_units * p.splits;
   if (p.splits > 1) {
     if (base_units > kMaxGroups)

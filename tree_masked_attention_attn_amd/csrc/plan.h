@@ -7,7 +7,7 @@
 #include <cstdint>
 #include <string>
 
-#include "../../include/tree_attn.h"
+#include "tree_attn.h"
 
 namespace ta {
 
@@ -33,27 +33,29 @@ struct AttnPlan {
   int32_t rows_per_head = 0;   // group * n_tree
   int32_t row_blocks = 0;      // ceil(rows_per_head / kRowsPerBlock)
   int32_t total_keys = 0;      // prefix_len + n_tree
-  int32_t n_tiles = 0;         // ceil(total_keys / kKeyTile)
+  int32_t n_tiles = 0;         // ceil(total_keys / kKeyTile): key stages
   int32_t splits = 0;          // key-range splits per row block
   int32_t n_units = 0;         // n_kv_heads * row_blocks * splits
   // Workspace layout (only when splits > 1). The arrival counters always sit
   // at offset 0 in a fixed-size region, whatever the shape, so a workspace
   // that calls of different shapes share never finds partial data of an
   // earlier call where it expects a counter.
-  size_t ws_cnt_offset = 0;    // int32 arrival counters [n_kv_heads * row_blocks]
+  size_t ws_cnt_offset = 0;    // int32 x4 per group: arrivals, departures, claim bits, pad
   size_t ws_ml_offset = 0;     // fp32 (max, sum) pairs [units][kRowsPerBlock][2]
   size_t ws_o_offset = 0;      // fp32 partial outputs [units][kRowsPerBlock][head_dim]
   size_t ws_bytes = 0;
 };
 
-constexpr int32_t kKeyTile = 32;       // keys per staged K/V tile
+constexpr int32_t kKeyTile = 64;       // keys per LDS stage (two 32-key MFMA sub-tiles)
 constexpr int32_t kWaves = 4;          // waves per workgroup
 constexpr int32_t kRowsPerWave = 32;   // query rows per wave (one 32-wide MFMA N tile)
 constexpr int32_t kRowsPerBlock = kWaves * kRowsPerWave;
 constexpr int32_t kTargetUnits = 512;  // 2 workgroups per CU on a 256-CU part
-constexpr int32_t kMinTilesPerSplit = 4;
-constexpr int32_t kMaxGroups = 4096;   // counters in the fixed region: n_kv_heads * row_blocks
-constexpr size_t kCounterBytes = kMaxGroups * sizeof(int32_t);
+constexpr int32_t kMinTilesPerSplit = 2;
+constexpr int32_t kMaxSplits = 32;     // one claim bit per split in a 32-bit word
+constexpr int32_t kMaxGroups = 4096;   // (KV head, row block) groups with counters
+constexpr int32_t kGroupWords = 4;     // arrivals, departures, claim bits, pad
+constexpr size_t kCounterBytes = kMaxGroups * kGroupWords * sizeof(int32_t);
 
 ta_status plan_tree_attn(const ta_kv_cache* cache, int32_t n_q_heads, int32_t prefix_len,
                          int32_t n_tree, AttnPlan* plan);

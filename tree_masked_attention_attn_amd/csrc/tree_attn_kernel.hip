@@ -44,14 +44,16 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
-constexpr int kTile = 32;
+constexpr int kTile = 32;     // keys per MFMA sub-tile (the M side of S^T = K Q^T)
+constexpr int kSub = 2;       // sub-tiles per LDS stage
+constexpr int kStage = kTile * kSub;
 constexpr int kBlockRows = 128;
 constexpr float kNegInf = -__builtin_huge_valf();
 
-// Position of key `k` (0..31) inside a transposed V row in LDS. The PV MFMA
-// reads, per lane half and k-slot, the keys that the S^T accumulator gave that
-// lane; this permutation makes those keys contiguous so one wide LDS read
-// fetches a whole operand.
+// Position of key `k` (0..31 within a sub-tile) inside a transposed V row in
+// LDS. The PV MFMA reads, per lane half and k-slot, the keys that the S^T
+// accumulator gave that lane; this permutation makes those keys contiguous so
+// one wide LDS read fetches a whole operand.
 template <typename T>
 __device__ __forceinline__ int vpos(int k) {
   if constexpr (std::is_same_v<T, float>) {
@@ -63,98 +65,103 @@ __device__ __forceinline__ int vpos(int k) {
   }
 }
 
+// One LDS stage holds kStage keys: K row-major [key][D] and V transposed
+// [D][kStage] (each 32-key sub-tile permuted by vpos), both rows padded by 16
+// bytes so the MFMA operand reads of 8 (or 16) consecutive lanes fall in
+// distinct banks.
 template <typename T, int D>
 struct Layout {
   static constexpr int ES = sizeof(T);
-  static constexpr int KSTR = D * ES + 16;        // K row stride in LDS (bytes)
-  static constexpr int VSTR = kTile * ES + 16;    // transposed V row stride
-  static constexpr int KBYTES = kTile * KSTR;
-  static constexpr int BUF = KBYTES + D * VSTR;   // one stage
-  static constexpr int KCHUNKS = kTile * D * ES / 16;       // 16-B chunks per K tile
-  static constexpr int KREP = (KCHUNKS + kThreads - 1) / kThreads;
-  static constexpr int VE = 8 / ES;                         // d values per 8-B V read
-  static constexpr int VBLOCKS = (kTile / 4) * (D / VE);    // 4 keys x VE d blocks
-  static constexpr int VREP = (VBLOCKS + kThreads - 1) / kThreads;
+  static constexpr int KSTR = D * ES + 16;
+  static constexpr int VSTR = kStage * ES + 16;
+  static constexpr int KBYTES = kStage * KSTR;
+  static constexpr int BUF = KBYTES + D * VSTR;
+  static constexpr int KCHUNKS = kStage * D * ES / 16;  // 16-B chunks of K per stage
+  static constexpr int KREP = KCHUNKS / kThreads;
+  static constexpr int VE = D / 16;                     // d values per key row per thread
+  static constexpr int VW = VE * ES / 4;                // their 32-bit words (2, 4 or 8)
+  static_assert(KCHUNKS % kThreads == 0, "K stage must split evenly over the threads");
 };
 
 template <typename T, int D>
 struct Stage {
   uint4 kreg[Layout<T, D>::KREP];
-  uint2 vreg[Layout<T, D>::VREP][4];
+  uint32_t vreg[4][Layout<T, D>::VW];  // 4 consecutive keys x VE d values
 };
 
-// Global -> registers for tile `tile`. Keys at or beyond total_keys load as 0
-// and are never read from memory.
+// Buffer resource over the K (or V) rows [k0, total_keys) of one head: loads
+// at or beyond the end return 0 in hardware (raw-buffer range check), so the
+// last stage needs no branches, and rows past total_keys are never read.
 template <typename T, int D>
-__device__ __forceinline__ void load_tile(Stage<T, D>& st, const T* kh, const T* vh, int tile,
-                                          int total_keys, int tid) {
-  using L = Layout<T, D>;
-  constexpr int CPR = D * L::ES / 16;  // 16-B chunks per K row
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t stage_rsrc(const T* head, int k0, int total_keys) {
+  const int left = total_keys - k0;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(head + (size_t)k0 * D), 0,
+                                           left > 0 ? left * D * (int)sizeof(T) : 0, 0x00020000);
+}
+
+template <int W>
+__device__ __forceinline__ void buf_words(uint32_t (&dst)[W], __amdgpu_buffer_rsrc_t r, int off) {
+  if constexpr (W == 2) {
+    const auto x = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    dst[0] = x[0]; dst[1] = x[1];
+  } else {
 #pragma unroll
-  for (int r = 0; r < L::KREP; ++r) {
-    const int ci = tid + r * kThreads;
-    const int key = ci / CPR, col = ci % CPR;
-    const int gk = tile * kTile + key;
-    uint4 x = make_uint4(0, 0, 0, 0);
-    if (ci < L::KCHUNKS && gk < total_keys)
-      x = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(kh + (size_t)gk * D) + col * 16);
-    st.kreg[r] = x;
-  }
-  constexpr int DG = D / L::VE;  // d groups per key row
-#pragma unroll
-  for (int r = 0; r < L::VREP; ++r) {
-    const int bi = tid + r * kThreads;
-    const int dg = bi % DG, kg = bi / DG;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int gk = tile * kTile + kg * 4 + b;
-      uint2 x = make_uint2(0, 0);
-      if (bi < L::VBLOCKS && gk < total_keys)
-        x = *reinterpret_cast<const uint2*>(vh + (size_t)gk * D + dg * L::VE);
-      st.vreg[r][b] = x;
+    for (int i = 0; i < W / 4; ++i) {
+      const auto x = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * i, 0, 0);
+      dst[4 * i] = x[0]; dst[4 * i + 1] = x[1]; dst[4 * i + 2] = x[2]; dst[4 * i + 3] = x[3];
     }
   }
 }
 
+// Global -> registers for the stage starting at key `k0`.
+// K: 16-B chunks in row order (a stage of K is contiguous in memory).
+// V: thread t takes the 4 keys 4*(t%16) .. +3 and the VE head_dim values
+// starting at (t/16)*VE, so that 16 consecutive lanes later write one whole
+// transposed row segment (128 contiguous bytes for bf16): no bank conflicts.
+template <typename T, int D>
+__device__ __forceinline__ void load_stage(Stage<T, D>& st, const T* kh, const T* vh, int k0,
+                                           int total_keys, int tid) {
+  using L = Layout<T, D>;
+  const __amdgpu_buffer_rsrc_t rk = stage_rsrc<T, D>(kh, k0, total_keys);
+  const __amdgpu_buffer_rsrc_t rv = stage_rsrc<T, D>(vh, k0, total_keys);
+#pragma unroll
+  for (int r = 0; r < L::KREP; ++r) {
+    const auto x = __builtin_amdgcn_raw_buffer_load_b128(rk, (tid + r * kThreads) * 16, 0, 0);
+    st.kreg[r] = make_uint4(x[0], x[1], x[2], x[3]);
+  }
+  const int kg = tid & 15, dg = tid >> 4;
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+    buf_words<L::VW>(st.vreg[b], rv, ((kg * 4 + b) * D + dg * L::VE) * L::ES);
+}
+
 // Registers -> LDS stage: K row-major, V transposed with keys permuted.
 template <typename T, int D>
-__device__ __forceinline__ void store_tile(const Stage<T, D>& st, char* buf, int tid) {
+__device__ __forceinline__ void store_stage(const Stage<T, D>& st, char* buf, int tid) {
   using L = Layout<T, D>;
   constexpr int CPR = D * L::ES / 16;
 #pragma unroll
   for (int r = 0; r < L::KREP; ++r) {
     const int ci = tid + r * kThreads;
-    if (ci < L::KCHUNKS)
-      *reinterpret_cast<uint4*>(buf + (ci / CPR) * L::KSTR + (ci % CPR) * 16) = st.kreg[r];
+    *reinterpret_cast<uint4*>(buf + (ci / CPR) * L::KSTR + (ci % CPR) * 16) = st.kreg[r];
   }
   char* vt = buf + L::KBYTES;
-  constexpr int DG = D / L::VE;
+  const int kg = tid & 15, dg = tid >> 4;
+  // 4 consecutive keys stay contiguous under vpos; sub-tile kg/8 starts at key 32*(kg/8).
+  const int col = ((kg >> 3) * kTile + vpos<T>((kg & 7) * 4)) * L::ES;
 #pragma unroll
-  for (int r = 0; r < L::VREP; ++r) {
-    const int bi = tid + r * kThreads;
-    if (bi >= L::VBLOCKS) continue;
-    const int dg = bi % DG, kg = bi / DG;
-    const int col = vpos<T>(kg * 4) * L::ES;  // 4 consecutive keys stay contiguous
+  for (int e = 0; e < L::VE; ++e) {
+    char* dst = vt + (dg * L::VE + e) * L::VSTR + col;
     if constexpr (std::is_same_v<T, float>) {
-      // 2 d values per key row; write 4 keys (16 B) per d.
-      const uint2* x = st.vreg[r];
-      *reinterpret_cast<uint4*>(vt + (dg * 2 + 0) * L::VSTR + col) = make_uint4(x[0].x, x[1].x, x[2].x, x[3].x);
-      *reinterpret_cast<uint4*>(vt + (dg * 2 + 1) * L::VSTR + col) = make_uint4(x[0].y, x[1].y, x[2].y, x[3].y);
+      *reinterpret_cast<uint4*>(dst) = make_uint4(st.vreg[0][e], st.vreg[1][e], st.vreg[2][e], st.vreg[3][e]);
     } else {
-      // 4 d values per key row; write 4 keys (8 B) per d (a 4x4 16-bit transpose).
-      const uint2* x = st.vreg[r];
-      const uint32_t lo01 = (x[0].x & 0xFFFFu) | (x[1].x << 16);
-      const uint32_t lo23 = (x[2].x & 0xFFFFu) | (x[3].x << 16);
-      const uint32_t hi01 = (x[0].x >> 16) | (x[1].x & 0xFFFF0000u);
-      const uint32_t hi23 = (x[2].x >> 16) | (x[3].x & 0xFFFF0000u);
-      const uint32_t lo01y = (x[0].y & 0xFFFFu) | (x[1].y << 16);
-      const uint32_t lo23y = (x[2].y & 0xFFFFu) | (x[3].y << 16);
-      const uint32_t hi01y = (x[0].y >> 16) | (x[1].y & 0xFFFF0000u);
-      const uint32_t hi23y = (x[2].y >> 16) | (x[3].y & 0xFFFF0000u);
-      *reinterpret_cast<uint2*>(vt + (dg * 4 + 0) * L::VSTR + col) = make_uint2(lo01, lo23);
-      *reinterpret_cast<uint2*>(vt + (dg * 4 + 1) * L::VSTR + col) = make_uint2(hi01, hi23);
-      *reinterpret_cast<uint2*>(vt + (dg * 4 + 2) * L::VSTR + col) = make_uint2(lo01y, lo23y);
-      *reinterpret_cast<uint2*>(vt + (dg * 4 + 3) * L::VSTR + col) = make_uint2(hi01y, hi23y);
+      // element e of each key row is 16-bit half (e % 2) of word e / 2; one
+      // byte permute packs that half of two keys into one word
+      const int w = e >> 1;
+      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+      *reinterpret_cast<uint2*>(dst) =
+          make_uint2(__builtin_amdgcn_perm(st.vreg[1][w], st.vreg[0][w], sel),
+                     __builtin_amdgcn_perm(st.vreg[3][w], st.vreg[2][w], sel));
     }
   }
 }
@@ -193,7 +200,7 @@ template <typename T, int D>
 __device__ __forceinline__ f32x16 qk_tile(const QFrag<T, D>& qf, const char* kbuf, int l32, int half) {
   using L = Layout<T, D>;
   f32x16 acc = {};
-  const char* krow = kbuf + l32 * L::KSTR;
+  const char* krow = kbuf + l32 * L::KSTR;  // kbuf: first key row of the sub-tile
   if constexpr (std::is_same_v<T, float>) {
 #pragma unroll
     for (int c = 0; c < D / 2; c += 4) {
@@ -212,9 +219,10 @@ __device__ __forceinline__ f32x16 qk_tile(const QFrag<T, D>& qf, const char* kbu
   return acc;
 }
 
-// O^T (D x 32 rows) += V^T P^T for one tile; p[j] pairs with the key layout of qk_tile.
+// O^T (D x 32 rows) += V^T P^T for one sub-tile; p[j] pairs with the key
+// layout of qk_tile; vbuf points at the sub-tile's first column of V^T.
 template <typename T, int D>
-__device__ __forceinline__ void pv_tile(f32x16 (&o)[D / 32], const float (&p)[16], const char* vbuf,
+__device__ __forceinline__ void pv_tile(f32x16 (&o)[D / 32], const float* p, const char* vbuf,
                                         int l32, int half) {
   using L = Layout<T, D>;
   if constexpr (std::is_same_v<T, float>) {
@@ -259,11 +267,132 @@ __device__ __forceinline__ void store4(T* dst, f32x4 x) {
   }
 }
 
+// Split partials are stored in "lane order": for block row r (0..127) the
+// float4 holding head_dim values 4c .. 4c+3 is element
+//   ((r/32 * D/32 + c/8) * 4 + (c%8)/2) * 64 + (c%2) * 32 + r%32
+// of the unit's [128 * D / 4] float4 array. That is exactly where lane
+// (half, l32) of the wave owning 32-row tile r/32 holds those values in its
+// O^T accumulator, so each partial store instruction writes 1 KB contiguously.
+template <int D>
+__device__ __forceinline__ int part_index(int r, int c) {
+  return (((r >> 5) * (D / 32) + (c >> 3)) * 4 + ((c & 7) >> 1)) * 64 + (c & 1) * 32 + (r & 31);
+}
+
+// Merge rows [r0, r1) of row block `grp` from all splits, in split order, and
+// write them to `out`. Weights exp2(m_s - M) / L go through LDS once per row.
+template <typename T, int D, int NTH>
+__device__ void merge_rows(const TreeAttnArgs& a, char* smem, int grp, int g, int rb, int r0, int r1,
+                           int tid) {
+  const int S = a.splits, nr = r1 - r0;
+  const size_t u0 = (size_t)grp * S;
+  float2* ml = reinterpret_cast<float2*>(smem);            // [S][nr]
+  float* w = reinterpret_cast<float*>(smem) + 2 * S * nr;  // [S][nr]
+  for (int i = tid; i < S * nr; i += NTH)
+    ml[i] = a.ws_ml[(u0 + i / nr) * kBlockRows + r0 + i % nr];
+  __syncthreads();
+  for (int r = tid; r < nr; r += NTH) {
+    float M = kNegInf;
+    for (int s = 0; s < S; ++s) M = fmaxf(M, ml[s * nr + r].x);
+    float L = 0.f;
+    for (int s = 0; s < S; ++s) {
+      const float2 x = ml[s * nr + r];
+      const float e = x.x == kNegInf ? 0.f : __builtin_amdgcn_exp2f(x.x - M);
+      w[s * nr + r] = e;
+      L += e * x.y;
+    }
+    const float inv = 1.f / L;
+    for (int s = 0; s < S; ++s) w[s * nr + r] *= inv;
+  }
+  __syncthreads();
+  constexpr int C4 = D / 4;  // float4 chunks per row
+  const f32x4* parts = reinterpret_cast<const f32x4*>(a.ws_o) + u0 * kBlockRows * C4;
+  for (int it = tid; it < nr * C4; it += NTH) {
+    const int r = it / C4, c = it % C4;
+    const int hrow = rb * kBlockRows + r0 + r;
+    if (hrow >= a.rows_per_head) continue;
+    const f32x4* src = parts + part_index<D>(r0 + r, c);
+    f32x4 acc = {0, 0, 0, 0};
+#pragma unroll 8
+    for (int s = 0; s < S; ++s) acc += w[s * nr + r] * src[(size_t)s * kBlockRows * C4];
+    const int nd = hrow / a.group, hd = g * a.group + hrow % a.group;
+    store4<T>(static_cast<T*>(a.out) + ((size_t)nd * a.n_q_heads + hd) * D + 4 * c, acc);
+  }
+  __syncthreads();  // LDS is reused by the next merge
+}
+
+// Cross-workgroup hand-off of one split, after its partial rows and (max,
+// sum) pairs are in the workspace (no grid barrier, no second launch):
+//  * release (agent scope, by one thread after the workgroup barrier: fences
+//    are cumulative, so one L2 write-back serves the whole workgroup), then
+//    count in; every split then waits a bounded number of polls for the
+//    others; the last to arrive never waits;
+//  * merge: row slice j of the block belongs to split j. A split that saw
+//    everyone arrive claims its own slice (one bit per slice, atomic OR); the
+//    last arrival then claims every slice still unclaimed, which covers
+//    splits that stopped waiting. Each slice is merged exactly once;
+//  * count out; the last one out clears the group's words for the next call.
+template <typename T, int D, int NTH>
+__device__ void split_handoff(const TreeAttnArgs& a, char* smem, int* s_flags, int* s_taken,
+                              int grp, int g, int rb, int split, int tid) {
+  __syncthreads();
+  int* gw = a.ws_cnt + (size_t)grp * 4;  // [0] arrivals, [1] departures, [2] claim bits
+  if (tid == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const int old = __hip_atomic_fetch_add(gw, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = old == a.splits - 1;
+    bool all_in = last;
+    for (int it = 0; !all_in && it < a.wait_polls; ++it) {
+      __builtin_amdgcn_s_sleep(2);
+      all_in = __hip_atomic_load(gw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.splits;
+    }
+    if (all_in) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // invalidates this CU's L1 too
+    *s_flags = (last ? 2 : 0) | (all_in ? 1 : 0);
+  }
+  __syncthreads();
+  const int flags = *s_flags;
+  if (flags & 1) {
+    const int sweep = (flags & 2) ? a.splits : 1;
+    for (int k = 0; k < sweep; ++k) {
+      const int j = (split + k) % a.splits;
+      if (tid == 0) {
+        const int old = __hip_atomic_fetch_or(gw + 2, 1 << j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *s_taken = (old >> j) & 1;
+      }
+      __syncthreads();
+      const bool taken = *s_taken;
+      __syncthreads();
+      if (!taken)
+        merge_rows<T, D, NTH>(a, smem, grp, g, rb, j * kBlockRows / a.splits, (j + 1) * kBlockRows / a.splits, tid);
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const int old = __hip_atomic_fetch_add(gw + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old == a.splits - 1) {
+      __hip_atomic_store(gw, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(gw + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(gw + 2, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// Scores more than 2^kSlack above the running reference trigger a rescale;
+// smaller increases are absorbed (weights stay below 2^kSlack, exact after the
+// final normalisation). This skips the O rescale on almost every tile.
+constexpr float kSlack = 8.f;
+
+// Waves per SIMD each instantiation is built for: two workgroups per CU,
+// except fp32 with head_dim 128 whose LDS stages only fit one.
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void tree_attn_kernel(const TreeAttnArgs a) {
+constexpr int kOccupancy = (std::is_same_v<T, float> && D == 128) ? 1 : 2;
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(kOccupancy<T, D>, kOccupancy<T, D>)))
+void tree_attn_kernel(const TreeAttnArgs a) {
   using L = Layout<T, D>;
   __shared__ __attribute__((aligned(16))) char smem[2 * L::BUF];
-  __shared__ int s_last;
+  __shared__ int s_flags, s_taken;
 
   // Work unit. Consecutive workgroup ids go round-robin over the 8 XCDs, so
   // give each XCD a contiguous run of units: the row blocks and splits of one
@@ -274,7 +403,7 @@ __global__ __launch_bounds__(kThreads) void tree_attn_kernel(const TreeAttnArgs 
   const int grp = u / a.splits;  // (KV head, row block)
   const int rb = grp % a.row_blocks;
   const int g = grp / a.row_blocks;
-  const int t0 = (int)((long long)split * a.n_tiles / a.splits);
+  const int t0 = (int)((long long)split * a.n_tiles / a.splits);       // in kStage-key stages
   const int t1 = (int)((long long)(split + 1) * a.n_tiles / a.splits);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -295,57 +424,66 @@ __global__ __launch_bounds__(kThreads) void tree_attn_kernel(const TreeAttnArgs 
   f32x16 o[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) o[dt] = f32x16{};
-  float m_run = kNegInf, l_run = 0.f;
+  float m_ref = kNegInf, l_run = 0.f;
 
   Stage<T, D> st;
-  load_tile<T, D>(st, kh, vh, t0, a.total_keys, tid);
-  store_tile<T, D>(st, smem, tid);
+  load_stage<T, D>(st, kh, vh, t0 * kStage, a.total_keys, tid);
+  store_stage<T, D>(st, smem, tid);
+  // Every global load issued so far (q and the first stage) has landed: the
+  // loop below then only ever waits for its own prefetch.
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  for (int tile = t0; tile < t1; ++tile) {
-    char* cur = smem + ((tile - t0) & 1) * L::BUF;
-    const bool more = tile + 1 < t1;
-    if (more) load_tile<T, D>(st, kh, vh, tile + 1, a.total_keys, tid);
+  const float c = a.scale_log2;  // > 0, so the max of raw scores gives the max of scaled ones
+  for (int stage = t0; stage < t1; ++stage) {
+    char* cur = smem + ((stage - t0) & 1) * L::BUF;
+    const bool more = stage + 1 < t1;
+    if (more) load_stage<T, D>(st, kh, vh, (stage + 1) * kStage, a.total_keys, tid);
 
-    const f32x16 s = qk_tile<T, D>(qf, cur, l32, half);
-    const int kb = tile * kTile;
-    float p[16];
-    float mx = kNegInf;
-    if (kb + kTile > a.prefix_len) {
+    float p[16 * kSub];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int key = kb + 8 * (j >> 2) + 4 * half + (j & 3);
+    for (int sub = 0; sub < kSub; ++sub) {
+      const f32x16 sc = qk_tile<T, D>(qf, cur + sub * kTile * L::KSTR, l32, half);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) p[16 * sub + j] = sc[j];
+    }
+    const int kb = stage * kStage;
+    if (kb + kStage > a.prefix_len) {  // the stage reaches the tree (or past the end)
+#pragma unroll
+      for (int j = 0; j < 16 * kSub; ++j) {
+        const int key = kb + kTile * (j >> 4) + 8 * ((j >> 2) & 3) + 4 * half + (j & 3);
         bool vis = key < a.prefix_len;
         if (!vis && key < a.total_keys) vis = (anc >> (key - a.prefix_len)) & 1;
-        p[j] = vis ? s[j] * a.scale_log2 : kNegInf;
-        mx = fmaxf(mx, p[j]);
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        p[j] = s[j] * a.scale_log2;
-        mx = fmaxf(mx, p[j]);
+        if (!vis) p[j] = kNegInf;
       }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == kNegInf ? 0.f : m_new;  // fully masked so far
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    float mx = p[0];
+#pragma unroll
+    for (int j = 1; j < 16 * kSub; ++j) mx = fmaxf(mx, p[j]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;  // both lane halves of a row agree
+    const bool bump = mx > m_ref + kSlack;
+    float alpha = 1.f;
+    if (bump) {
+      alpha = __builtin_amdgcn_exp2f(m_ref - mx);  // 0 on the first visible stage
+      m_ref = mx;
+    }
+    const float nm = m_ref == kNegInf ? 0.f : -m_ref;  // nothing visible yet: weights are 0
     float psum = 0.f;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      p[j] = __builtin_amdgcn_exp2f(p[j] - m_use);
+    for (int j = 0; j < 16 * kSub; ++j) {
+      p[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(p[j], c, nm));
       psum += p[j];
     }
     l_run = l_run * alpha + psum;
-    m_run = m_new;
-    if (__ballot(alpha != 1.0f)) {
+    if (__ballot(bump)) {
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
     }
-    pv_tile<T, D>(o, p, cur + L::KBYTES, l32, half);
+#pragma unroll
+    for (int sub = 0; sub < kSub; ++sub)
+      pv_tile<T, D>(o, p + 16 * sub, cur + L::KBYTES + sub * kTile * L::ES, l32, half);
 
-    if (more) store_tile<T, D>(st, smem + ((tile + 1 - t0) & 1) * L::BUF, tid);
+    if (more) store_stage<T, D>(st, smem + ((stage + 1 - t0) & 1) * L::BUF, tid);
     __syncthreads();
   }
 
@@ -366,52 +504,407 @@ __global__ __launch_bounds__(kThreads) void tree_attn_kernel(const TreeAttnArgs 
     return;
   }
 
-  // Split: publish this split's partial rows, then take a ticket.
+  // Publish this split's rows (reference max, sum, unnormalised output), then hand off.
   {
-    float* po = a.ws_o + ((size_t)u * kBlockRows + rloc) * D;
+    f32x4* po = reinterpret_cast<f32x4*>(a.ws_o) + (size_t)u * kBlockRows * (D / 4);
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-      for (int jq = 0; jq < 4; ++jq) {
-        f32x4 x = {o[dt][4 * jq], o[dt][4 * jq + 1], o[dt][4 * jq + 2], o[dt][4 * jq + 3]};
-        *reinterpret_cast<f32x4*>(po + 32 * dt + 8 * jq + 4 * half) = x;
-      }
-    if (half == 0) a.ws_ml[(size_t)u * kBlockRows + rloc] = make_float2(m_run, l_tot);
+      for (int jq = 0; jq < 4; ++jq)
+        po[((wave * (D / 32) + dt) * 4 + jq) * 64 + lane] =
+            f32x4{o[dt][4 * jq], o[dt][4 * jq + 1], o[dt][4 * jq + 2], o[dt][4 * jq + 3]};
+    if (half == 0) a.ws_ml[(size_t)u * kBlockRows + rloc] = make_float2(m_ref, l_tot);
   }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  __syncthreads();
-  if (tid == 0) {
-    const int old = __hip_atomic_fetch_add(a.ws_cnt + grp, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const bool last = old == a.splits - 1;
-    if (last) __hip_atomic_store(a.ws_cnt + grp, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = last;
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  split_handoff<T, D, kThreads>(a, smem, &s_flags, &s_taken, grp, g, rb, split, tid);
+}
 
-  // Last arrival: merge the splits of this row block, in split order.
-  const size_t u0 = (size_t)grp * a.splits;
-  constexpr int C4 = D / 4;  // float4 chunks per row
-  for (int item = tid; item < kBlockRows * C4; item += kThreads) {
-    const int r = item / C4, c = item % C4;
-    const int hrow = rb * kBlockRows + r;
-    if (hrow >= a.rows_per_head) continue;
-    float M = kNegInf;
-    for (int s2 = 0; s2 < a.splits; ++s2) M = fmaxf(M, a.ws_ml[(u0 + s2) * kBlockRows + r].x);
-    float Lsum = 0.f;
-    f32x4 acc = {0, 0, 0, 0};
-    for (int s2 = 0; s2 < a.splits; ++s2) {
-      const float2 ml = a.ws_ml[(u0 + s2) * kBlockRows + r];
-      const float w = ml.x == kNegInf ? 0.f : __builtin_amdgcn_exp2f(ml.x - M);
-      Lsum += w * ml.y;
-      acc += w * *reinterpret_cast<const f32x4*>(a.ws_o + ((u0 + s2) * kBlockRows + r) * D + 4 * c);
-    }
-    const int nd = hrow / a.group;
-    const int hd = g * a.group + hrow % a.group;
-    store4<T>(static_cast<T*>(a.out) + ((size_t)nd * a.n_q_heads + hd) * D + 4 * c, acc * (1.f / Lsum));
+// ============================================================================
+// bf16 kernel. Same maths and hand-off as above, built for the MFMA/LDS
+// balance of CDNA4:
+//  * 4 waves = 2 row groups x 2 key halves. Wave (rp, kh) owns block rows
+//    64 rp .. 64 rp + 63 (two 32-row MFMA N tiles) and, of every 64-key stage,
+//    the 32-key half kh. Each K or V fragment read from LDS feeds two MFMAs
+//    (both row tiles), which keeps LDS traffic well under its bandwidth; the
+//    two key halves are merged through LDS at the end.
+//  * K and V reach LDS by buffer-to-LDS DMA (no staging registers, no VALU)
+//    into a ring of three 64-key stages, two stages ahead of the MFMAs. Rows
+//    are stored as-is with their 16-byte chunks XOR-swizzled by row, so the
+//    K operand reads (ds_read_b128) and the transposed V reads
+//    (ds_read_b64_tr_b16, which hands each lane 4 keys of one head_dim column)
+//    are free of bank conflicts. Keys past prefix_len + n_tree fall outside
+//    the buffer range and arrive as zeros.
+// ============================================================================
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
+
+constexpr int kRingKeys = 64;
+
+// NT: 32-row MFMA tiles per wave (1 or 2). A workgroup always covers 128 rows
+// and both 32-key halves of each stage, so it has 2 * 4 / NT waves.
+template <int D, int NT>
+struct BfGeo {
+  static constexpr int RW = 4 / NT;                 // row groups (waves per key half)
+  static constexpr int NW = 2 * RW;                 // waves
+  static constexpr int NTH = 64 * NW;               // threads
+  static constexpr int CPR = D / 8;                 // 16-B chunks per row
+  static constexpr int ROWB = D * 2;                // bytes per row
+  static constexpr int KVB = kRingKeys * ROWB;      // K (or V) bytes per stage
+  static constexpr int STAGEB = 2 * KVB;
+  static constexpr int DMA_KV = kRingKeys * CPR / NTH;  // DMA instructions per thread for K (and V)
+  static constexpr int DMA = 2 * DMA_KV;                // per thread per stage
+  static_assert(kRingKeys * CPR % NTH == 0, "stage must split evenly over the threads");
+};
+
+// Chunk c of row r sits at chunk c ^ bf_swz(r). LDS has 64 banks of 4 bytes
+// (256 bytes, i.e. 16 sixteen-byte bank groups, per cycle): a ds_read_b128 is
+// served 16 lanes at a time, a ds_read_b64_tr_b16 32 lanes at a time.
+// K reads: 16 consecutive rows at one logical chunk -> bf_swz is a bijection
+// on r mod 16 (D = 128), so the 16 chunks hit 16 different bank groups; for
+// D = 64 two rows share a 256-byte line: row bit 0 picks the half and bits
+// 1-3 permute the chunk within it.
+// Transposed V reads: 32 lanes read rows r0..r0+3 (r0 a multiple of 4) at
+// chunks 4t..4t+3 -> bits 2-3 of bf_swz (D = 128), or the half plus bit 2
+// (D = 64), tell the 4 rows apart, so the 16 chunks hit 16 different groups.
+template <int D>
+__device__ __forceinline__ int bf_swz(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+// vmcnt(n) with every other counter left alone (gfx9 encoding).
+#define TA_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw-buffer resource (gfx9 layout) over `bytes` bytes at `base`, held in SGPRs.
+__device__ __forceinline__ i32x4 bf_rsrc(const void* base, int bytes) {
+  const unsigned long long p = reinterpret_cast<unsigned long long>(base);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane(static_cast<int>(p & 0xffffffffu));
+  r[1] = __builtin_amdgcn_readfirstlane(static_cast<int>(p >> 32));  // stride 0
+  r[2] = __builtin_amdgcn_readfirstlane(bytes);                      // range: zero beyond
+  r[3] = 0x00020000;
+  return r;
+}
+
+// One 16-byte-per-lane buffer-to-LDS DMA: lane i's 16 bytes from byte `voff`
+// of the resource land at LDS address lds + 16 i. Issued through asm so the
+// compiler neither sees an LDS write nor inserts waits for it; every wait on
+// these loads is explicit (TA_WAIT_VM), and the ring's barriers order them
+// against the LDS reads.
+__device__ __forceinline__ void bf_dma16(i32x4 rsrc, const char* lds, int voff) {
+  const unsigned addr = static_cast<unsigned>(
+      reinterpret_cast<unsigned long>((__attribute__((address_space(3))) const char*)lds));
+  asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
+               :
+               : "v"(voff), "s"(__builtin_amdgcn_readfirstlane(addr)), "s"(rsrc)
+               : "memory", "m0");
+}
+
+// DMA keys [k0, k0 + 64) of K and V into a stage. Instruction r of wave w fills
+// the 1 KB of 16-byte slots [(NW r + w) * 64, +64); lane i's slot holds row
+// slot / CPR, physical chunk slot % CPR, i.e. logical chunk that ^ bf_swz(row).
+template <int D, int NT>
+__device__ __forceinline__ void bf_dma(char* stage, const __bf16* kh, const __bf16* vh, int k0,
+                                       int total_keys, int wave, int lane) {
+  using G = BfGeo<D, NT>;
+  const int left = total_keys - k0;
+  const int nrec = left > 0 ? left * G::ROWB : 0;
+  const i32x4 rk = bf_rsrc(kh + (size_t)k0 * D, nrec);
+  const i32x4 rv = bf_rsrc(vh + (size_t)k0 * D, nrec);
+#pragma unroll
+  for (int r = 0; r < G::DMA_KV; ++r) {
+    const int blk = r * G::NW + wave;
+    const int slot = blk * 64 + lane;
+    const int row = slot / G::CPR, phys = slot % G::CPR;
+    const int off = row * G::ROWB + ((phys ^ bf_swz<D>(row)) << 4);
+    bf_dma16(rk, stage + blk * 1024, off);
+    bf_dma16(rv, stage + G::KVB + blk * 1024, off);
   }
 }
+
+__device__ __forceinline__ float max16(const float* p) {
+  float a0 = fmaxf(fmaxf(p[0], p[1]), fmaxf(p[2], p[3]));
+  float a1 = fmaxf(fmaxf(p[4], p[5]), fmaxf(p[6], p[7]));
+  float a2 = fmaxf(fmaxf(p[8], p[9]), fmaxf(p[10], p[11]));
+  float a3 = fmaxf(fmaxf(p[12], p[13]), fmaxf(p[14], p[15]));
+  return fmaxf(fmaxf(a0, a1), fmaxf(a2, a3));
+}
+
+__device__ __forceinline__ float sum16(const float* p) {  // fixed pairwise order
+  float a0 = (p[0] + p[1]) + (p[2] + p[3]);
+  float a1 = (p[4] + p[5]) + (p[6] + p[7]);
+  float a2 = (p[8] + p[9]) + (p[10] + p[11]);
+  float a3 = (p[12] + p[13]) + (p[14] + p[15]);
+  return (a0 + a1) + (a2 + a3);
+}
+
+template <int D, int NT>
+struct BfState {
+  bf16x8 qf[NT][D / 16];  // Q fragments of the wave's row tiles
+  f32x16 o[NT][D / 32];   // O^T accumulators
+  float m_ref[NT], l_run[NT];
+  uint64_t anc[NT];
+};
+
+// One 64-key stage for wave (row group, kh): QK on its 32-key half for its
+// row tiles, online softmax, PV.
+template <int D, int NT>
+__device__ __forceinline__ void bf_stage(BfState<D, NT>& st, const char* stage, int k0, int kh, int lane,
+                                         const TreeAttnArgs& a) {
+  using G = BfGeo<D, NT>;
+  const int half = lane >> 5, l32 = lane & 31;
+  // S^T = K Q^T: K rows 32 kh + l32, chunk 2cc + half. All fragments are read
+  // first (one LDS latency, not D/16), and even/odd chunks accumulate in two
+  // independent chains so consecutive MFMAs do not wait on each other.
+  f32x16 sc[NT];
+  {
+    const int krow = 32 * kh + l32;
+    const char* kr = stage + krow * G::ROWB;
+    const int sw = bf_swz<D>(krow);
+    bf16x8 kf[D / 16];
+#pragma unroll
+    for (int cc = 0; cc < D / 16; ++cc)
+      kf[cc] = *reinterpret_cast<const bf16x8*>(kr + (((2 * cc + half) ^ sw) << 4));
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      f32x16 acc0 = {}, acc1 = {};
+#pragma unroll
+      for (int cc = 0; cc < D / 16; cc += 2) {
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[cc], st.qf[nt][cc], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[cc + 1], st.qf[nt][cc + 1], acc1, 0, 0, 0);
+      }
+      sc[nt] = acc0 + acc1;
+    }
+  }
+  const int kb = k0 + 32 * kh;  // first key of this half
+  const float c = a.scale_log2;
+  bf16x8 pf[NT][2];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    float p[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) p[j] = sc[nt][j];
+    if (kb + 32 > a.prefix_len) {  // reaches the tree (or past the end)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int key = kb + 8 * (j >> 2) + 4 * half + (j & 3);
+        bool vis = key < a.prefix_len;
+        if (!vis && key < a.total_keys) vis = (st.anc[nt] >> (key - a.prefix_len)) & 1;
+        if (!vis) p[j] = kNegInf;
+      }
+    }
+    float mx = max16(p);
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;  // both lane halves of a row agree
+    const bool bump = mx > st.m_ref[nt] + kSlack;
+    float alpha = 1.f;
+    if (bump) {
+      alpha = __builtin_amdgcn_exp2f(st.m_ref[nt] - mx);  // 0 on the first visible keys
+      st.m_ref[nt] = mx;
+    }
+    const float nm = st.m_ref[nt] == kNegInf ? 0.f : -st.m_ref[nt];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) p[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(p[j], c, nm));
+    st.l_run[nt] = st.l_run[nt] * alpha + sum16(p);
+    if (__ballot(bump)) {
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) st.o[nt][dt] *= alpha;
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) pf[nt][ks][q] = static_cast<__bf16>(p[8 * ks + q]);
+  }
+  // O^T += V^T P^T. The A operand (32 head_dim rows x 16 keys) comes from two
+  // transposed reads: lane (g = lane/16, j = lane%16) of a 16-lane group
+  // points at V[key e = j/4][head_dim 16 (g%2) + 4 (j%4) ..] and receives, for
+  // head_dim 16 (g%2) + j, the 4 keys the group pointed at.
+  const char* vs = stage + G::KVB;
+  const int e = (lane & 15) >> 2, q = lane & 3, g1 = (lane >> 4) & 1;
+  bf16x8 vf[2][D / 32];  // all V^T fragments of the half first, then the MFMAs
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int r1 = 32 * kh + 16 * ks + 4 * half + e, r2 = r1 + 8;
+    const int s1 = bf_swz<D>(r1), s2 = bf_swz<D>(r2);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      const int ch = 4 * dt + 2 * g1 + (q >> 1), inner = (q & 1) * 8;
+      const bf16x4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+          (__attribute__((address_space(3))) bf16x4v*)(vs + r1 * G::ROWB + ((ch ^ s1) << 4) + inner));
+      const bf16x4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+          (__attribute__((address_space(3))) bf16x4v*)(vs + r2 * G::ROWB + ((ch ^ s2) << 4) + inner));
+      vf[ks][dt] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+  }
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        st.o[nt][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ks][dt], pf[nt][ks], st.o[nt][dt], 0, 0, 0);
+}
+
+// One ring step: wait for this stage's DMA (leaving the next stage's in
+// flight), barrier, start the DMA two stages ahead, compute.
+#define TA_BF_STEP(CUR, AHEAD2, S)                                                   \
+  do {                                                                               \
+    if ((S) + 1 < t1) TA_WAIT_VM(G::DMA); else TA_WAIT_VM(0);                        \
+    __builtin_amdgcn_s_barrier();                                                    \
+    asm volatile("" ::: "memory");                                                   \
+    if ((S) + 2 < t1) bf_dma<D, NT>(AHEAD2, kh_ptr, vh_ptr, ((S) + 2) * kRingKeys, a.total_keys, wave, lane); \
+    bf_stage<D, NT>(st, CUR, (S) * kRingKeys, kh, lane, a);                          \
+  } while (0)
+
+template <int NT>
+constexpr int kBfThreads = 512 / NT;  // == BfGeo<D, NT>::NTH
+
+template <int D, int NT>
+__global__ __launch_bounds__(kBfThreads<NT>)
+__attribute__((amdgpu_waves_per_eu(3 - NT, 3 - NT)))  // 8 waves: 2 per SIMD; 4 waves: 1
+void tree_attn_bf16_kernel(const TreeAttnArgs a) {
+  using G = BfGeo<D, NT>;
+  // Three separate arrays: with statically known buffers the compiler can
+  // tell the in-flight DMA target from the stage being read.
+  __shared__ __attribute__((aligned(1024))) char ring0[G::STAGEB];
+  __shared__ __attribute__((aligned(1024))) char ring1[G::STAGEB];
+  __shared__ __attribute__((aligned(1024))) char ring2[G::STAGEB];
+  __shared__ int s_flags, s_taken;
+
+  const int b = blockIdx.x;
+  const int u = (a.n_units % 8 == 0) ? (b % 8) * (a.n_units / 8) + b / 8 : b;
+  const int split = u % a.splits;
+  const int grp = u / a.splits;
+  const int rb = grp % a.row_blocks;
+  const int g = grp / a.row_blocks;
+  const int t0 = (int)((long long)split * a.n_tiles / a.splits);  // in 64-key stages
+  const int t1 = (int)((long long)(split + 1) * a.n_tiles / a.splits);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int rg = wave % G::RW, kh = wave / G::RW;  // row group, key half
+  static_assert(G::NTH == kBfThreads<NT>, "thread count");
+
+  const __bf16* kh_ptr = static_cast<const __bf16*>(a.k) + (size_t)g * a.kv_head_stride;
+  const __bf16* vh_ptr = static_cast<const __bf16*>(a.v) + (size_t)g * a.kv_head_stride;
+  // First two stages in flight before anything else.
+  bf_dma<D, NT>(ring0, kh_ptr, vh_ptr, t0 * kRingKeys, a.total_keys, wave, lane);
+  if (t0 + 1 < t1) bf_dma<D, NT>(ring1, kh_ptr, vh_ptr, (t0 + 1) * kRingKeys, a.total_keys, wave, lane);
+
+  BfState<D, NT> st;
+  int node[NT], head[NT];
+  bool row_ok[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int row = rb * kBlockRows + 32 * (NT * rg + nt) + l32;
+    row_ok[nt] = row < a.rows_per_head;
+    node[nt] = row_ok[nt] ? row / a.group : 0;
+    head[nt] = g * a.group + (row_ok[nt] ? row % a.group : 0);
+    st.anc[nt] = row_ok[nt] ? a.anc[node[nt]] : 0;
+    const __bf16* qrow = static_cast<const __bf16*>(a.q) + ((size_t)node[nt] * a.n_q_heads + head[nt]) * D;
+#pragma unroll
+    for (int cc = 0; cc < D / 16; ++cc) {
+      bf16x8 x = {};
+      if (row_ok[nt]) x = *reinterpret_cast<const bf16x8*>(qrow + 16 * cc + 8 * half);
+      st.qf[nt][cc] = x;
+    }
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) st.o[nt][dt] = f32x16{};
+    st.m_ref[nt] = kNegInf;
+    st.l_run[nt] = 0.f;
+  }
+
+  // Q (global loads) must have landed before the loop: the compiler cannot see
+  // that the loop's explicit waits cover them and would otherwise wait for all
+  // loads, DMA included, inside the loop.
+  __builtin_amdgcn_s_waitcnt(0);
+  for (int s = t0; s < t1; s += 3) {
+    TA_BF_STEP(ring0, ring2, s);
+    if (s + 1 < t1) TA_BF_STEP(ring1, ring0, s + 1);
+    if (s + 2 < t1) TA_BF_STEP(ring2, ring1, s + 2);
+  }
+  TA_WAIT_VM(0);
+  __syncthreads();  // every wave is done with the ring: reuse it below
+
+  // Merge the two key halves: waves kh = 1 hand (m, l, O) to waves kh = 0
+  // through LDS in lane order (conflict-free). 32-row tile t = NT rg + nt of
+  // the block goes to ring0 (t < 2) or ring1, its (m, l) pairs to ring2.
+  float l_tot[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) l_tot[nt] = st.l_run[nt] + __shfl_xor(st.l_run[nt], 32);
+  if (kh == 1) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int t = NT * rg + nt;
+      f32x4* xo = reinterpret_cast<f32x4*>(t < 2 ? ring0 : ring1) + (t & 1) * (D / 32) * 4 * 64;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int jq = 0; jq < 4; ++jq)
+          xo[(dt * 4 + jq) * 64 + lane] =
+              f32x4{st.o[nt][dt][4 * jq], st.o[nt][dt][4 * jq + 1], st.o[nt][dt][4 * jq + 2], st.o[nt][dt][4 * jq + 3]};
+      if (half == 0) reinterpret_cast<float2*>(ring2)[t * 32 + l32] = make_float2(st.m_ref[nt], l_tot[nt]);
+    }
+  }
+  __syncthreads();
+  if (kh == 0) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int t = NT * rg + nt;
+      const f32x4* xo = reinterpret_cast<const f32x4*>(t < 2 ? ring0 : ring1) + (t & 1) * (D / 32) * 4 * 64;
+      const float2 other = reinterpret_cast<const float2*>(ring2)[t * 32 + l32];
+      const float M = fmaxf(st.m_ref[nt], other.x);
+      const float w0 = st.m_ref[nt] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(st.m_ref[nt] - M);
+      const float w1 = other.x == kNegInf ? 0.f : __builtin_amdgcn_exp2f(other.x - M);
+      st.m_ref[nt] = M;
+      l_tot[nt] = w0 * l_tot[nt] + w1 * other.y;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int jq = 0; jq < 4; ++jq) {
+          const f32x4 y = xo[(dt * 4 + jq) * 64 + lane];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) st.o[nt][dt][4 * jq + i] = w0 * st.o[nt][dt][4 * jq + i] + w1 * y[i];
+        }
+    }
+    if (a.splits == 1) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        if (!row_ok[nt]) continue;
+        __bf16* orow = static_cast<__bf16*>(a.out) + ((size_t)node[nt] * a.n_q_heads + head[nt]) * D;
+        const float inv = 1.f / l_tot[nt];
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int jq = 0; jq < 4; ++jq) {
+            f32x4 x = {st.o[nt][dt][4 * jq], st.o[nt][dt][4 * jq + 1], st.o[nt][dt][4 * jq + 2], st.o[nt][dt][4 * jq + 3]};
+            store4<__bf16>(orow + 32 * dt + 8 * jq + 4 * half, x * inv);
+          }
+      }
+    } else {
+      f32x4* po = reinterpret_cast<f32x4*>(a.ws_o) + (size_t)u * kBlockRows * (D / 4);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int t = NT * rg + nt;  // 32-row tile of the block
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int jq = 0; jq < 4; ++jq)
+            po[((t * (D / 32) + dt) * 4 + jq) * 64 + lane] =
+                f32x4{st.o[nt][dt][4 * jq], st.o[nt][dt][4 * jq + 1], st.o[nt][dt][4 * jq + 2], st.o[nt][dt][4 * jq + 3]};
+        if (half == 0) a.ws_ml[(size_t)u * kBlockRows + 32 * t + l32] = make_float2(st.m_ref[nt], l_tot[nt]);
+      }
+    }
+  }
+  if (a.splits == 1) return;
+  split_handoff<__bf16, D, G::NTH>(a, ring0, &s_flags, &s_taken, grp, g, rb, split, tid);
+}
+
+#undef TA_BF_STEP
+
+// 32-row tiles per wave of the bf16 kernel: 1 = 8 waves (2 per SIMD, latency
+// hidden across waves), 2 = 4 waves (half the LDS reads per MFMA).
+constexpr int kBf16RowTiles = 1;
 
 }  // namespace
 
@@ -419,10 +912,11 @@ hipError_t launch_tree_attn(const TreeAttnArgs& a, int32_t dtype, int32_t head_d
                             hipStream_t stream) {
   const dim3 grid(a.n_units), block(kThreads);
   if (dtype == 1) {
+    constexpr int NT = kBf16RowTiles;
     if (head_dim == 128)
-      hipLaunchKernelGGL((tree_attn_kernel<__bf16, 128>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((tree_attn_bf16_kernel<128, NT>), grid, dim3(BfGeo<128, NT>::NTH), 0, stream, a);
     else
-      hipLaunchKernelGGL((tree_attn_kernel<__bf16, 64>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((tree_attn_bf16_kernel<64, NT>), grid, dim3(BfGeo<64, NT>::NTH), 0, stream, a);
   } else {
     if (head_dim == 128)
       hipLaunchKernelGGL((tree_attn_kernel<float, 128>), grid, block, 0, stream, a);
