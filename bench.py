@@ -10,13 +10,23 @@ Timing: inputs are resident in HBM before the timed region. ``--rotate`` input
 sets are cycled so that the working set exceeds twice the 256 MB Infinity
 Cache (each set is one layer's K/V, as in a real step where the other layers
 have evicted it). A short device sleep is queued first so the host runs ahead
-and the kernels execute back to back; HIP events on the launch stream bracket
-every kernel. Prints ONE JSON line.
+and the kernels execute back to back. HIP events on the launch stream bracket
+the whole timed region (-> ms_per_step) and every kernel in it (-> the
+per-kernel means the roofline uses). Prints ONE JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
+
+Counter support (the traffic figure of the roofline):
+    --copy-calib        also run one plain 256 MiB device copy (the
+                        FETCH_SIZE / WRITE_SIZE calibration kernel)
+    --summarize DIR OUT turn rocprofv3 output under DIR (kernel-trace stats or
+                        counter CSVs) into the text summary OUT and exit
 """
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import math
 import os
@@ -35,6 +45,20 @@ HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 FP32_PEAK_TFLOPS = 157.3   # MI355X fp32 vector
 MALL_BYTES = 256 << 20
+COPY_BYTES = 256 << 20     # calibration copy size
+KERNEL_SOURCES = ["tree_masked_attention_attn_amd/csrc/tree_attn_kernel.hip",
+                  "tree_masked_attention_attn_amd/csrc/plan.cpp",
+                  "tree_masked_attention_attn_amd/csrc/plan.h",
+                  "tree_masked_attention_attn_amd/csrc/api.cpp"]
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def tree_attn_work(cfg, parent):
@@ -68,6 +92,23 @@ def reroot_bytes(cfg, src_rows, prefix, n_layers=1):
 def pct(xs, p):
     xs = sorted(xs)
     return xs[min(len(xs) - 1, max(0, int(round(p / 100 * (len(xs) - 1)))))]
+
+
+def traffic_file(cfg):
+    return os.path.join(PROFILES, f"tree_attn_{cfg['dtype']}_{cfg['name']}_traffic.txt")
+
+
+def load_traffic(cfg):
+    """HBM bytes per tree_attn launch from the committed counter summary, or
+    None when there is none or the kernel sources changed since."""
+    path = traffic_file(cfg)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.loads(f.read().split("```json", 1)[1].split("```", 1)[0])
+    if rec.get("source_sha") != kernel_source_sha():
+        return None
+    return rec.get("traffic_bytes")
 
 
 def cpu_baseline(cfg, x, path, surv, budget_s):
@@ -104,6 +145,107 @@ def _one_node(oracle, q, k, v, P, parent, i, hkv):
     return oracle.tree_attn_ref(q[: i + 1], k, v, P, parent[: i + 1], hkv)[i]
 
 
+# --------------------------------------------------------------------------
+# rocprofv3 output -> committed text summaries
+
+
+def _rows(d, pattern):
+    out = []
+    for f in sorted(glob.glob(os.path.join(d, "**", pattern), recursive=True)):
+        with open(f) as fh:
+            out.extend(csv.DictReader(fh))
+    return out
+
+
+def summarize(d, out_path, command):
+    lines = [f"# rocprofv3 summary: {os.path.basename(out_path)}", "", "Command (from the repository root):", "",
+             "```", command, "```", ""]
+    stats = _rows(d, "*kernel_stats.csv")
+    if stats:
+        lines += ["Kernel statistics (durations in microseconds):", "",
+                  "| kernel | calls | total us | average us | min us | max us | share |",
+                  "|---|---|---|---|---|---|---|"]
+        for r in stats:
+            lines.append(f"| {r['Name'][:90]} | {r['Calls']} | {float(r['TotalDurationNs']) / 1e3:.1f} | "
+                         f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                         f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% |")
+    dbs = sorted(glob.glob(os.path.join(d, "**", "*_results.db"), recursive=True))
+    if not stats and dbs:  # rocpd output: per-dispatch durations in the `kernels` view
+        import sqlite3
+        lines += ["Kernel statistics from the kernel trace (durations in microseconds):", "",
+                  "| kernel | calls | total us | average us | min us | max us |", "|---|---|---|---|---|---|"]
+        for db in dbs:
+            con = sqlite3.connect(db)
+            for name, n, tot, avg, mn, mx in con.execute(
+                    "select name, count(*), sum(duration), avg(duration), min(duration), max(duration) "
+                    "from kernels group by name order by sum(duration) desc"):
+                lines.append(f"| {name[:90]} | {n} | {tot / 1e3:.1f} | {avg / 1e3:.2f} | {mn / 1e3:.2f} | "
+                             f"{mx / 1e3:.2f} |")
+            con.close()
+        lines.append("")
+    counters = _rows(d, "*counter_collection.csv")
+    if counters:
+        per = {}
+        for r in counters:
+            name = r["Kernel_Name"]
+            key = ("tree_attn" if "tree_attn" in name else "kv_reroot" if "kv_reroot" in name
+                   else "copy" if "copy" in name.lower() else None)
+            if key is None:
+                continue
+            per.setdefault((key, r["Counter_Name"]), {}).setdefault(r["Dispatch_Id"], 0.0)
+            per[(key, r["Counter_Name"])][r["Dispatch_Id"]] += float(r["Counter_Value"])
+        lines += ["Counters per dispatch (tree_attn, kv_reroot: mean over dispatches; copy: the",
+                  "largest copy dispatch, which is the calibration copy):", "",
+                  "| kernel | counter | dispatches | value |", "|---|---|---|---|"]
+        agg = {}
+        for (k, c), vals in sorted(per.items()):
+            v = list(vals.values())
+            # the calibration copy is the largest copy dispatch (uploads are smaller)
+            agg[(k, c)] = max(v) if k == "copy" else statistics.fmean(v)
+            what = "largest" if k == "copy" else "mean"
+            lines.append(f"| {k} | {c} | {len(v)} | {agg[(k, c)]:.1f} ({what}) |")
+        lines.append("")
+        return lines, agg
+    return lines, {}
+
+
+def main_summarize(args):
+    d, out = args.summarize
+    lines, agg = summarize(d, out, args.command or "")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(f"wrote {out}")
+
+
+def main_traffic(args):
+    """Combine a FETCH_SIZE and a WRITE_SIZE counter run into the traffic record."""
+    fetch_dir, write_dir = args.traffic
+    cfg = W.config(args.config)
+    _, fa = summarize(fetch_dir, "", "")
+    _, wa = summarize(write_dir, "", "")
+    copy_kib = COPY_BYTES / 1024
+    f_fac = fa[("copy", "FETCH_SIZE")] / copy_kib
+    w_fac = wa[("copy", "WRITE_SIZE")] / copy_kib
+    f_kib = fa[("tree_attn", "FETCH_SIZE")]
+    w_kib = wa[("tree_attn", "WRITE_SIZE")]
+    rec = {"kernel": "tree_attn", "workload": cfg["name"], "source_sha": kernel_source_sha(),
+           "fetch_kib_per_dispatch": round(f_kib, 1), "write_kib_per_dispatch": round(w_kib, 1),
+           "copy_bytes": COPY_BYTES, "copy_fetch_factor": round(f_fac, 4), "copy_write_factor": round(w_fac, 4),
+           "traffic_bytes": int(round((f_kib / f_fac + w_kib / w_fac) * 1024))}
+    text = ["# HBM traffic of tree_attn, " + cfg["name"], "",
+            "FETCH_SIZE and WRITE_SIZE (KiB per dispatch) from two rocprofv3 --pmc runs, each divided by",
+            f"what the same counter reads for one plain {COPY_BYTES >> 20} MiB device copy in the same process.",
+            "bench.py reports traffic_bytes only while source_sha matches the kernel sources.", "",
+            "Commands (from the repository root):", "", "```", args.command or "", "```", "",
+            "```json", json.dumps(rec, indent=1), "```", ""]
+    with open(traffic_file(cfg), "w") as f:
+        f.write("\n".join(text))
+    print(json.dumps(rec))
+
+
+# --------------------------------------------------------------------------
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -113,11 +255,20 @@ def main():
     ap.add_argument("--rotate", type=int, default=0, help="input sets cycled (0 = enough to exceed 2x MALL)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib", action="store_true", help="also run one plain device copy (counter calibration)")
+    ap.add_argument("--summarize", nargs=2, metavar=("DIR", "OUT"))
+    ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--command", default=None, help="command line recorded in a summary")
     args = ap.parse_args()
+
+    if args.summarize:
+        return main_summarize(args)
+    if args.traffic:
+        return main_traffic(args)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the tree-attention path shards by KV head with no "
-              "exchange, and this build runs and reports on a single MI355X only.", file=sys.stderr)
+              "exchange, and this benchmark runs and reports on a single MI355X only.", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -146,6 +297,14 @@ def main():
     ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
+    if args.copy_calib:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     def step(i, ev=None):
         s = sets[i % rotate]
         if ev is not None:
@@ -161,19 +320,39 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
+    # Timed region: K steps, bracketed by synchronize on both sides.
     K = args.steps
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
     torch.cuda._sleep(int(2.4e9 * 0.02 * max(1, K / 200)))  # ~20 ms per 200 steps: the host runs ahead
     t_wall = time.perf_counter()
+    t_start.record(stream)
     for i in range(K):
         step(i, evs[i])
+    t_end.record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
     attn_us = [evs[i][0].elapsed_time(evs[i][1]) * 1e3 for i in range(K)]
     reroot_us = [evs[i][1].elapsed_time(evs[i][2]) * 1e3 for i in range(K)]
-    total_us = evs[0][0].elapsed_time(evs[-1][2]) * 1e3
+    total_us = t_start.elapsed_time(t_end) * 1e3
 
-    # The same kernels with one input set (L2/MALL warm), labelled as such.
+    # The same tree_attn launches back to back with no events between them
+    # (cross-checks the per-launch event figure), and once with one input
+    # set (L2/MALL warm), both labelled as such.
+    def attn_only(i):
+        s = sets[i % rotate]
+        ta.tree_attn(s["q"], s["k"], s["v"], P, parent, out=s["out"], workspace=ws)
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(int(2.4e9 * 0.01))
+    e0.record(stream)
+    for i in range(100):
+        attn_only(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    b2b_us = e0.elapsed_time(e1) * 1e3 / 100
     hot = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(50)]
     torch.cuda._sleep(int(2.4e9 * 0.01))
     for i in range(50):
@@ -187,13 +366,13 @@ def main():
     rr_mean = statistics.fmean(reroot_us)
     hbm_gbs = nbytes / (attn_mean * 1e-6) / 1e9
     tflops = flops / (attn_mean * 1e-6) / 1e12
-    mfma_bound = cfg["dtype"] == "bf16" and flops / BF16_PEAK_TFLOPS > nbytes / HBM_PEAK_GBS * 1e3
-    if mfma_bound:
+    traffic = load_traffic(cfg)
+    if cfg["dtype"] == "bf16" and flops / BF16_PEAK_TFLOPS > nbytes / HBM_PEAK_GBS * 1e3:
         roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": None}
+                "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": traffic}
     else:
         roof = {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(hbm_gbs / HBM_PEAK_GBS, 4), "traffic": None}
+                "frac": round(hbm_gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -218,13 +397,14 @@ def main():
                                                                               cfg["n_q_heads"], P, cfg["n_tree"])},
         "tree_attn": {"us_mean": round(attn_mean, 2), "us_p10": round(pct(attn_us, 10), 2),
                       "us_p50": round(pct(attn_us, 50), 2), "us_p90": round(pct(attn_us, 90), 2),
+                      "us_back_to_back": round(b2b_us, 2), "hot_cache_us_p50": round(hot_us, 2),
                       "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
                       "hbm_GBs": round(hbm_gbs, 1), "hbm_frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
-                      "TFLOPs": round(tflops, 1), "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4),
-                      "hot_cache_us_p50": round(hot_us, 2)},
+                      "TFLOPs": round(tflops, 1), "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4)},
         "kv_reroot": {"us_mean": round(rr_mean, 2), "us_p50": round(pct(reroot_us, 50), 2),
                       "algorithmic_bytes": rr_bytes, "GBs": round(rr_bytes / (rr_mean * 1e-6) / 1e9, 2)},
         "wall_s_timed_region": round(t_wall, 4),
+        "kernel_source_sha": kernel_source_sha(),
         "roofline": roof,
         "cpu_baseline": cpu,
     }

@@ -31,6 +31,7 @@
 // in a register; only tiles that reach past the prefix test it.
 #include <hip/hip_runtime.h>
 
+#include <cstddef>
 #include <type_traits>
 
 #include "launch.h"
@@ -278,6 +279,37 @@ __device__ __forceinline__ int part_index(int r, int c) {
   return (((r >> 5) * (D / 32) + (c >> 3)) * 4 + ((c & 7) >> 1)) * 64 + (c & 1) * 32 + (r & 31);
 }
 
+// Split partials are written with device-scope stores (cache policy sc1): they
+// go through this XCD's L2 to memory, so the release before the hand-off
+// finds no dirty lines of theirs to write back. A plain store would leave
+// them dirty, and every split's release would write back the XCD's whole
+// backlog of partials, one split after another.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+constexpr int kWriteThrough = 16;
+
+struct PartialSink {
+  __amdgpu_buffer_rsrc_t o, ml;
+};
+
+template <int D>
+__device__ __forceinline__ PartialSink partial_sink(const TreeAttnArgs& a, int u) {
+  PartialSink k;
+  k.o = __builtin_amdgcn_make_buffer_rsrc(a.ws_o + (size_t)u * kBlockRows * D, 0, kBlockRows * D * 4, 0x00020000);
+  k.ml = __builtin_amdgcn_make_buffer_rsrc(a.ws_ml + (size_t)u * kBlockRows, 0, kBlockRows * 8, 0x00020000);
+  return k;
+}
+
+// float4 number i of the unit's partial rows (lane order, see part_index)
+__device__ __forceinline__ void put_partial(const PartialSink& k, int i, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), k.o, i * 16, 0, kWriteThrough);
+}
+
+// (reference max, sum) of block row r
+__device__ __forceinline__ void put_ml(const PartialSink& k, int r, float m, float l) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, make_float2(m, l)), k.ml, r * 8, 0, kWriteThrough);
+}
+
 // Merge rows [r0, r1) of row block `grp` from all splits, in split order, and
 // write them to `out`. Weights exp2(m_s - M) / L go through LDS once per row.
 template <typename T, int D, int NTH>
@@ -506,62 +538,70 @@ void tree_attn_kernel(const TreeAttnArgs a) {
 
   // Publish this split's rows (reference max, sum, unnormalised output), then hand off.
   {
-    f32x4* po = reinterpret_cast<f32x4*>(a.ws_o) + (size_t)u * kBlockRows * (D / 4);
+    const PartialSink sink = partial_sink<D>(a, u);
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
       for (int jq = 0; jq < 4; ++jq)
-        po[((wave * (D / 32) + dt) * 4 + jq) * 64 + lane] =
-            f32x4{o[dt][4 * jq], o[dt][4 * jq + 1], o[dt][4 * jq + 2], o[dt][4 * jq + 3]};
-    if (half == 0) a.ws_ml[(size_t)u * kBlockRows + rloc] = make_float2(m_ref, l_tot);
+        put_partial(sink, ((wave * (D / 32) + dt) * 4 + jq) * 64 + lane,
+                    f32x4{o[dt][4 * jq], o[dt][4 * jq + 1], o[dt][4 * jq + 2], o[dt][4 * jq + 3]});
+    if (half == 0) put_ml(sink, rloc, m_ref, l_tot);
   }
   split_handoff<T, D, kThreads>(a, smem, &s_flags, &s_taken, grp, g, rb, split, tid);
 }
 
 // ============================================================================
-// bf16 kernel. Same maths and hand-off as above, built for the MFMA/LDS
-// balance of CDNA4:
-//  * 4 waves = 2 row groups x 2 key halves. Wave (rp, kh) owns block rows
-//    64 rp .. 64 rp + 63 (two 32-row MFMA N tiles) and, of every 64-key stage,
-//    the 32-key half kh. Each K or V fragment read from LDS feeds two MFMAs
-//    (both row tiles), which keeps LDS traffic well under its bandwidth; the
-//    two key halves are merged through LDS at the end.
+// bf16 kernel. Same maths and hand-off as above, built for CDNA4's balance of
+// MFMA, VALU and LDS:
+//  * 4 waves, one per SIMD, = 2 row groups x 2 key halves. Wave (rg, kh) owns
+//    block rows 64 rg .. 64 rg + 63 (two 32-row MFMA N tiles) and, of every
+//    64-key stage, the 32-key half kh. Each K or V fragment read from LDS
+//    feeds two MFMAs (both row tiles), which halves the LDS traffic per MFMA
+//    against one tile per wave; the two key halves are merged through LDS at
+//    the end.
+//  * Software pipeline inside the wave: iteration s issues the QK MFMAs of
+//    stage s + 1 and the PV MFMAs of stage s - 1 while the VALU computes the
+//    softmax of stage s, so the matrix cores and the VALU work side by side
+//    (a single wave keeps both busy when their instructions interleave).
 //  * K and V reach LDS by buffer-to-LDS DMA (no staging registers, no VALU)
-//    into a ring of three 64-key stages, two stages ahead of the MFMAs. Rows
-//    are stored as-is with their 16-byte chunks XOR-swizzled by row, so the
-//    K operand reads (ds_read_b128) and the transposed V reads
-//    (ds_read_b64_tr_b16, which hands each lane 4 keys of one head_dim column)
-//    are free of bank conflicts. Keys past prefix_len + n_tree fall outside
-//    the buffer range and arrive as zeros.
+//    into two rings of four 64-key slots; each slot is refilled three
+//    iterations before it is read. Q and the ancestor table are staged the
+//    same way, so the compiler sees no vector-memory loads and every wait on
+//    memory is an explicit vmcnt. Rows are stored as-is with their 16-byte
+//    chunks XOR-swizzled by row, so the K operand reads (ds_read_b128) and
+//    the transposed V reads (ds_read_b64_tr_b16, which hand each lane 4 keys
+//    of one head_dim column) are free of bank conflicts. Keys past
+//    prefix_len + n_tree fall outside the buffer range and arrive as zeros.
 // ============================================================================
-typedef __attribute__((address_space(3))) void lds_void;
 typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kRingKeys = 64;
+constexpr int kBfWaves = 4;
+constexpr int kBfThreads = 64 * kBfWaves;
+constexpr int kRing = 4;  // slots per ring (K and V each)
 
-// NT: 32-row MFMA tiles per wave (1 or 2). A workgroup always covers 128 rows
-// and both 32-key halves of each stage, so it has 2 * 4 / NT waves.
-template <int D, int NT>
+template <int D>
 struct BfGeo {
-  static constexpr int RW = 4 / NT;                 // row groups (waves per key half)
-  static constexpr int NW = 2 * RW;                 // waves
-  static constexpr int NTH = 64 * NW;               // threads
-  static constexpr int CPR = D / 8;                 // 16-B chunks per row
-  static constexpr int ROWB = D * 2;                // bytes per row
-  static constexpr int KVB = kRingKeys * ROWB;      // K (or V) bytes per stage
-  static constexpr int STAGEB = 2 * KVB;
-  static constexpr int DMA_KV = kRingKeys * CPR / NTH;  // DMA instructions per thread for K (and V)
-  static constexpr int DMA = 2 * DMA_KV;                // per thread per stage
-  static_assert(kRingKeys * CPR % NTH == 0, "stage must split evenly over the threads");
+  static constexpr int CPR = D / 8;                   // 16-byte chunks per row
+  static constexpr int ROWB = D * 2;                  // bytes per row
+  static constexpr int SLOT = 64 * ROWB;              // one 64-key K (or V) stage
+  static constexpr int OPS = 64 * CPR / kBfThreads;   // DMA instructions per thread per slot
+  static constexpr int QOPS = kBlockRows * CPR / kBfThreads;
+  static constexpr int VRING = kRing * SLOT;          // the V ring follows the K ring
+  static constexpr int QSTAGE = VRING + 2 * SLOT;     // Q waits in V slots 2 and 3
+  static constexpr int ANC = 2 * kRing * SLOT;        // ancestor table (64 x u64) + DMA spill
+  static constexpr int LDS = ANC + 1024;
+  static_assert(64 * CPR % kBfThreads == 0 && kBlockRows * CPR % kBfThreads == 0, "DMA split");
+  static_assert(QSTAGE + kBlockRows * ROWB <= ANC, "Q staging must fit in V slots 2-3");
 };
 
 // Chunk c of row r sits at chunk c ^ bf_swz(r). LDS has 64 banks of 4 bytes
 // (256 bytes, i.e. 16 sixteen-byte bank groups, per cycle): a ds_read_b128 is
 // served 16 lanes at a time, a ds_read_b64_tr_b16 32 lanes at a time.
-// K reads: 16 consecutive rows at one logical chunk -> bf_swz is a bijection
-// on r mod 16 (D = 128), so the 16 chunks hit 16 different bank groups; for
-// D = 64 two rows share a 256-byte line: row bit 0 picks the half and bits
-// 1-3 permute the chunk within it.
+// K and Q reads: 16 consecutive rows at one logical chunk -> bf_swz is a
+// bijection on r mod 16 (D = 128), so the 16 chunks hit 16 different bank
+// groups; for D = 64 two rows share a 256-byte line: row bit 0 picks the half
+// and bits 1-3 permute the chunk within it.
 // Transposed V reads: 32 lanes read rows r0..r0+3 (r0 a multiple of 4) at
 // chunks 4t..4t+3 -> bits 2-3 of bf_swz (D = 128), or the half plus bit 2
 // (D = 64), tell the 4 rows apart, so the 16 chunks hit 16 different groups.
@@ -574,7 +614,21 @@ __device__ __forceinline__ int bf_swz(int r) {
 // vmcnt(n) with every other counter left alone (gfx9 encoding).
 #define TA_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
 
-typedef int i32x4 __attribute__((ext_vector_type(4)));
+// vmcnt(x) for a wave-uniform x, rounded down to a multiple of 4 (waiting
+// for more than needed is always safe).
+__device__ __forceinline__ void wait_vm_atmost(int x) {
+  if (x >= 20) TA_WAIT_VM(20);
+  else if (x >= 16) TA_WAIT_VM(16);
+  else if (x >= 12) TA_WAIT_VM(12);
+  else if (x >= 8) TA_WAIT_VM(8);
+  else if (x >= 4) TA_WAIT_VM(4);
+  else TA_WAIT_VM(0);
+}
+
+__device__ __forceinline__ void bf_barrier() {
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 // Raw-buffer resource (gfx9 layout) over `bytes` bytes at `base`, held in SGPRs.
 __device__ __forceinline__ i32x4 bf_rsrc(const void* base, int bytes) {
@@ -590,8 +644,8 @@ __device__ __forceinline__ i32x4 bf_rsrc(const void* base, int bytes) {
 // One 16-byte-per-lane buffer-to-LDS DMA: lane i's 16 bytes from byte `voff`
 // of the resource land at LDS address lds + 16 i. Issued through asm so the
 // compiler neither sees an LDS write nor inserts waits for it; every wait on
-// these loads is explicit (TA_WAIT_VM), and the ring's barriers order them
-// against the LDS reads.
+// these loads is explicit (TA_WAIT_VM), and the barriers order them against
+// the LDS reads.
 __device__ __forceinline__ void bf_dma16(i32x4 rsrc, const char* lds, int voff) {
   const unsigned addr = static_cast<unsigned>(
       reinterpret_cast<unsigned long>((__attribute__((address_space(3))) const char*)lds));
@@ -601,25 +655,50 @@ __device__ __forceinline__ void bf_dma16(i32x4 rsrc, const char* lds, int voff) 
                : "memory", "m0");
 }
 
-// DMA keys [k0, k0 + 64) of K and V into a stage. Instruction r of wave w fills
-// the 1 KB of 16-byte slots [(NW r + w) * 64, +64); lane i's slot holds row
-// slot / CPR, physical chunk slot % CPR, i.e. logical chunk that ^ bf_swz(row).
-template <int D, int NT>
-__device__ __forceinline__ void bf_dma(char* stage, const __bf16* kh, const __bf16* vh, int k0,
-                                       int total_keys, int wave, int lane) {
-  using G = BfGeo<D, NT>;
-  const int left = total_keys - k0;
-  const int nrec = left > 0 ? left * G::ROWB : 0;
-  const i32x4 rk = bf_rsrc(kh + (size_t)k0 * D, nrec);
-  const i32x4 rv = bf_rsrc(vh + (size_t)k0 * D, nrec);
+// DMA keys [k0, k0 + 64) of one head's K (or V) into a slot. Instruction o of
+// wave w fills the 1 KB of 16-byte positions [(4 o + w) * 64, +64); position
+// i holds row i / CPR, physical chunk i % CPR, i.e. logical chunk that
+// ^ bf_swz(row).
+template <int D>
+__device__ __forceinline__ void bf_dma_slot(char* slot, const __bf16* head, int k0, int total_keys,
+                                            int wave, int lane) {
+  using G = BfGeo<D>;
+  const i32x4 r = bf_rsrc(head + (size_t)k0 * D, (total_keys - k0) * G::ROWB);
 #pragma unroll
-  for (int r = 0; r < G::DMA_KV; ++r) {
-    const int blk = r * G::NW + wave;
-    const int slot = blk * 64 + lane;
-    const int row = slot / G::CPR, phys = slot % G::CPR;
-    const int off = row * G::ROWB + ((phys ^ bf_swz<D>(row)) << 4);
-    bf_dma16(rk, stage + blk * 1024, off);
-    bf_dma16(rv, stage + G::KVB + blk * 1024, off);
+  for (int o = 0; o < G::OPS; ++o) {
+    const int blk = o * kBfWaves + wave;
+    const int i = blk * 64 + lane;
+    const int row = i / G::CPR, phys = i % G::CPR;
+    bf_dma16(r, slot + blk * 1024, row * G::ROWB + ((phys ^ bf_swz<D>(row)) << 4));
+  }
+}
+
+// DMA the block's 128 query rows (same swizzled layout; rows past the head's
+// rows read as zeros) and, from the kernel arguments, the ancestor table.
+template <int D>
+__device__ __forceinline__ void bf_dma_q_anc(char* lds, const TreeAttnArgs& a, int g, int rb, int wave,
+                                             int lane) {
+  using G = BfGeo<D>;
+  const int qbytes = a.n_tree * a.n_q_heads * G::ROWB;
+  const i32x4 r = bf_rsrc(a.q, qbytes);
+#pragma unroll
+  for (int o = 0; o < G::QOPS; ++o) {
+    const int blk = o * kBfWaves + wave;
+    const int i = blk * 64 + lane;
+    const int row = i / G::CPR, phys = i % G::CPR;
+    const int hr = rb * kBlockRows + row;
+    int off = qbytes;  // out of range: zeros
+    if (hr < a.rows_per_head)
+      off = ((hr / a.group) * a.n_q_heads + g * a.group + hr % a.group) * G::ROWB +
+            ((phys ^ bf_swz<D>(row)) << 4);
+    bf_dma16(r, lds + G::QSTAGE + blk * 1024, off);
+  }
+  if (wave == 0) {
+    // The arguments block sits at the start of the kernarg segment; its 512-byte
+    // ancestor table is read by lanes 0..31, lanes 32..63 fall out of range.
+    const char* args = (const char*)__builtin_amdgcn_kernarg_segment_ptr();
+    const i32x4 ra = bf_rsrc(args + offsetof(TreeAttnArgs, anc), 64 * 8);
+    bf_dma16(ra, lds + G::ANC, lane * 16);
   }
 }
 
@@ -639,89 +718,59 @@ __device__ __forceinline__ float sum16(const float* p) {  // fixed pairwise orde
   return (a0 + a1) + (a2 + a3);
 }
 
-template <int D, int NT>
-struct BfState {
-  bf16x8 qf[NT][D / 16];  // Q fragments of the wave's row tiles
-  f32x16 o[NT][D / 32];   // O^T accumulators
-  float m_ref[NT], l_run[NT];
-  uint64_t anc[NT];
+// v_permlane32_swap: a = [a_lo, b_lo], b = [a_hi, b_hi] (lo/hi: lanes 0-31 /
+// 32-63). Written as asm because the compiler builtin returns its first
+// result for both halves; the s_nop covers the VALU-write hazard on the
+// operands.
+__device__ __forceinline__ void swap32(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+
+template <int D>
+struct BfWave {
+  bf16x8 qf[2][D / 16];  // Q fragments of the wave's two row tiles
+  f32x16 o[2][D / 32];   // O^T accumulators
+  float m_ref[2], l_run[2];
+  float alpha[2];        // rescale of O owed by the last softmax (applied before the next PV)
+  bool pend;             // some row of the wave owes one
+  uint64_t anc[2];
 };
 
-// One 64-key stage for wave (row group, kh): QK on its 32-key half for its
-// row tiles, online softmax, PV.
-template <int D, int NT>
-__device__ __forceinline__ void bf_stage(BfState<D, NT>& st, const char* stage, int k0, int kh, int lane,
-                                         const TreeAttnArgs& a) {
-  using G = BfGeo<D, NT>;
-  const int half = lane >> 5, l32 = lane & 31;
-  // S^T = K Q^T: K rows 32 kh + l32, chunk 2cc + half. All fragments are read
-  // first (one LDS latency, not D/16), and even/odd chunks accumulate in two
-  // independent chains so consecutive MFMAs do not wait on each other.
-  f32x16 sc[NT];
-  {
-    const int krow = 32 * kh + l32;
-    const char* kr = stage + krow * G::ROWB;
-    const int sw = bf_swz<D>(krow);
-    bf16x8 kf[D / 16];
+// Settle the rescale the last softmax owes O. Kept a real branch (the asm
+// stops the compiler from speculating 128 multiplies): references move
+// rarely, by design of the lazy maximum.
+template <int D>
+__device__ __forceinline__ void bf_rescale(BfWave<D>& w) {
+  if (w.pend) {
+    asm volatile("" ::: "memory");
 #pragma unroll
-    for (int cc = 0; cc < D / 16; ++cc)
-      kf[cc] = *reinterpret_cast<const bf16x8*>(kr + (((2 * cc + half) ^ sw) << 4));
+    for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      f32x16 acc0 = {}, acc1 = {};
-#pragma unroll
-      for (int cc = 0; cc < D / 16; cc += 2) {
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[cc], st.qf[nt][cc], acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[cc + 1], st.qf[nt][cc + 1], acc1, 0, 0, 0);
-      }
-      sc[nt] = acc0 + acc1;
-    }
+      for (int dt = 0; dt < D / 32; ++dt) w.o[nt][dt] *= w.alpha[nt];
   }
-  const int kb = k0 + 32 * kh;  // first key of this half
-  const float c = a.scale_log2;
-  bf16x8 pf[NT][2];
+}
+
+// K fragments of the wave's 32-key half: K rows 32 kh + l32, chunk 2 cc + half.
+template <int D>
+__device__ __forceinline__ void bf_read_k(bf16x8 (&kf)[D / 16], const char* slot, int kh, int lane) {
+  using G = BfGeo<D>;
+  const int krow = 32 * kh + (lane & 31);
+  const char* kr = slot + krow * G::ROWB;
+  const int sw = bf_swz<D>(krow), half = lane >> 5;
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    float p[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) p[j] = sc[nt][j];
-    if (kb + 32 > a.prefix_len) {  // reaches the tree (or past the end)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int key = kb + 8 * (j >> 2) + 4 * half + (j & 3);
-        bool vis = key < a.prefix_len;
-        if (!vis && key < a.total_keys) vis = (st.anc[nt] >> (key - a.prefix_len)) & 1;
-        if (!vis) p[j] = kNegInf;
-      }
-    }
-    float mx = max16(p);
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;  // both lane halves of a row agree
-    const bool bump = mx > st.m_ref[nt] + kSlack;
-    float alpha = 1.f;
-    if (bump) {
-      alpha = __builtin_amdgcn_exp2f(st.m_ref[nt] - mx);  // 0 on the first visible keys
-      st.m_ref[nt] = mx;
-    }
-    const float nm = st.m_ref[nt] == kNegInf ? 0.f : -st.m_ref[nt];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) p[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(p[j], c, nm));
-    st.l_run[nt] = st.l_run[nt] * alpha + sum16(p);
-    if (__ballot(bump)) {
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) st.o[nt][dt] *= alpha;
-    }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int q = 0; q < 8; ++q) pf[nt][ks][q] = static_cast<__bf16>(p[8 * ks + q]);
-  }
-  // O^T += V^T P^T. The A operand (32 head_dim rows x 16 keys) comes from two
-  // transposed reads: lane (g = lane/16, j = lane%16) of a 16-lane group
-  // points at V[key e = j/4][head_dim 16 (g%2) + 4 (j%4) ..] and receives, for
-  // head_dim 16 (g%2) + j, the 4 keys the group pointed at.
-  const char* vs = stage + G::KVB;
-  const int e = (lane & 15) >> 2, q = lane & 3, g1 = (lane >> 4) & 1;
-  bf16x8 vf[2][D / 32];  // all V^T fragments of the half first, then the MFMAs
+  for (int cc = 0; cc < D / 16; ++cc)
+    kf[cc] = *reinterpret_cast<const bf16x8*>(kr + (((2 * cc + half) ^ sw) << 4));
+}
+
+// V^T fragments (A operand of O^T += V^T P^T, 32 head_dim rows x 16 keys) of
+// the wave's half, from two transposed reads each: lane (g = lane/16,
+// j = lane%16) of a 16-lane group points at V[key e = j/4][head_dim
+// 16 (g%2) + 4 (j%4) ..] and receives, for head_dim 16 (g%2) + j, the 4 keys
+// the group pointed at.
+template <int D>
+__device__ __forceinline__ void bf_read_v(bf16x8 (&vf)[2][D / 32], const char* slot, int kh, int lane) {
+  using G = BfGeo<D>;
+  const int half = lane >> 5, e = (lane & 15) >> 2, q = lane & 3, g1 = (lane >> 4) & 1;
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
     const int r1 = 32 * kh + 16 * ks + 4 * half + e, r2 = r1 + 8;
@@ -730,45 +779,146 @@ __device__ __forceinline__ void bf_stage(BfState<D, NT>& st, const char* stage, 
     for (int dt = 0; dt < D / 32; ++dt) {
       const int ch = 4 * dt + 2 * g1 + (q >> 1), inner = (q & 1) * 8;
       const bf16x4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-          (__attribute__((address_space(3))) bf16x4v*)(vs + r1 * G::ROWB + ((ch ^ s1) << 4) + inner));
+          (__attribute__((address_space(3))) bf16x4v*)(slot + r1 * G::ROWB + ((ch ^ s1) << 4) + inner));
       const bf16x4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-          (__attribute__((address_space(3))) bf16x4v*)(vs + r2 * G::ROWB + ((ch ^ s2) << 4) + inner));
+          (__attribute__((address_space(3))) bf16x4v*)(slot + r2 * G::ROWB + ((ch ^ s2) << 4) + inner));
       vf[ks][dt] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     }
   }
+}
+
+// S^T = K Q^T for both row tiles (keys = M, rows = N, head_dim = K): after
+// the product lane (l32, half) holds, for row l32 of the tile, the scores of
+// keys 8 (j/4) + 4 half + j%4 of the half, j = 0..15.
+template <int D>
+__device__ __forceinline__ void bf_qk(f32x16 (&s)[2], const bf16x8 (&kf)[D / 16], const BfWave<D>& w) {
+  s[0] = f32x16{};
+  s[1] = f32x16{};
+#pragma unroll
+  for (int cc = 0; cc < D / 16; ++cc)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) s[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[cc], w.qf[nt][cc], s[nt], 0, 0, 0);
+}
+
+// O^T += V^T P^T for both row tiles.
+template <int D>
+__device__ __forceinline__ void bf_pv(BfWave<D>& w, const bf16x8 (&vf)[2][D / 32], const bf16x8 (&p)[2][2]) {
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        st.o[nt][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ks][dt], pf[nt][ks], st.o[nt][dt], 0, 0, 0);
+      for (int nt = 0; nt < 2; ++nt)
+        w.o[nt][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ks][dt], p[nt][ks], w.o[nt][dt], 0, 0, 0);
 }
 
-// One ring step: wait for this stage's DMA (leaving the next stage's in
-// flight), barrier, start the DMA two stages ahead, compute.
-#define TA_BF_STEP(CUR, AHEAD2, S)                                                   \
-  do {                                                                               \
-    if ((S) + 1 < t1) TA_WAIT_VM(G::DMA); else TA_WAIT_VM(0);                        \
-    __builtin_amdgcn_s_barrier();                                                    \
-    asm volatile("" ::: "memory");                                                   \
-    if ((S) + 2 < t1) bf_dma<D, NT>(AHEAD2, kh_ptr, vh_ptr, ((S) + 2) * kRingKeys, a.total_keys, wave, lane); \
-    bf_stage<D, NT>(st, CUR, (S) * kRingKeys, kh, lane, a);                          \
-  } while (0)
+// Visibility of the 32 keys kb .. kb + 31 for a row whose ancestor-or-self
+// set is `anc`: bit i set iff key kb + i is a prefix key or one of the row's
+// tree nodes (anc has no bits past n_tree, so keys past the end are hidden).
+__device__ __forceinline__ uint32_t visible32(uint64_t anc, int kb, int prefix_len) {
+  const int d = kb - prefix_len;  // key kb is tree node d when d >= 0
+  uint32_t tree;
+  if (d >= 0) tree = d < 64 ? static_cast<uint32_t>(anc >> d) : 0u;
+  else tree = d > -32 ? static_cast<uint32_t>(anc << (-d)) : 0u;
+  const uint32_t pre = d <= -32 ? ~0u : (d >= 0 ? 0u : ((1u << (-d)) - 1u));
+  return pre | tree;
+}
 
-template <int NT>
-constexpr int kBfThreads = 512 / NT;  // == BfGeo<D, NT>::NTH
+// Online softmax of one stage's scores (keys kb .. kb + 31 of this half):
+// masks tree keys that are not ancestors, raises the reference max lazily
+// (only when a score exceeds it by more than 2^kSlack), and returns the bf16
+// weights (B operand of the PV product); the factors alpha that rescale O
+// are left in the wave state for bf_rescale.
+// Straight-line code apart from the (uniform) mask test, so that the
+// compiler can interleave it with the MFMAs of the same iteration.
+template <int D>
+__device__ __forceinline__ void bf_softmax(BfWave<D>& w, f32x16 (&sc)[2], bf16x8 (&p)[2][2], int kb, int half,
+                                           const TreeAttnArgs& a) {
+  float x[2][16];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) x[nt][j] = sc[nt][j];
+  if (kb + 32 > a.prefix_len) {  // reaches the tree (or past the end)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const uint32_t vis = visible32(w.anc[nt], kb, a.prefix_len);
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (!((vis >> (8 * (j >> 2) + 4 * half + (j & 3))) & 1u)) x[nt][j] = kNegInf;
+    }
+  }
+  // Row max over both lane halves, for both tiles: two lane swaps.
+  float m0 = max16(x[0]), m1 = max16(x[1]);
+  swap32(m0, m1);
+  float mt = fmaxf(m0, m1), mt2 = mt;  // lanes 0-31: tile 0's max; 32-63: tile 1's
+  swap32(mt, mt2);                     // mt: tile 0's max everywhere, mt2: tile 1's
+  const float c = a.scale_log2;
+  const float mx[2] = {mt * c, mt2 * c};
+  bool bump_any = false;
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const bool bump = mx[nt] > w.m_ref[nt] + kSlack;
+    const float al = __builtin_amdgcn_exp2f(w.m_ref[nt] - mx[nt]);  // 0 on the first visible keys
+    w.alpha[nt] = bump ? al : 1.f;
+    w.m_ref[nt] = bump ? mx[nt] : w.m_ref[nt];
+    bump_any |= bump;
+    const float nm = w.m_ref[nt] == kNegInf ? 0.f : -w.m_ref[nt];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) x[nt][j] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[nt][j], c, nm));
+    w.l_run[nt] = w.l_run[nt] * w.alpha[nt] + sum16(x[nt]);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) p[nt][ks][q] = static_cast<__bf16>(x[nt][8 * ks + q]);
+  }
+  w.pend = __ballot(bump_any) != 0;
+}
 
-template <int D, int NT>
-__global__ __launch_bounds__(kBfThreads<NT>)
-__attribute__((amdgpu_waves_per_eu(3 - NT, 3 - NT)))  // 8 waves: 2 per SIMD; 4 waves: 1
+// One pipeline iteration on stage s: softmax of s (scores in `sc`), QK of
+// s + 1 from `knext` (when QK), PV of s - 1 from `vprev` with its weights
+// `pp` (when PV). On return sc holds the scores of s + 1 and pp the weights
+// of s. The rescale owed by softmax(s - 1) is settled first: O then holds
+// stages up to s - 2 against the reference of s - 1, as PV(s - 1) needs.
+// The softmax, PV and QK form one straight-line block whose MFMAs are spread
+// evenly through the VALU work (a wave issues in order, so MFMA and VALU only
+// overlap when they alternate in the instruction stream).
+template <int D, bool QK, bool PV>
+__device__ __forceinline__ void bf_iter(BfWave<D>& w, f32x16 (&sc)[2], bf16x8 (&pp)[2][2], const char* knext,
+                                        const char* vprev, int kb, int kh, int lane, const TreeAttnArgs& a) {
+  bf16x8 kf[D / 16];
+  bf16x8 vf[2][D / 32];
+  if constexpr (PV) bf_rescale<D>(w);
+  if constexpr (PV) bf_read_v<D>(vf, vprev, kh, lane);
+  if constexpr (QK) bf_read_k<D>(kf, knext, kh, lane);
+  bf16x8 pn[2][2];
+  bf_softmax<D>(w, sc, pn, kb, lane >> 5, a);
+  if constexpr (PV) bf_pv<D>(w, vf, pp);
+  if constexpr (QK) bf_qk<D>(sc, kf, w);
+  constexpr int kMfma = (QK ? D / 8 : 0) + (PV ? D / 8 : 0);
+  if constexpr (kMfma > 0) {
+    // 0x008 MFMA, 0x002 VALU: start with VALU (the max needs no LDS data),
+    // then one MFMA per few VALU instructions.
+    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+#pragma unroll
+    for (int i = 0; i < kMfma; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+    }
+  }
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    pp[nt][0] = pn[nt][0];
+    pp[nt][1] = pn[nt][1];
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kBfThreads)
+__attribute__((amdgpu_waves_per_eu(1, 1)))  // one wave per SIMD, up to 512 registers
 void tree_attn_bf16_kernel(const TreeAttnArgs a) {
-  using G = BfGeo<D, NT>;
-  // Three separate arrays: with statically known buffers the compiler can
-  // tell the in-flight DMA target from the stage being read.
-  __shared__ __attribute__((aligned(1024))) char ring0[G::STAGEB];
-  __shared__ __attribute__((aligned(1024))) char ring1[G::STAGEB];
-  __shared__ __attribute__((aligned(1024))) char ring2[G::STAGEB];
+  using G = BfGeo<D>;
+  __shared__ __attribute__((aligned(1024))) char lds[G::LDS];
   __shared__ int s_flags, s_taken;
 
   const int b = blockIdx.x;
@@ -779,97 +929,151 @@ void tree_attn_bf16_kernel(const TreeAttnArgs a) {
   const int g = grp / a.row_blocks;
   const int t0 = (int)((long long)split * a.n_tiles / a.splits);  // in 64-key stages
   const int t1 = (int)((long long)(split + 1) * a.n_tiles / a.splits);
+  const int n = t1 - t0;  // >= 1
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, l32 = lane & 31;
-  const int rg = wave % G::RW, kh = wave / G::RW;  // row group, key half
-  static_assert(G::NTH == kBfThreads<NT>, "thread count");
-
+  const int rg = wave & 1, kh = wave >> 1;  // row group, key half
   const __bf16* kh_ptr = static_cast<const __bf16*>(a.k) + (size_t)g * a.kv_head_stride;
   const __bf16* vh_ptr = static_cast<const __bf16*>(a.v) + (size_t)g * a.kv_head_stride;
-  // First two stages in flight before anything else.
-  bf_dma<D, NT>(ring0, kh_ptr, vh_ptr, t0 * kRingKeys, a.total_keys, wave, lane);
-  if (t0 + 1 < t1) bf_dma<D, NT>(ring1, kh_ptr, vh_ptr, (t0 + 1) * kRingKeys, a.total_keys, wave, lane);
+  char* const kring = lds;
+  char* const vring = lds + G::VRING;
+  auto kslot = [&](int j) { return kring + (j & (kRing - 1)) * G::SLOT; };
+  auto vslot = [&](int j) { return vring + (j & (kRing - 1)) * G::SLOT; };
+  auto dma_k = [&](int j) { bf_dma_slot<D>(kslot(j), kh_ptr, (t0 + j) * 64, a.total_keys, wave, lane); };
+  auto dma_v = [&](int j) { bf_dma_slot<D>(vslot(j), vh_ptr, (t0 + j) * 64, a.total_keys, wave, lane); };
 
-  BfState<D, NT> st;
-  int node[NT], head[NT];
-  bool row_ok[NT];
+  // DMA issue order (j = stage index within the split): Q and ancestors, K0..K3,
+  // V0, V1; then iteration j issues K(j+4) and V(j+2). Iteration j needs K(j+1)
+  // and V(j-1); the waits below count the DMA instructions issued after the
+  // newest of those, which may stay in flight.
+  bf_dma_q_anc<D>(lds, a, g, rb, wave, lane);
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int row = rb * kBlockRows + 32 * (NT * rg + nt) + l32;
+  for (int j = 0; j < 4; ++j)
+    if (j < n) dma_k(j);
+  dma_v(0);
+  if (1 < n) dma_v(1);
+  auto iter_ops = [&](int j) {  // DMA instructions iteration j issues (j = -1: V1 of the prologue)
+    if (j < 0) return G::OPS;
+    return G::OPS * ((j + 4 < n) + (j + 2 < n));
+  };
+
+  BfWave<D> w;
+  int node[2], head[2];
+  bool row_ok[2];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int row = rb * kBlockRows + 32 * (2 * rg + nt) + l32;
     row_ok[nt] = row < a.rows_per_head;
     node[nt] = row_ok[nt] ? row / a.group : 0;
     head[nt] = g * a.group + (row_ok[nt] ? row % a.group : 0);
-    st.anc[nt] = row_ok[nt] ? a.anc[node[nt]] : 0;
-    const __bf16* qrow = static_cast<const __bf16*>(a.q) + ((size_t)node[nt] * a.n_q_heads + head[nt]) * D;
 #pragma unroll
-    for (int cc = 0; cc < D / 16; ++cc) {
-      bf16x8 x = {};
-      if (row_ok[nt]) x = *reinterpret_cast<const bf16x8*>(qrow + 16 * cc + 8 * half);
-      st.qf[nt][cc] = x;
-    }
+    for (int dt = 0; dt < D / 32; ++dt) w.o[nt][dt] = f32x16{};
+    w.m_ref[nt] = kNegInf;
+    w.l_run[nt] = 0.f;
+    w.alpha[nt] = 1.f;
+  }
+  w.pend = false;
+
+  // Q, the ancestors and K0 have landed: read Q and the ancestor bits, QK(0).
+  wait_vm_atmost(G::OPS * ((n > 1) + (n > 2) + (n > 3) + 1 + (n > 1)));
+  bf_barrier();
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) st.o[nt][dt] = f32x16{};
-    st.m_ref[nt] = kNegInf;
-    st.l_run[nt] = 0.f;
+  for (int nt = 0; nt < 2; ++nt) {
+    const int row = 32 * (2 * rg + nt) + l32;
+    const char* qr = lds + G::QSTAGE + row * G::ROWB;
+    const int sw = bf_swz<D>(row);
+#pragma unroll
+    for (int cc = 0; cc < D / 16; ++cc)
+      w.qf[nt][cc] = *reinterpret_cast<const bf16x8*>(qr + (((2 * cc + half) ^ sw) << 4));
+    w.anc[nt] = row_ok[nt] ? reinterpret_cast<const uint64_t*>(lds + G::ANC)[node[nt]] : 0;
+  }
+  f32x16 sc[2];
+  bf16x8 pp[2][2];
+  {
+    bf16x8 kf[D / 16];
+    bf_read_k<D>(kf, kslot(0), kh, lane);
+    bf_qk<D>(sc, kf, w);
   }
 
-  // Q (global loads) must have landed before the loop: the compiler cannot see
-  // that the loop's explicit waits cover them and would otherwise wait for all
-  // loads, DMA included, inside the loop.
-  __builtin_amdgcn_s_waitcnt(0);
-  for (int s = t0; s < t1; s += 3) {
-    TA_BF_STEP(ring0, ring2, s);
-    if (s + 1 < t1) TA_BF_STEP(ring1, ring0, s + 1);
-    if (s + 2 < t1) TA_BF_STEP(ring2, ring1, s + 2);
+  // Iteration 0: softmax(0) and QK(1); no PV yet.
+  wait_vm_atmost(G::OPS * ((n > 2) + (n > 3) + 1 + (n > 1)));
+  bf_barrier();
+  if (4 < n) dma_k(4);
+  if (2 < n) dma_v(2);  // over the Q staging area: Q was read before the barrier
+  if (n > 1)
+    bf_iter<D, true, false>(w, sc, pp, kslot(1), nullptr, t0 * 64 + 32 * kh, kh, lane, a);
+  else
+    bf_iter<D, false, false>(w, sc, pp, nullptr, nullptr, t0 * 64 + 32 * kh, kh, lane, a);
+  // Steady state.
+  for (int j = 1; j < n - 1; ++j) {
+    wait_vm_atmost(iter_ops(j - 2) + iter_ops(j - 1));
+    bf_barrier();
+    if (j + 4 < n) dma_k(j + 4);
+    if (j + 2 < n) dma_v(j + 2);
+    bf_iter<D, true, true>(w, sc, pp, kslot(j + 1), vslot(j - 1), (t0 + j) * 64 + 32 * kh, kh, lane, a);
+  }
+  // Last iteration: softmax(n-1) and PV(n-2); then PV(n-1).
+  if (n > 1) {
+    wait_vm_atmost(iter_ops(n - 3) + iter_ops(n - 2));
+    bf_barrier();
+    bf_iter<D, false, true>(w, sc, pp, nullptr, vslot(n - 2), (t0 + n - 1) * 64 + 32 * kh, kh, lane, a);
   }
   TA_WAIT_VM(0);
-  __syncthreads();  // every wave is done with the ring: reuse it below
+  bf_barrier();
+  {
+    bf16x8 vf[2][D / 32];
+    bf_read_v<D>(vf, vslot(n - 1), kh, lane);
+    bf_rescale<D>(w);
+    bf_pv<D>(w, vf, pp);
+  }
+  __syncthreads();  // every wave is done with the rings: reuse them below
 
   // Merge the two key halves: waves kh = 1 hand (m, l, O) to waves kh = 0
-  // through LDS in lane order (conflict-free). 32-row tile t = NT rg + nt of
-  // the block goes to ring0 (t < 2) or ring1, its (m, l) pairs to ring2.
-  float l_tot[NT];
+  // through LDS in lane order (conflict-free). 32-row tile t = 2 rg + nt of
+  // the block goes to [t * 32 D floats], its (m, l) pairs after the 4 tiles.
+  constexpr int TILE_F4 = 32 * D / 4;
+  f32x4* xo = reinterpret_cast<f32x4*>(lds);
+  float2* xml = reinterpret_cast<float2*>(lds + 4 * TILE_F4 * 16);
+  float l_tot[2];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) l_tot[nt] = st.l_run[nt] + __shfl_xor(st.l_run[nt], 32);
+  for (int nt = 0; nt < 2; ++nt) l_tot[nt] = w.l_run[nt] + __shfl_xor(w.l_run[nt], 32);
   if (kh == 1) {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int t = NT * rg + nt;
-      f32x4* xo = reinterpret_cast<f32x4*>(t < 2 ? ring0 : ring1) + (t & 1) * (D / 32) * 4 * 64;
+    for (int nt = 0; nt < 2; ++nt) {
+      const int t = 2 * rg + nt;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
         for (int jq = 0; jq < 4; ++jq)
-          xo[(dt * 4 + jq) * 64 + lane] =
-              f32x4{st.o[nt][dt][4 * jq], st.o[nt][dt][4 * jq + 1], st.o[nt][dt][4 * jq + 2], st.o[nt][dt][4 * jq + 3]};
-      if (half == 0) reinterpret_cast<float2*>(ring2)[t * 32 + l32] = make_float2(st.m_ref[nt], l_tot[nt]);
+          xo[t * TILE_F4 + (dt * 4 + jq) * 64 + lane] =
+              f32x4{w.o[nt][dt][4 * jq], w.o[nt][dt][4 * jq + 1], w.o[nt][dt][4 * jq + 2], w.o[nt][dt][4 * jq + 3]};
+      if (half == 0) xml[t * 32 + l32] = make_float2(w.m_ref[nt], l_tot[nt]);
     }
   }
   __syncthreads();
   if (kh == 0) {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int t = NT * rg + nt;
-      const f32x4* xo = reinterpret_cast<const f32x4*>(t < 2 ? ring0 : ring1) + (t & 1) * (D / 32) * 4 * 64;
-      const float2 other = reinterpret_cast<const float2*>(ring2)[t * 32 + l32];
-      const float M = fmaxf(st.m_ref[nt], other.x);
-      const float w0 = st.m_ref[nt] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(st.m_ref[nt] - M);
+    for (int nt = 0; nt < 2; ++nt) {
+      const int t = 2 * rg + nt;
+      const float2 other = xml[t * 32 + l32];
+      const float M = fmaxf(w.m_ref[nt], other.x);
+      const float w0 = w.m_ref[nt] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(w.m_ref[nt] - M);
       const float w1 = other.x == kNegInf ? 0.f : __builtin_amdgcn_exp2f(other.x - M);
-      st.m_ref[nt] = M;
+      w.m_ref[nt] = M;
       l_tot[nt] = w0 * l_tot[nt] + w1 * other.y;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
         for (int jq = 0; jq < 4; ++jq) {
-          const f32x4 y = xo[(dt * 4 + jq) * 64 + lane];
+          const f32x4 y = xo[t * TILE_F4 + (dt * 4 + jq) * 64 + lane];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) st.o[nt][dt][4 * jq + i] = w0 * st.o[nt][dt][4 * jq + i] + w1 * y[i];
+          for (int i = 0; i < 4; ++i) w.o[nt][dt][4 * jq + i] = w0 * w.o[nt][dt][4 * jq + i] + w1 * y[i];
         }
     }
     if (a.splits == 1) {
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
+      for (int nt = 0; nt < 2; ++nt) {
         if (!row_ok[nt]) continue;
         __bf16* orow = static_cast<__bf16*>(a.out) + ((size_t)node[nt] * a.n_q_heads + head[nt]) * D;
         const float inv = 1.f / l_tot[nt];
@@ -877,34 +1081,29 @@ void tree_attn_bf16_kernel(const TreeAttnArgs a) {
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
           for (int jq = 0; jq < 4; ++jq) {
-            f32x4 x = {st.o[nt][dt][4 * jq], st.o[nt][dt][4 * jq + 1], st.o[nt][dt][4 * jq + 2], st.o[nt][dt][4 * jq + 3]};
+            f32x4 x = {w.o[nt][dt][4 * jq], w.o[nt][dt][4 * jq + 1], w.o[nt][dt][4 * jq + 2], w.o[nt][dt][4 * jq + 3]};
             store4<__bf16>(orow + 32 * dt + 8 * jq + 4 * half, x * inv);
           }
       }
     } else {
-      f32x4* po = reinterpret_cast<f32x4*>(a.ws_o) + (size_t)u * kBlockRows * (D / 4);
+      const PartialSink sink = partial_sink<D>(a, u);
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const int t = NT * rg + nt;  // 32-row tile of the block
+      for (int nt = 0; nt < 2; ++nt) {
+        const int t = 2 * rg + nt;  // 32-row tile of the block
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
           for (int jq = 0; jq < 4; ++jq)
-            po[((t * (D / 32) + dt) * 4 + jq) * 64 + lane] =
-                f32x4{st.o[nt][dt][4 * jq], st.o[nt][dt][4 * jq + 1], st.o[nt][dt][4 * jq + 2], st.o[nt][dt][4 * jq + 3]};
-        if (half == 0) a.ws_ml[(size_t)u * kBlockRows + 32 * t + l32] = make_float2(st.m_ref[nt], l_tot[nt]);
+            put_partial(sink, ((t * (D / 32) + dt) * 4 + jq) * 64 + lane,
+                        f32x4{w.o[nt][dt][4 * jq], w.o[nt][dt][4 * jq + 1], w.o[nt][dt][4 * jq + 2],
+                              w.o[nt][dt][4 * jq + 3]});
+        if (half == 0) put_ml(sink, 32 * t + l32, w.m_ref[nt], l_tot[nt]);
       }
     }
   }
   if (a.splits == 1) return;
-  split_handoff<__bf16, D, G::NTH>(a, ring0, &s_flags, &s_taken, grp, g, rb, split, tid);
+  split_handoff<__bf16, D, kBfThreads>(a, lds, &s_flags, &s_taken, grp, g, rb, split, tid);
 }
-
-#undef TA_BF_STEP
-
-// 32-row tiles per wave of the bf16 kernel: 1 = 8 waves (2 per SIMD, latency
-// hidden across waves), 2 = 4 waves (half the LDS reads per MFMA).
-constexpr int kBf16RowTiles = 1;
 
 }  // namespace
 
@@ -912,11 +1111,10 @@ hipError_t launch_tree_attn(const TreeAttnArgs& a, int32_t dtype, int32_t head_d
                             hipStream_t stream) {
   const dim3 grid(a.n_units), block(kThreads);
   if (dtype == 1) {
-    constexpr int NT = kBf16RowTiles;
     if (head_dim == 128)
-      hipLaunchKernelGGL((tree_attn_bf16_kernel<128, NT>), grid, dim3(BfGeo<128, NT>::NTH), 0, stream, a);
+      hipLaunchKernelGGL((tree_attn_bf16_kernel<128>), grid, dim3(kBfThreads), 0, stream, a);
     else
-      hipLaunchKernelGGL((tree_attn_bf16_kernel<64, NT>), grid, dim3(BfGeo<64, NT>::NTH), 0, stream, a);
+      hipLaunchKernelGGL((tree_attn_bf16_kernel<64>), grid, dim3(kBfThreads), 0, stream, a);
   } else {
     if (head_dim == 128)
       hipLaunchKernelGGL((tree_attn_kernel<float, 128>), grid, block, 0, stream, a);
