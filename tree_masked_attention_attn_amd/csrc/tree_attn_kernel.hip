@@ -576,52 +576,65 @@ void tree_attn_kernel(const TreeAttnArgs a) {
 typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kBfWaves = 4;
-constexpr int kBfThreads = 64 * kBfWaves;
+// NT: 32-row MFMA tiles per wave. A workgroup always covers 128 rows and both
+// 32-key halves of each stage: 8 / NT waves (NT = 1: two waves per SIMD;
+// NT = 2: one wave per SIMD, each K or V fragment feeding two MFMAs).
+#ifndef TA_BF16_NT
+#define TA_BF16_NT 1
+#endif
+template <int NT>
+constexpr int kBfWaves = 8 / NT;
+template <int NT>
+constexpr int kBfThreads = 64 * kBfWaves<NT>;
 constexpr int kRing = 4;  // slots per ring (K and V each)
 
+// LDS layout. Rows are stored with padding rather than swizzling, so that
+// every fragment read of a wave is one base address plus compile-time
+// offsets. LDS has 64 banks of 4 bytes: 16 sixteen-byte bank groups per
+// 256 bytes, served to 16 lanes of a ds_read_b128 or 32 lanes of a
+// ds_read_b64_tr_b16 at a time.
+//  * K (and Q) rows: stride KS = D/8 + 1 chunks. A K read has 16 lanes on 16
+//    consecutive rows at one chunk c: groups (KS r + c) mod 16 are distinct
+//    because KS is odd.
+//  * V rows: stride VS chunks, VS = 4 mod 16 (D = 128) or 12 mod 16 (D = 64).
+//    A transposed read has 32 lanes on rows r0 + e (e < 4) and chunks
+//    4t + j (j < 4): groups (VS e + j + const) mod 16 are all distinct.
 template <int D>
 struct BfGeo {
   static constexpr int CPR = D / 8;                   // 16-byte chunks per row
-  static constexpr int ROWB = D * 2;                  // bytes per row
-  static constexpr int SLOT = 64 * ROWB;              // one 64-key K (or V) stage
-  static constexpr int OPS = 64 * CPR / kBfThreads;   // DMA instructions per thread per slot
-  static constexpr int QOPS = kBlockRows * CPR / kBfThreads;
-  static constexpr int VRING = kRing * SLOT;          // the V ring follows the K ring
-  static constexpr int QSTAGE = VRING + 2 * SLOT;     // Q waits in V slots 2 and 3
-  static constexpr int ANC = 2 * kRing * SLOT;        // ancestor table (64 x u64) + DMA spill
+  static constexpr int ROWB = D * 2;                  // bytes per row in HBM
+  static constexpr int KS = CPR + 1;                  // K / Q row stride in LDS, chunks
+  static constexpr int VS = D == 128 ? 20 : 12;       // V row stride in LDS, chunks
+  static constexpr int KSLOT = 64 * KS * 16;          // one 64-key K stage
+  static constexpr int VSLOT = 64 * VS * 16;          // one 64-key V stage
+  // A slot of row stride S is filled by S 64-lane DMA instructions.
+  static constexpr int VRING = kRing * KSLOT;         // the V ring follows the K ring
+  static constexpr int QSTAGE0 = 3 * KSLOT;           // Q rows 0-63 wait in K slot 3,
+  static constexpr int QSTAGE1 = VRING + 3 * VSLOT;   // rows 64-127 in V slot 3 (K layout)
+  static constexpr int ANC = kRing * (KSLOT + VSLOT); // ancestor table (64 x u64) + DMA spill
   static constexpr int LDS = ANC + 1024;
-  static_assert(64 * CPR % kBfThreads == 0 && kBlockRows * CPR % kBfThreads == 0, "DMA split");
-  static_assert(QSTAGE + kBlockRows * ROWB <= ANC, "Q staging must fit in V slots 2-3");
+  static_assert(kBlockRows == 128 && VS >= CPR && VS % 16 == (D == 128 ? 4 : 12), "layout");
+  static_assert(LDS <= 160 * 1024, "LDS");
 };
-
-// Chunk c of row r sits at chunk c ^ bf_swz(r). LDS has 64 banks of 4 bytes
-// (256 bytes, i.e. 16 sixteen-byte bank groups, per cycle): a ds_read_b128 is
-// served 16 lanes at a time, a ds_read_b64_tr_b16 32 lanes at a time.
-// K and Q reads: 16 consecutive rows at one logical chunk -> bf_swz is a
-// bijection on r mod 16 (D = 128), so the 16 chunks hit 16 different bank
-// groups; for D = 64 two rows share a 256-byte line: row bit 0 picks the half
-// and bits 1-3 permute the chunk within it.
-// Transposed V reads: 32 lanes read rows r0..r0+3 (r0 a multiple of 4) at
-// chunks 4t..4t+3 -> bits 2-3 of bf_swz (D = 128), or the half plus bit 2
-// (D = 64), tell the 4 rows apart, so the 16 chunks hit 16 different groups.
-template <int D>
-__device__ __forceinline__ int bf_swz(int r) {
-  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
-  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
-}
 
 // vmcnt(n) with every other counter left alone (gfx9 encoding).
 #define TA_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
 
-// vmcnt(x) for a wave-uniform x, rounded down to a multiple of 4 (waiting
+// vmcnt(x) for a wave-uniform x, rounded down to an even number (waiting
 // for more than needed is always safe).
 __device__ __forceinline__ void wait_vm_atmost(int x) {
-  if (x >= 20) TA_WAIT_VM(20);
+  if (x >= 24) TA_WAIT_VM(24);
+  else if (x >= 22) TA_WAIT_VM(22);
+  else if (x >= 20) TA_WAIT_VM(20);
+  else if (x >= 18) TA_WAIT_VM(18);
   else if (x >= 16) TA_WAIT_VM(16);
+  else if (x >= 14) TA_WAIT_VM(14);
   else if (x >= 12) TA_WAIT_VM(12);
+  else if (x >= 10) TA_WAIT_VM(10);
   else if (x >= 8) TA_WAIT_VM(8);
+  else if (x >= 6) TA_WAIT_VM(6);
   else if (x >= 4) TA_WAIT_VM(4);
+  else if (x >= 2) TA_WAIT_VM(2);
   else TA_WAIT_VM(0);
 }
 
@@ -655,44 +668,57 @@ __device__ __forceinline__ void bf_dma16(i32x4 rsrc, const char* lds, int voff) 
                : "memory", "m0");
 }
 
-// DMA keys [k0, k0 + 64) of one head's K (or V) into a slot. Instruction o of
-// wave w fills the 1 KB of 16-byte positions [(4 o + w) * 64, +64); position
-// i holds row i / CPR, physical chunk i % CPR, i.e. logical chunk that
-// ^ bf_swz(row).
-template <int D>
-__device__ __forceinline__ void bf_dma_slot(char* slot, const __bf16* head, int k0, int total_keys,
-                                            int wave, int lane) {
+// Per-lane source offsets of the DMA instructions that fill one slot of row
+// stride S chunks: instruction op (op = 4 o + wave) covers LDS positions
+// [64 op, 64 op + 64) of the slot, position p = row * S + chunk; padding
+// chunks read out of range (zeros). The same for every stage.
+template <int D, int S, int W, int NW>
+__device__ __forceinline__ void bf_dma_offsets(int (&off)[W], int wave, int lane) {
   using G = BfGeo<D>;
-  const i32x4 r = bf_rsrc(head + (size_t)k0 * D, (total_keys - k0) * G::ROWB);
 #pragma unroll
-  for (int o = 0; o < G::OPS; ++o) {
-    const int blk = o * kBfWaves + wave;
-    const int i = blk * 64 + lane;
-    const int row = i / G::CPR, phys = i % G::CPR;
-    bf_dma16(r, slot + blk * 1024, row * G::ROWB + ((phys ^ bf_swz<D>(row)) << 4));
+  for (int o = 0; o < W; ++o) {
+    const int p = (o * NW + wave) * 64 + lane;
+    const int row = p / S, ch = p % S;
+    off[o] = ch < G::CPR ? row * G::ROWB + ch * 16 : (1 << 30);
   }
 }
 
-// DMA the block's 128 query rows (same swizzled layout; rows past the head's
-// rows read as zeros) and, from the kernel arguments, the ancestor table.
-template <int D>
+// DMA keys [k0, k0 + 64) of one head's K (or V) into a slot of row stride S.
+template <int D, int S, int W, int NW>
+__device__ __forceinline__ void bf_dma_slot(char* slot, const __bf16* head, int k0, int total_keys,
+                                            const int (&off)[W], int wave) {
+  using G = BfGeo<D>;
+  const i32x4 r = bf_rsrc(head + (size_t)k0 * D, (total_keys - k0) * G::ROWB);
+#pragma unroll
+  for (int o = 0; o < W; ++o) {
+    const int op = o * NW + wave;
+    if (op < S) bf_dma16(r, slot + op * 1024, off[o]);
+  }
+}
+
+// DMA the block's 128 query rows (K layout; rows 0-63 into K slot 3, rows
+// 64-127 into V slot 3; rows past the head's rows and padding read as zeros)
+// and, from the kernel arguments, the ancestor table.
+template <int D, int NW>
 __device__ __forceinline__ void bf_dma_q_anc(char* lds, const TreeAttnArgs& a, int g, int rb, int wave,
                                              int lane) {
   using G = BfGeo<D>;
   const int qbytes = a.n_tree * a.n_q_heads * G::ROWB;
   const i32x4 r = bf_rsrc(a.q, qbytes);
 #pragma unroll
-  for (int o = 0; o < G::QOPS; ++o) {
-    const int blk = o * kBfWaves + wave;
-    const int i = blk * 64 + lane;
-    const int row = i / G::CPR, phys = i % G::CPR;
-    const int hr = rb * kBlockRows + row;
-    int off = qbytes;  // out of range: zeros
-    if (hr < a.rows_per_head)
-      off = ((hr / a.group) * a.n_q_heads + g * a.group + hr % a.group) * G::ROWB +
-            ((phys ^ bf_swz<D>(row)) << 4);
-    bf_dma16(r, lds + G::QSTAGE + blk * 1024, off);
-  }
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int o = 0; o < (G::KS + NW - 1) / NW; ++o) {
+      const int op = o * NW + wave;
+      if (op >= G::KS) continue;
+      const int p = op * 64 + lane;
+      const int row = 64 * h + p / G::KS, ch = p % G::KS;
+      const int hr = rb * kBlockRows + row;
+      int off = qbytes;  // out of range: zeros
+      if (ch < G::CPR && hr < a.rows_per_head)
+        off = ((hr / a.group) * a.n_q_heads + g * a.group + hr % a.group) * G::ROWB + ch * 16;
+      bf_dma16(r, lds + (h ? G::QSTAGE1 : G::QSTAGE0) + op * 1024, off);
+    }
   if (wave == 0) {
     // The arguments block sits at the start of the kernarg segment; its 512-byte
     // ancestor table is read by lanes 0..31, lanes 32..63 fall out of range.
@@ -702,12 +728,18 @@ __device__ __forceinline__ void bf_dma_q_anc(char* lds, const TreeAttnArgs& a, i
   }
 }
 
+// Max of 16 scores with the NaN-propagating maximum (v_maximum3_f32 on
+// gfx950): fmaxf's NaN rules would cost an extra canonicalising instruction
+// per input. Scores are finite or -inf.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 __device__ __forceinline__ float max16(const float* p) {
-  float a0 = fmaxf(fmaxf(p[0], p[1]), fmaxf(p[2], p[3]));
-  float a1 = fmaxf(fmaxf(p[4], p[5]), fmaxf(p[6], p[7]));
-  float a2 = fmaxf(fmaxf(p[8], p[9]), fmaxf(p[10], p[11]));
-  float a3 = fmaxf(fmaxf(p[12], p[13]), fmaxf(p[14], p[15]));
-  return fmaxf(fmaxf(a0, a1), fmaxf(a2, a3));
+  const float a = vmax(vmax(p[0], p[1]), p[2]);
+  const float b = vmax(vmax(p[3], p[4]), p[5]);
+  const float c = vmax(vmax(p[6], p[7]), p[8]);
+  const float d = vmax(vmax(p[9], p[10]), p[11]);
+  const float e = vmax(vmax(p[12], p[13]), p[14]);
+  return vmax(vmax(vmax(a, b), c), vmax(vmax(d, e), p[15]));
 }
 
 __device__ __forceinline__ float sum16(const float* p) {  // fixed pairwise order
@@ -726,25 +758,25 @@ __device__ __forceinline__ void swap32(float& a, float& b) {
   asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
 }
 
-template <int D>
+template <int D, int NT>
 struct BfWave {
-  bf16x8 qf[2][D / 16];  // Q fragments of the wave's two row tiles
-  f32x16 o[2][D / 32];   // O^T accumulators
-  float m_ref[2], l_run[2];
-  float alpha[2];        // rescale of O owed by the last softmax (applied before the next PV)
-  bool pend;             // some row of the wave owes one
-  uint64_t anc[2];
+  bf16x8 qf[NT][D / 16];  // Q fragments of the wave's row tiles
+  f32x16 o[NT][D / 32];   // O^T accumulators
+  float m_ref[NT], l_run[NT];
+  float alpha[NT];        // rescale of O owed by the last softmax (applied before the next PV)
+  bool pend;              // some row of the wave owes one
+  uint64_t anc[NT];
 };
 
 // Settle the rescale the last softmax owes O. Kept a real branch (the asm
 // stops the compiler from speculating 128 multiplies): references move
 // rarely, by design of the lazy maximum.
-template <int D>
-__device__ __forceinline__ void bf_rescale(BfWave<D>& w) {
+template <int D, int NT>
+__device__ __forceinline__ void bf_rescale(BfWave<D, NT>& w) {
   if (w.pend) {
     asm volatile("" ::: "memory");
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) w.o[nt][dt] *= w.alpha[nt];
   }
@@ -754,12 +786,9 @@ __device__ __forceinline__ void bf_rescale(BfWave<D>& w) {
 template <int D>
 __device__ __forceinline__ void bf_read_k(bf16x8 (&kf)[D / 16], const char* slot, int kh, int lane) {
   using G = BfGeo<D>;
-  const int krow = 32 * kh + (lane & 31);
-  const char* kr = slot + krow * G::ROWB;
-  const int sw = bf_swz<D>(krow), half = lane >> 5;
+  const char* base = slot + (32 * kh + (lane & 31)) * (G::KS * 16) + (lane >> 5) * 16;
 #pragma unroll
-  for (int cc = 0; cc < D / 16; ++cc)
-    kf[cc] = *reinterpret_cast<const bf16x8*>(kr + (((2 * cc + half) ^ sw) << 4));
+  for (int cc = 0; cc < D / 16; ++cc) kf[cc] = *reinterpret_cast<const bf16x8*>(base + 32 * cc);
 }
 
 // V^T fragments (A operand of O^T += V^T P^T, 32 head_dim rows x 16 keys) of
@@ -770,45 +799,43 @@ __device__ __forceinline__ void bf_read_k(bf16x8 (&kf)[D / 16], const char* slot
 template <int D>
 __device__ __forceinline__ void bf_read_v(bf16x8 (&vf)[2][D / 32], const char* slot, int kh, int lane) {
   using G = BfGeo<D>;
+  constexpr int RS = G::VS * 16;  // row stride, bytes
   const int half = lane >> 5, e = (lane & 15) >> 2, q = lane & 3, g1 = (lane >> 4) & 1;
+  const char* base = slot + (32 * kh + 4 * half + e) * RS + (2 * g1 + (q >> 1)) * 16 + (q & 1) * 8;
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    const int r1 = 32 * kh + 16 * ks + 4 * half + e, r2 = r1 + 8;
-    const int s1 = bf_swz<D>(r1), s2 = bf_swz<D>(r2);
+  for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
-      const int ch = 4 * dt + 2 * g1 + (q >> 1), inner = (q & 1) * 8;
       const bf16x4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-          (__attribute__((address_space(3))) bf16x4v*)(slot + r1 * G::ROWB + ((ch ^ s1) << 4) + inner));
+          (__attribute__((address_space(3))) bf16x4v*)(base + 16 * ks * RS + 64 * dt));
       const bf16x4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-          (__attribute__((address_space(3))) bf16x4v*)(slot + r2 * G::ROWB + ((ch ^ s2) << 4) + inner));
+          (__attribute__((address_space(3))) bf16x4v*)(base + (16 * ks + 8) * RS + 64 * dt));
       vf[ks][dt] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     }
-  }
 }
 
-// S^T = K Q^T for both row tiles (keys = M, rows = N, head_dim = K): after
+// S^T = K Q^T for the wave's row tiles (keys = M, rows = N, head_dim = K): after
 // the product lane (l32, half) holds, for row l32 of the tile, the scores of
 // keys 8 (j/4) + 4 half + j%4 of the half, j = 0..15.
-template <int D>
-__device__ __forceinline__ void bf_qk(f32x16 (&s)[2], const bf16x8 (&kf)[D / 16], const BfWave<D>& w) {
-  s[0] = f32x16{};
-  s[1] = f32x16{};
+template <int D, int NT>
+__device__ __forceinline__ void bf_qk(f32x16 (&s)[NT], const bf16x8 (&kf)[D / 16], const BfWave<D, NT>& w) {
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) s[nt] = f32x16{};
 #pragma unroll
   for (int cc = 0; cc < D / 16; ++cc)
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) s[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[cc], w.qf[nt][cc], s[nt], 0, 0, 0);
+    for (int nt = 0; nt < NT; ++nt) s[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[cc], w.qf[nt][cc], s[nt], 0, 0, 0);
 }
 
-// O^T += V^T P^T for both row tiles.
-template <int D>
-__device__ __forceinline__ void bf_pv(BfWave<D>& w, const bf16x8 (&vf)[2][D / 32], const bf16x8 (&p)[2][2]) {
+// O^T += V^T P^T for the wave's row tiles.
+template <int D, int NT>
+__device__ __forceinline__ void bf_pv(BfWave<D, NT>& w, const bf16x8 (&vf)[2][D / 32], const bf16x8 (&p)[NT][2]) {
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
+      for (int nt = 0; nt < NT; ++nt)
         w.o[nt][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ks][dt], p[nt][ks], w.o[nt][dt], 0, 0, 0);
 }
 
@@ -824,98 +851,152 @@ __device__ __forceinline__ uint32_t visible32(uint64_t anc, int kb, int prefix_l
   return pre | tree;
 }
 
-// Online softmax of one stage's scores (keys kb .. kb + 31 of this half):
-// masks tree keys that are not ancestors, raises the reference max lazily
-// (only when a score exceeds it by more than 2^kSlack), and returns the bf16
-// weights (B operand of the PV product); the factors alpha that rescale O
-// are left in the wave state for bf_rescale.
-// Straight-line code apart from the (uniform) mask test, so that the
-// compiler can interleave it with the MFMAs of the same iteration.
-template <int D>
-__device__ __forceinline__ void bf_softmax(BfWave<D>& w, f32x16 (&sc)[2], bf16x8 (&p)[2][2], int kb, int half,
-                                           const TreeAttnArgs& a) {
-  float x[2][16];
+// Scores of one stage (keys kb .. kb + 31 of this half) copied out of the
+// accumulators, with tree keys that are not ancestors (and keys past the
+// end) set to -inf. The mask is a uniform branch taken only by stages that
+// reach the tree.
+template <int D, int NT>
+__device__ __forceinline__ void bf_scores(const BfWave<D, NT>& w, const f32x16 (&sc)[NT], float (&x)[NT][16],
+                                          int kb, int half, const TreeAttnArgs& a) {
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt)
+  for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
     for (int j = 0; j < 16; ++j) x[nt][j] = sc[nt][j];
-  if (kb + 32 > a.prefix_len) {  // reaches the tree (or past the end)
+  if (kb + 32 > a.prefix_len) {
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
+    for (int nt = 0; nt < NT; ++nt) {
       const uint32_t vis = visible32(w.anc[nt], kb, a.prefix_len);
 #pragma unroll
       for (int j = 0; j < 16; ++j)
         if (!((vis >> (8 * (j >> 2) + 4 * half + (j & 3))) & 1u)) x[nt][j] = kNegInf;
     }
   }
-  // Row max over both lane halves, for both tiles: two lane swaps.
-  float m0 = max16(x[0]), m1 = max16(x[1]);
-  swap32(m0, m1);
-  float mt = fmaxf(m0, m1), mt2 = mt;  // lanes 0-31: tile 0's max; 32-63: tile 1's
-  swap32(mt, mt2);                     // mt: tile 0's max everywhere, mt2: tile 1's
+}
+
+// One pipeline iteration on stage j (QK, PV, VN select the parts that exist):
+//  * settle the rescale softmax(j - 1) owes O, then PV(j - 1) from the V
+//    fragments `vf` (read from LDS at the end of the previous iteration) and
+//    the weights `pp`;
+//  * softmax(j) of the scores `sc` -> weights, left in `pp`: the reference
+//    max is raised lazily (only when a score exceeds it by more than
+//    2^kSlack), and the factors alpha that rescale O wait in the wave state;
+//  * QK(j + 1) from the K slot `knext` -> `sc`;
+//  * read V(j) from `vcur` into `vf` for the next iteration's PV, so that the
+//    PV MFMAs never wait for LDS.
+// A wave issues in order, so MFMA and VALU work overlap only where they
+// alternate in the instruction stream: the softmax is cut into steps, and
+// after each step the next MFMAs of the iteration are issued (PV first, its
+// operands are already in registers; then QK, whose K fragments have been in
+// flight since the top). sched_barrier keeps the compiler from regrouping.
+template <int D, int NT, bool QK, bool PV, bool VN>
+__device__ __forceinline__ void bf_iter(BfWave<D, NT>& w, f32x16 (&sc)[NT], bf16x8 (&pp)[NT][2],
+                                        bf16x8 (&vf)[2][D / 32], const char* knext, const char* vcur, int kb,
+                                        int kh, int lane, const TreeAttnArgs& a) {
+  constexpr int NPV = PV ? 2 * (D / 32) * NT : 0;  // k-steps x head_dim tiles x row tiles
+  constexpr int NQK = QK ? (D / 16) * NT : 0;      // k-steps x row tiles
+  constexpr int NM = NPV + NQK;
+  constexpr int NSTEP = 7 * NT + 2;
+  bf16x8 kf[D / 16];
+  float x[NT][16];
+  // The two branches (rare rescale, tree mask) come first.
+  if constexpr (PV) bf_rescale<D, NT>(w);
+  bf_scores<D, NT>(w, sc, x, kb, lane >> 5, a);
+  if constexpr (QK) bf_read_k<D>(kf, knext, kh, lane);
+
+  f32x16 sn[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) sn[nt] = f32x16{};
+  int issued = 0;
+  auto mfma_upto = [&](int target) {
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      if (i < issued || i >= target) continue;
+      if (i < NPV) {
+        const int ks = i / ((D / 32) * NT), dt = (i / NT) % (D / 32), nt = i % NT;
+        w.o[nt][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ks][dt], pp[nt][ks], w.o[nt][dt], 0, 0, 0);
+      } else {
+        const int k = i - NPV, cc = k / NT, nt = k % NT;
+        sn[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[cc], w.qf[nt][cc], sn[nt], 0, 0, 0);
+      }
+    }
+    issued = target > issued ? target : issued;
+  };
+  int step = 0;
+  auto step_done = [&]() {  // after each softmax step: the MFMAs up to its share
+    ++step;
+    mfma_upto((NM * step) / NSTEP);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
   const float c = a.scale_log2;
-  const float mx[2] = {mt * c, mt2 * c};
+  float mx[NT], nm[NT];
+  // Row maxima over this lane's 16 keys, then over both lane halves.
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    mx[nt] = max16(x[nt]);
+    step_done();
+  }
+  if constexpr (NT == 2) {
+    swap32(mx[0], mx[1]);
+    float mt = vmax(mx[0], mx[1]), mt2 = mt;  // lanes 0-31: tile 0's max; 32-63: tile 1's
+    swap32(mt, mt2);                          // mt: tile 0's max everywhere, mt2: tile 1's
+    mx[0] = mt;
+    mx[1] = mt2;
+  } else {
+    float lo = mx[0], hi = mx[0];
+    swap32(lo, hi);  // lo: the low half's max everywhere, hi: the high half's
+    mx[0] = vmax(lo, hi);
+  }
   bool bump_any = false;
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const bool bump = mx[nt] > w.m_ref[nt] + kSlack;
-    const float al = __builtin_amdgcn_exp2f(w.m_ref[nt] - mx[nt]);  // 0 on the first visible keys
+  for (int nt = 0; nt < NT; ++nt) {
+    const float m = mx[nt] * c;
+    const bool bump = m > w.m_ref[nt] + kSlack;
+    const float al = __builtin_amdgcn_exp2f(w.m_ref[nt] - m);  // 0 on the first visible keys
     w.alpha[nt] = bump ? al : 1.f;
-    w.m_ref[nt] = bump ? mx[nt] : w.m_ref[nt];
+    w.m_ref[nt] = bump ? m : w.m_ref[nt];
     bump_any |= bump;
-    const float nm = w.m_ref[nt] == kNegInf ? 0.f : -w.m_ref[nt];
+    nm[nt] = w.m_ref[nt] == kNegInf ? 0.f : -w.m_ref[nt];
+  }
+  step_done();
+  // The weights, 4 per step.
 #pragma unroll
-    for (int j = 0; j < 16; ++j) x[nt][j] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[nt][j], c, nm));
+  for (int e = 0; e < 4 * NT; ++e) {
+    const int nt = e / 4, j0 = 4 * (e % 4);
+#pragma unroll
+    for (int j = j0; j < j0 + 4; ++j) x[nt][j] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[nt][j], c, nm[nt]));
+    step_done();
+  }
+  // Row sums, bf16 weights, the rescale flag.
+  bf16x8 pn[NT][2];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
     w.l_run[nt] = w.l_run[nt] * w.alpha[nt] + sum16(x[nt]);
+    step_done();
+  }
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int q = 0; q < 8; ++q) p[nt][ks][q] = static_cast<__bf16>(x[nt][8 * ks + q]);
+      for (int q = 0; q < 8; ++q) pn[nt][ks][q] = static_cast<__bf16>(x[nt][8 * ks + q]);
+    step_done();
   }
   w.pend = __ballot(bump_any) != 0;
-}
-
-// One pipeline iteration on stage s: softmax of s (scores in `sc`), QK of
-// s + 1 from `knext` (when QK), PV of s - 1 from `vprev` with its weights
-// `pp` (when PV). On return sc holds the scores of s + 1 and pp the weights
-// of s. The rescale owed by softmax(s - 1) is settled first: O then holds
-// stages up to s - 2 against the reference of s - 1, as PV(s - 1) needs.
-// The softmax, PV and QK form one straight-line block whose MFMAs are spread
-// evenly through the VALU work (a wave issues in order, so MFMA and VALU only
-// overlap when they alternate in the instruction stream).
-template <int D, bool QK, bool PV>
-__device__ __forceinline__ void bf_iter(BfWave<D>& w, f32x16 (&sc)[2], bf16x8 (&pp)[2][2], const char* knext,
-                                        const char* vprev, int kb, int kh, int lane, const TreeAttnArgs& a) {
-  bf16x8 kf[D / 16];
-  bf16x8 vf[2][D / 32];
-  if constexpr (PV) bf_rescale<D>(w);
-  if constexpr (PV) bf_read_v<D>(vf, vprev, kh, lane);
-  if constexpr (QK) bf_read_k<D>(kf, knext, kh, lane);
-  bf16x8 pn[2][2];
-  bf_softmax<D>(w, sc, pn, kb, lane >> 5, a);
-  if constexpr (PV) bf_pv<D>(w, vf, pp);
-  if constexpr (QK) bf_qk<D>(sc, kf, w);
-  constexpr int kMfma = (QK ? D / 8 : 0) + (PV ? D / 8 : 0);
-  if constexpr (kMfma > 0) {
-    // 0x008 MFMA, 0x002 VALU: start with VALU (the max needs no LDS data),
-    // then one MFMA per few VALU instructions.
-    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+  step_done();
+  mfma_upto(NM);
 #pragma unroll
-    for (int i = 0; i < kMfma; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
-    }
-  }
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
+  for (int nt = 0; nt < NT; ++nt) {
     pp[nt][0] = pn[nt][0];
     pp[nt][1] = pn[nt][1];
+    if constexpr (QK) sc[nt] = sn[nt];
   }
+  if constexpr (VN) bf_read_v<D>(vf, vcur, kh, lane);
 }
 
-template <int D>
-__global__ __launch_bounds__(kBfThreads)
-__attribute__((amdgpu_waves_per_eu(1, 1)))  // one wave per SIMD, up to 512 registers
+template <int D, int NT>
+__global__ __launch_bounds__(kBfThreads<NT>)
+__attribute__((amdgpu_waves_per_eu(kBfWaves<NT> / 4, kBfWaves<NT> / 4)))  // waves per SIMD
 void tree_attn_bf16_kernel(const TreeAttnArgs a) {
   using G = BfGeo<D>;
   __shared__ __attribute__((aligned(1024))) char lds[G::LDS];
@@ -933,37 +1014,51 @@ void tree_attn_bf16_kernel(const TreeAttnArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, l32 = lane & 31;
-  const int rg = wave & 1, kh = wave >> 1;  // row group, key half
+  constexpr int NW = kBfWaves<NT>, RW = NW / 2;  // waves, row groups
+  const int rg = wave % RW, kh = wave / RW;      // row group, key half
   const __bf16* kh_ptr = static_cast<const __bf16*>(a.k) + (size_t)g * a.kv_head_stride;
   const __bf16* vh_ptr = static_cast<const __bf16*>(a.v) + (size_t)g * a.kv_head_stride;
   char* const kring = lds;
   char* const vring = lds + G::VRING;
-  auto kslot = [&](int j) { return kring + (j & (kRing - 1)) * G::SLOT; };
-  auto vslot = [&](int j) { return vring + (j & (kRing - 1)) * G::SLOT; };
-  auto dma_k = [&](int j) { bf_dma_slot<D>(kslot(j), kh_ptr, (t0 + j) * 64, a.total_keys, wave, lane); };
-  auto dma_v = [&](int j) { bf_dma_slot<D>(vslot(j), vh_ptr, (t0 + j) * 64, a.total_keys, wave, lane); };
-
-  // DMA issue order (j = stage index within the split): Q and ancestors, K0..K3,
-  // V0, V1; then iteration j issues K(j+4) and V(j+2). Iteration j needs K(j+1)
-  // and V(j-1); the waits below count the DMA instructions issued after the
-  // newest of those, which may stay in flight.
-  bf_dma_q_anc<D>(lds, a, g, rb, wave, lane);
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    if (j < n) dma_k(j);
-  dma_v(0);
-  if (1 < n) dma_v(1);
-  auto iter_ops = [&](int j) {  // DMA instructions iteration j issues (j = -1: V1 of the prologue)
-    if (j < 0) return G::OPS;
-    return G::OPS * ((j + 4 < n) + (j + 2 < n));
+  auto kslot = [&](int j) { return kring + (j & (kRing - 1)) * G::KSLOT; };
+  auto vslot = [&](int j) { return vring + (j & (kRing - 1)) * G::VSLOT; };
+  constexpr int KW = (G::KS + NW - 1) / NW, VW = (G::VS + NW - 1) / NW;  // DMA ops per wave (at most)
+  int koff[KW], voff[VW];
+  bf_dma_offsets<D, G::KS, KW, NW>(koff, wave, lane);
+  bf_dma_offsets<D, G::VS, VW, NW>(voff, wave, lane);
+  auto dma_k = [&](int j) {
+    bf_dma_slot<D, G::KS, KW, NW>(kslot(j), kh_ptr, (t0 + j) * 64, a.total_keys, koff, wave);
+  };
+  auto dma_v = [&](int j) {
+    bf_dma_slot<D, G::VS, VW, NW>(vslot(j), vh_ptr, (t0 + j) * 64, a.total_keys, voff, wave);
   };
 
-  BfWave<D> w;
-  int node[2], head[2];
-  bool row_ok[2];
+  // DMA issue order (j = stage index within the split): Q and ancestors, K0,
+  // K1, K2, V0, V1, V2; iteration 0 issues K3, K4, V3 (over the Q staging
+  // areas, after Q has been read); iteration j >= 1 issues K(j+4), V(j+3).
+  // Iteration j needs K(j+1) and V(j); each wait counts the DMA instructions
+  // issued after the newest of those, which may stay in flight.
+  bf_dma_q_anc<D, NW>(lds, a, g, rb, wave, lane);
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int row = rb * kBlockRows + 32 * (2 * rg + nt) + l32;
+  for (int j = 0; j < 3; ++j)
+    if (j < n) dma_k(j);
+#pragma unroll
+  for (int j = 0; j < 3; ++j)
+    if (j < n) dma_v(j);
+  // DMA instructions this wave issues per K (V) stage: ops NW o + wave < KS (VS).
+  const int KO = (G::KS - wave + NW - 1) / NW;
+  const int VO = (G::VS - wave + NW - 1) / NW;
+  auto iter_ops = [&](int j) {  // DMA instructions iteration j issues
+    if (j == 0) return KO * ((3 < n) + (4 < n)) + VO * (3 < n);
+    return KO * (j + 4 < n) + VO * (j + 3 < n);
+  };
+
+  BfWave<D, NT> w;
+  int node[NT], head[NT];
+  bool row_ok[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int row = rb * kBlockRows + 32 * (NT * rg + nt) + l32;
     row_ok[nt] = row < a.rows_per_head;
     node[nt] = row_ok[nt] ? row / a.group : 0;
     head[nt] = g * a.group + (row_ok[nt] ? row % a.group : 0);
@@ -976,57 +1071,56 @@ void tree_attn_bf16_kernel(const TreeAttnArgs a) {
   w.pend = false;
 
   // Q, the ancestors and K0 have landed: read Q and the ancestor bits, QK(0).
-  wait_vm_atmost(G::OPS * ((n > 1) + (n > 2) + (n > 3) + 1 + (n > 1)));
+  wait_vm_atmost(KO * ((n > 1) + (n > 2)) + VO * (1 + (n > 1) + (n > 2)));
   bf_barrier();
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int row = 32 * (2 * rg + nt) + l32;
-    const char* qr = lds + G::QSTAGE + row * G::ROWB;
-    const int sw = bf_swz<D>(row);
+  for (int nt = 0; nt < NT; ++nt) {
+    const int row = 32 * (NT * rg + nt) + l32;
+    const char* qr = lds + (row < 64 ? G::QSTAGE0 : G::QSTAGE1) + (row & 63) * (G::KS * 16) + half * 16;
 #pragma unroll
-    for (int cc = 0; cc < D / 16; ++cc)
-      w.qf[nt][cc] = *reinterpret_cast<const bf16x8*>(qr + (((2 * cc + half) ^ sw) << 4));
+    for (int cc = 0; cc < D / 16; ++cc) w.qf[nt][cc] = *reinterpret_cast<const bf16x8*>(qr + 32 * cc);
     w.anc[nt] = row_ok[nt] ? reinterpret_cast<const uint64_t*>(lds + G::ANC)[node[nt]] : 0;
   }
-  f32x16 sc[2];
-  bf16x8 pp[2][2];
+  f32x16 sc[NT];
+  bf16x8 pp[NT][2];
+  bf16x8 vf[2][D / 32];
   {
     bf16x8 kf[D / 16];
     bf_read_k<D>(kf, kslot(0), kh, lane);
-    bf_qk<D>(sc, kf, w);
+    bf_qk<D, NT>(sc, kf, w);
   }
+  auto kb_of = [&](int j) { return (t0 + j) * 64 + 32 * kh; };
 
-  // Iteration 0: softmax(0) and QK(1); no PV yet.
-  wait_vm_atmost(G::OPS * ((n > 2) + (n > 3) + 1 + (n > 1)));
-  bf_barrier();
+  // Iteration 0: softmax(0), QK(1), read V(0); no PV yet. Needs K1 and V0.
+  wait_vm_atmost(VO * ((n > 1) + (n > 2)));
+  bf_barrier();  // Q has been read by every wave: its staging slots are free
+  if (3 < n) dma_k(3);
   if (4 < n) dma_k(4);
-  if (2 < n) dma_v(2);  // over the Q staging area: Q was read before the barrier
+  if (3 < n) dma_v(3);
   if (n > 1)
-    bf_iter<D, true, false>(w, sc, pp, kslot(1), nullptr, t0 * 64 + 32 * kh, kh, lane, a);
+    bf_iter<D, NT, true, false, true>(w, sc, pp, vf, kslot(1), vslot(0), kb_of(0), kh, lane, a);
   else
-    bf_iter<D, false, false>(w, sc, pp, nullptr, nullptr, t0 * 64 + 32 * kh, kh, lane, a);
-  // Steady state.
+    bf_iter<D, NT, false, false, true>(w, sc, pp, vf, nullptr, vslot(0), kb_of(0), kh, lane, a);
+  // Steady state: iteration j needs K(j+1) and V(j).
   for (int j = 1; j < n - 1; ++j) {
-    wait_vm_atmost(iter_ops(j - 2) + iter_ops(j - 1));
+    int after;  // DMA instructions issued after the newest one needed
+    if (j == 1) after = VO * (n > 2) + iter_ops(0);
+    else if (j == 2) after = (n > 3 ? KO * (n > 4) + VO : 0) + iter_ops(1);
+    else after = iter_ops(j - 2) + iter_ops(j - 1);
+    wait_vm_atmost(after);
     bf_barrier();
     if (j + 4 < n) dma_k(j + 4);
-    if (j + 2 < n) dma_v(j + 2);
-    bf_iter<D, true, true>(w, sc, pp, kslot(j + 1), vslot(j - 1), (t0 + j) * 64 + 32 * kh, kh, lane, a);
+    if (j + 3 < n) dma_v(j + 3);
+    bf_iter<D, NT, true, true, true>(w, sc, pp, vf, kslot(j + 1), vslot(j), kb_of(j), kh, lane, a);
   }
-  // Last iteration: softmax(n-1) and PV(n-2); then PV(n-1).
+  // Last iteration (j = n - 1): PV(n-2), softmax(n-1), read V(n-1); no DMA left.
   if (n > 1) {
-    wait_vm_atmost(iter_ops(n - 3) + iter_ops(n - 2));
+    TA_WAIT_VM(0);
     bf_barrier();
-    bf_iter<D, false, true>(w, sc, pp, nullptr, vslot(n - 2), (t0 + n - 1) * 64 + 32 * kh, kh, lane, a);
+    bf_iter<D, NT, false, true, true>(w, sc, pp, vf, nullptr, vslot(n - 1), kb_of(n - 1), kh, lane, a);
   }
-  TA_WAIT_VM(0);
-  bf_barrier();
-  {
-    bf16x8 vf[2][D / 32];
-    bf_read_v<D>(vf, vslot(n - 1), kh, lane);
-    bf_rescale<D>(w);
-    bf_pv<D>(w, vf, pp);
-  }
+  bf_rescale<D, NT>(w);
+  bf_pv<D, NT>(w, vf, pp);
   __syncthreads();  // every wave is done with the rings: reuse them below
 
   // Merge the two key halves: waves kh = 1 hand (m, l, O) to waves kh = 0
@@ -1035,13 +1129,13 @@ void tree_attn_bf16_kernel(const TreeAttnArgs a) {
   constexpr int TILE_F4 = 32 * D / 4;
   f32x4* xo = reinterpret_cast<f32x4*>(lds);
   float2* xml = reinterpret_cast<float2*>(lds + 4 * TILE_F4 * 16);
-  float l_tot[2];
+  float l_tot[NT];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) l_tot[nt] = w.l_run[nt] + __shfl_xor(w.l_run[nt], 32);
+  for (int nt = 0; nt < NT; ++nt) l_tot[nt] = w.l_run[nt] + __shfl_xor(w.l_run[nt], 32);
   if (kh == 1) {
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int t = 2 * rg + nt;
+    for (int nt = 0; nt < NT; ++nt) {
+      const int t = NT * rg + nt;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -1054,8 +1148,8 @@ void tree_attn_bf16_kernel(const TreeAttnArgs a) {
   __syncthreads();
   if (kh == 0) {
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int t = 2 * rg + nt;
+    for (int nt = 0; nt < NT; ++nt) {
+      const int t = NT * rg + nt;
       const float2 other = xml[t * 32 + l32];
       const float M = fmaxf(w.m_ref[nt], other.x);
       const float w0 = w.m_ref[nt] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(w.m_ref[nt] - M);
@@ -1073,7 +1167,7 @@ void tree_attn_bf16_kernel(const TreeAttnArgs a) {
     }
     if (a.splits == 1) {
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
+      for (int nt = 0; nt < NT; ++nt) {
         if (!row_ok[nt]) continue;
         __bf16* orow = static_cast<__bf16*>(a.out) + ((size_t)node[nt] * a.n_q_heads + head[nt]) * D;
         const float inv = 1.f / l_tot[nt];
@@ -1088,8 +1182,8 @@ void tree_attn_bf16_kernel(const TreeAttnArgs a) {
     } else {
       const PartialSink sink = partial_sink<D>(a, u);
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const int t = 2 * rg + nt;  // 32-row tile of the block
+      for (int nt = 0; nt < NT; ++nt) {
+        const int t = NT * rg + nt;  // 32-row tile of the block
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -1102,7 +1196,7 @@ void tree_attn_bf16_kernel(const TreeAttnArgs a) {
     }
   }
   if (a.splits == 1) return;
-  split_handoff<__bf16, D, kBfThreads>(a, lds, &s_flags, &s_taken, grp, g, rb, split, tid);
+  split_handoff<__bf16, D, kBfThreads<NT>>(a, lds, &s_flags, &s_taken, grp, g, rb, split, tid);
 }
 
 }  // namespace
@@ -1112,9 +1206,9 @@ hipError_t launch_tree_attn(const TreeAttnArgs& a, int32_t dtype, int32_t head_d
   const dim3 grid(a.n_units), block(kThreads);
   if (dtype == 1) {
     if (head_dim == 128)
-      hipLaunchKernelGGL((tree_attn_bf16_kernel<128>), grid, dim3(kBfThreads), 0, stream, a);
+      hipLaunchKernelGGL((tree_attn_bf16_kernel<128, TA_BF16_NT>), grid, dim3(kBfThreads<TA_BF16_NT>), 0, stream, a);
     else
-      hipLaunchKernelGGL((tree_attn_bf16_kernel<64>), grid, dim3(kBfThreads), 0, stream, a);
+      hipLaunchKernelGGL((tree_attn_bf16_kernel<64, TA_BF16_NT>), grid, dim3(kBfThreads<TA_BF16_NT>), 0, stream, a);
   } else {
     if (head_dim == 128)
       hipLaunchKernelGGL((tree_attn_kernel<float, 128>), grid, block, 0, stream, a);
