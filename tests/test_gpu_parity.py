@@ -225,3 +225,22 @@ def test_reroot_then_attend_equals_attend_on_gpu():
         after = ta.tree_attn(q[surv].contiguous(), k, v, new_p, new_par)
         torch.cuda.synchronize()
         check_close(W.to_f64(after), W.to_f64(before[surv]), "bf16", "re-rooted survivors")
+
+
+@pytest.mark.parametrize("polls", [0, 1])
+def test_split_merge_when_splits_stop_waiting(polls):
+    """With the wait bound forced down from the host, splits leave their row
+    slices to the last arrival (the give-up path of the hand-off); the
+    result must not change."""
+    cfg = W.config("llama3_8b_verify")
+    say(f"[give-up] {cfg['name']} wait polls {polls}")
+    x = W.make_inputs(cfg)
+    ta.set_split_wait_limit(polls)
+    try:
+        got = gpu_attn(x)
+        again = gpu_attn(x)
+    finally:
+        ta.set_split_wait_limit(20000)
+    ref = ref_attn(x, cfg["n_kv_heads"])
+    check_close(got, ref, cfg["dtype"], f"give-up polls={polls}")
+    check_close(again, ref, cfg["dtype"], f"give-up polls={polls}, second call")

@@ -40,7 +40,7 @@ struct AttnPlan {
   // at offset 0 in a fixed-size region, whatever the shape, so a workspace
   // that calls of different shapes share never finds partial data of an
   // earlier call where it expects a counter.
-  size_t ws_cnt_offset = 0;    // int32 x4 per group: arrivals, departures, claim bits, pad
+  size_t ws_cnt_offset = 0;    // int32 x4 per group: arrivals, departures, give-up bits, pad
   size_t ws_ml_offset = 0;     // fp32 (max, sum) pairs [units][kRowsPerBlock][2]
   size_t ws_o_offset = 0;      // fp32 partial outputs [units][kRowsPerBlock][head_dim]
   size_t ws_bytes = 0;
@@ -52,9 +52,9 @@ constexpr int32_t kRowsPerWave = 32;   // query rows per wave (one 32-wide MFMA 
 constexpr int32_t kRowsPerBlock = kWaves * kRowsPerWave;
 constexpr int32_t kTargetUnits = 512;  // 2 workgroups per CU on a 256-CU part
 constexpr int32_t kMinTilesPerSplit = 2;
-constexpr int32_t kMaxSplits = 32;     // one claim bit per split in a 32-bit word
+constexpr int32_t kMaxSplits = 32;     // one give-up bit per split in a 32-bit word
 constexpr int32_t kMaxGroups = 4096;   // (KV head, row block) groups with counters
-constexpr int32_t kGroupWords = 4;     // arrivals, departures, claim bits, pad
+constexpr int32_t kGroupWords = 4;     // arrivals, departures, give-up bits, pad
 constexpr size_t kCounterBytes = kMaxGroups * kGroupWords * sizeof(int32_t);
 
 ta_status plan_tree_attn(const ta_kv_cache* cache, int32_t n_q_heads, int32_t prefix_len,

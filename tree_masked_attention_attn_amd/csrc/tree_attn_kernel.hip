@@ -310,92 +310,94 @@ __device__ __forceinline__ void put_ml(const PartialSink& k, int r, float m, flo
   __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, make_float2(m, l)), k.ml, r * 8, 0, kWriteThrough);
 }
 
-// Merge rows [r0, r1) of row block `grp` from all splits, in split order, and
-// write them to `out`. Weights exp2(m_s - M) / L go through LDS once per row.
+// Merge rows [r0, r1) of row block `grp` from all splits and write them to
+// `out`. One memory round trip per 8 splits: each thread loads, for its
+// (row, float4 of head_dim), every split's (max, sum) pair and partial in one
+// batch, then combines them online in split order (deterministic for a
+// given shape): M is the running max, acc and L are rescaled by 2^(M_old - M).
 template <typename T, int D, int NTH>
-__device__ void merge_rows(const TreeAttnArgs& a, char* smem, int grp, int g, int rb, int r0, int r1,
-                           int tid) {
+__device__ void merge_rows(const TreeAttnArgs& a, int grp, int g, int rb, int r0, int r1, int tid) {
+  constexpr int C4 = D / 4;  // float4 chunks per row
   const int S = a.splits, nr = r1 - r0;
   const size_t u0 = (size_t)grp * S;
-  float2* ml = reinterpret_cast<float2*>(smem);            // [S][nr]
-  float* w = reinterpret_cast<float*>(smem) + 2 * S * nr;  // [S][nr]
-  for (int i = tid; i < S * nr; i += NTH)
-    ml[i] = a.ws_ml[(u0 + i / nr) * kBlockRows + r0 + i % nr];
-  __syncthreads();
-  for (int r = tid; r < nr; r += NTH) {
-    float M = kNegInf;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, ml[s * nr + r].x);
-    float L = 0.f;
-    for (int s = 0; s < S; ++s) {
-      const float2 x = ml[s * nr + r];
-      const float e = x.x == kNegInf ? 0.f : __builtin_amdgcn_exp2f(x.x - M);
-      w[s * nr + r] = e;
-      L += e * x.y;
-    }
-    const float inv = 1.f / L;
-    for (int s = 0; s < S; ++s) w[s * nr + r] *= inv;
-  }
-  __syncthreads();
-  constexpr int C4 = D / 4;  // float4 chunks per row
   const f32x4* parts = reinterpret_cast<const f32x4*>(a.ws_o) + u0 * kBlockRows * C4;
+  const float2* mls = a.ws_ml + u0 * kBlockRows;
   for (int it = tid; it < nr * C4; it += NTH) {
-    const int r = it / C4, c = it % C4;
-    const int hrow = rb * kBlockRows + r0 + r;
+    const int br = r0 + it / C4, c = it % C4;  // block row, float4 column
+    const int hrow = rb * kBlockRows + br;
     if (hrow >= a.rows_per_head) continue;
-    const f32x4* src = parts + part_index<D>(r0 + r, c);
-    f32x4 acc = {0, 0, 0, 0};
-#pragma unroll 8
-    for (int s = 0; s < S; ++s) acc += w[s * nr + r] * src[(size_t)s * kBlockRows * C4];
+    const f32x4* src = parts + part_index<D>(br, c);
+    float M = kNegInf, L = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < S; s0 += 8) {
+      float2 ml[8];
+      f32x4 o[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        if (s0 + k < S) {
+          ml[k] = mls[(size_t)(s0 + k) * kBlockRows + br];
+          o[k] = src[(size_t)(s0 + k) * kBlockRows * C4];
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        if (s0 + k >= S || ml[k].x == kNegInf) continue;  // a split with no visible key adds nothing
+        const float Mn = fmaxf(M, ml[k].x);
+        const float sa = M == kNegInf ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
+        const float sb = __builtin_amdgcn_exp2f(ml[k].x - Mn);
+        acc = acc * sa + o[k] * sb;
+        L = L * sa + ml[k].y * sb;
+        M = Mn;
+      }
+    }
     const int nd = hrow / a.group, hd = g * a.group + hrow % a.group;
-    store4<T>(static_cast<T*>(a.out) + ((size_t)nd * a.n_q_heads + hd) * D + 4 * c, acc);
+    store4<T>(static_cast<T*>(a.out) + ((size_t)nd * a.n_q_heads + hd) * D + 4 * c, acc * (1.f / L));
   }
-  __syncthreads();  // LDS is reused by the next merge
 }
 
 // Cross-workgroup hand-off of one split, after its partial rows and (max,
-// sum) pairs are in the workspace (no grid barrier, no second launch):
-//  * release (agent scope, by one thread after the workgroup barrier: fences
-//    are cumulative, so one L2 write-back serves the whole workgroup), then
-//    count in; every split then waits a bounded number of polls for the
-//    others; the last to arrive never waits;
-//  * merge: row slice j of the block belongs to split j. A split that saw
-//    everyone arrive claims its own slice (one bit per slice, atomic OR); the
-//    last arrival then claims every slice still unclaimed, which covers
-//    splits that stopped waiting. Each slice is merged exactly once;
-//  * count out; the last one out clears the group's words for the next call.
+// sum) pairs are in the workspace (no grid barrier, no second launch). One
+// thread per workgroup:
+//  * counts in with a sequentially consistent add, which also releases the
+//    split's partials (stored through to memory, so the release is cheap);
+//  * waits a bounded number of polls for the other splits; the last to
+//    arrive never waits;
+//  * a split that saw everyone arrive merges its own row slice (slice j of
+//    the block belongs to split j). One that stopped waiting marks itself in
+//    the give-up mask and looks once more; the last arrival merges its own
+//    slice and every slice in that mask. Both sides use sequentially
+//    consistent operations, so at least one of them covers each slice; a
+//    slice merged twice is written twice with the same bytes;
+//  * counts out; the last one out clears the group's words for the next call.
 template <typename T, int D, int NTH>
-__device__ void split_handoff(const TreeAttnArgs& a, char* smem, int* s_flags, int* s_taken,
-                              int grp, int g, int rb, int split, int tid) {
+__device__ void split_handoff(const TreeAttnArgs& a, int* s_flags, int* s_mask, int grp, int g, int rb,
+                              int split, int tid) {
   __syncthreads();
-  int* gw = a.ws_cnt + (size_t)grp * 4;  // [0] arrivals, [1] departures, [2] claim bits
+  int* gw = a.ws_cnt + (size_t)grp * 4;  // [0] arrivals, [1] departures, [2] give-up bits
   if (tid == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    const int old = __hip_atomic_fetch_add(gw, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int old = __hip_atomic_fetch_add(gw, 1, __ATOMIC_SEQ_CST, __HIP_MEMORY_SCOPE_AGENT);
     const bool last = old == a.splits - 1;
     bool all_in = last;
     for (int it = 0; !all_in && it < a.wait_polls; ++it) {
       __builtin_amdgcn_s_sleep(2);
       all_in = __hip_atomic_load(gw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.splits;
     }
+    if (!all_in) {
+      __hip_atomic_fetch_or(gw + 2, 1 << split, __ATOMIC_SEQ_CST, __HIP_MEMORY_SCOPE_AGENT);
+      all_in = __hip_atomic_load(gw, __ATOMIC_SEQ_CST, __HIP_MEMORY_SCOPE_AGENT) == a.splits;
+    }
+    int others = 0;
+    if (last) others = __hip_atomic_load(gw + 2, __ATOMIC_SEQ_CST, __HIP_MEMORY_SCOPE_AGENT) & ~(1 << split);
     if (all_in) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // invalidates this CU's L1 too
-    *s_flags = (last ? 2 : 0) | (all_in ? 1 : 0);
+    *s_flags = all_in ? 1 : 0;
+    *s_mask = others;
   }
   __syncthreads();
-  const int flags = *s_flags;
-  if (flags & 1) {
-    const int sweep = (flags & 2) ? a.splits : 1;
-    for (int k = 0; k < sweep; ++k) {
-      const int j = (split + k) % a.splits;
-      if (tid == 0) {
-        const int old = __hip_atomic_fetch_or(gw + 2, 1 << j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        *s_taken = (old >> j) & 1;
-      }
-      __syncthreads();
-      const bool taken = *s_taken;
-      __syncthreads();
-      if (!taken)
-        merge_rows<T, D, NTH>(a, smem, grp, g, rb, j * kBlockRows / a.splits, (j + 1) * kBlockRows / a.splits, tid);
-    }
+  if (*s_flags) {
+    const int others = *s_mask;
+    for (int j = 0; j < a.splits; ++j)
+      if (j == split || ((others >> j) & 1))
+        merge_rows<T, D, NTH>(a, grp, g, rb, j * kBlockRows / a.splits, (j + 1) * kBlockRows / a.splits, tid);
   }
   __syncthreads();
   if (tid == 0) {
@@ -547,7 +549,7 @@ void tree_attn_kernel(const TreeAttnArgs a) {
                     f32x4{o[dt][4 * jq], o[dt][4 * jq + 1], o[dt][4 * jq + 2], o[dt][4 * jq + 3]});
     if (half == 0) put_ml(sink, rloc, m_ref, l_tot);
   }
-  split_handoff<T, D, kThreads>(a, smem, &s_flags, &s_taken, grp, g, rb, split, tid);
+  split_handoff<T, D, kThreads>(a, &s_flags, &s_taken, grp, g, rb, split, tid);
 }
 
 // ============================================================================
@@ -1196,7 +1198,7 @@ void tree_attn_bf16_kernel(const TreeAttnArgs a) {
     }
   }
   if (a.splits == 1) return;
-  split_handoff<__bf16, D, kBfThreads<NT>>(a, lds, &s_flags, &s_taken, grp, g, rb, split, tid);
+  split_handoff<__bf16, D, kBfThreads<NT>>(a, &s_flags, &s_taken, grp, g, rb, split, tid);
 }
 
 }  // namespace
