@@ -116,7 +116,8 @@ ta_status plan_tree_attn(const ta_kv_cache* cache, int32_t n_q_heads, int32_t pr
     p.ws_ml_offset = kCounterBytes;
     const size_t ml_bytes = units * kRowsPerBlock * 2 * sizeof(float);
     p.ws_o_offset = align_up(p.ws_ml_offset + ml_bytes, 256);
-    const size_t o_bytes = units * kRowsPerBlock * p.head_dim * sizeof(float);
+    // partial rows: fp32 for fp32 caches, row-normalised fp16 for bf16 caches
+    const size_t o_bytes = units * kRowsPerBlock * p.head_dim * (cache->dtype == TA_BF16 ? 2 : 4);
     p.ws_bytes = align_up(p.ws_o_offset + o_bytes, 256);
   }
   *plan = p;

@@ -42,7 +42,7 @@ struct AttnPlan {
   // earlier call where it expects a counter.
   size_t ws_cnt_offset = 0;    // int32 x4 per group: arrivals, departures, give-up bits, pad
   size_t ws_ml_offset = 0;     // fp32 (max, sum) pairs [units][kRowsPerBlock][2]
-  size_t ws_o_offset = 0;      // fp32 partial outputs [units][kRowsPerBlock][head_dim]
+  size_t ws_o_offset = 0;      // partial outputs [units][kRowsPerBlock][head_dim]: fp32, or fp16 for bf16
   size_t ws_bytes = 0;
 };
 

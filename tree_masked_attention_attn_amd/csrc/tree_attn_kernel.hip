@@ -292,10 +292,12 @@ struct PartialSink {
   __amdgpu_buffer_rsrc_t o, ml;
 };
 
-template <int D>
+// PT: element type of the partial rows (float, or _Float16 for the bf16 path).
+template <int D, typename PT>
 __device__ __forceinline__ PartialSink partial_sink(const TreeAttnArgs& a, int u) {
   PartialSink k;
-  k.o = __builtin_amdgcn_make_buffer_rsrc(a.ws_o + (size_t)u * kBlockRows * D, 0, kBlockRows * D * 4, 0x00020000);
+  const char* o = reinterpret_cast<const char*>(a.ws_o) + (size_t)u * kBlockRows * D * sizeof(PT);
+  k.o = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(o), 0, kBlockRows * D * (int)sizeof(PT), 0x00020000);
   k.ml = __builtin_amdgcn_make_buffer_rsrc(a.ws_ml + (size_t)u * kBlockRows, 0, kBlockRows * 8, 0x00020000);
   return k;
 }
@@ -305,28 +307,39 @@ __device__ __forceinline__ void put_partial(const PartialSink& k, int i, f32x4 v
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), k.o, i * 16, 0, kWriteThrough);
 }
 
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+// ... the same four values as fp16 (8 bytes)
+__device__ __forceinline__ void put_partial_h(const PartialSink& k, int i, f32x4 v) {
+  const f16x4 h = {static_cast<_Float16>(v[0]), static_cast<_Float16>(v[1]), static_cast<_Float16>(v[2]),
+                   static_cast<_Float16>(v[3])};
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, h), k.o, i * 8, 0, kWriteThrough);
+}
+
 // (reference max, sum) of block row r
 __device__ __forceinline__ void put_ml(const PartialSink& k, int r, float m, float l) {
   __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, make_float2(m, l)), k.ml, r * 8, 0, kWriteThrough);
 }
 
 // Merge rows [r0, r1) of row block `grp` from all splits and write them to
-// `out`. One memory round trip per 8 splits: each thread loads, for its
+// `out` (PT: element type of the partial rows). One memory round trip per 8
+// splits: each thread loads, for its
 // (row, float4 of head_dim), every split's (max, sum) pair and partial in one
 // batch, then combines them online in split order (deterministic for a
 // given shape): M is the running max, acc and L are rescaled by 2^(M_old - M).
-template <typename T, int D, int NTH>
+template <typename T, typename PT, int D, int NTH>
 __device__ void merge_rows(const TreeAttnArgs& a, int grp, int g, int rb, int r0, int r1, int tid) {
-  constexpr int C4 = D / 4;  // float4 chunks per row
+  constexpr int C4 = D / 4;  // chunks of 4 values per row
+  using V4 = std::conditional_t<std::is_same_v<PT, float>, f32x4, f16x4>;
   const int S = a.splits, nr = r1 - r0;
   const size_t u0 = (size_t)grp * S;
-  const f32x4* parts = reinterpret_cast<const f32x4*>(a.ws_o) + u0 * kBlockRows * C4;
+  const V4* parts = reinterpret_cast<const V4*>(a.ws_o) + u0 * kBlockRows * C4;
   const float2* mls = a.ws_ml + u0 * kBlockRows;
   for (int it = tid; it < nr * C4; it += NTH) {
     const int br = r0 + it / C4, c = it % C4;  // block row, float4 column
     const int hrow = rb * kBlockRows + br;
     if (hrow >= a.rows_per_head) continue;
-    const f32x4* src = parts + part_index<D>(br, c);
+    const V4* src = parts + part_index<D>(br, c);
     float M = kNegInf, L = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int s0 = 0; s0 < S; s0 += 8) {
@@ -336,7 +349,9 @@ __device__ void merge_rows(const TreeAttnArgs& a, int grp, int g, int rb, int r0
       for (int k = 0; k < 8; ++k) {
         if (s0 + k < S) {
           ml[k] = mls[(size_t)(s0 + k) * kBlockRows + br];
-          o[k] = src[(size_t)(s0 + k) * kBlockRows * C4];
+          const V4 x = src[(size_t)(s0 + k) * kBlockRows * C4];
+          o[k] = f32x4{static_cast<float>(x[0]), static_cast<float>(x[1]), static_cast<float>(x[2]),
+                       static_cast<float>(x[3])};
         }
       }
 #pragma unroll
@@ -358,24 +373,38 @@ __device__ void merge_rows(const TreeAttnArgs& a, int grp, int g, int rb, int r0
 // Cross-workgroup hand-off of one split, after its partial rows and (max,
 // sum) pairs are in the workspace (no grid barrier, no second launch). One
 // thread per workgroup:
-//  * counts in with a sequentially consistent add, which also releases the
-//    split's partials (stored through to memory, so the release is cheap);
+//  * counts in. Everything the split shares was written with device-scope
+//    stores (through L2 to memory), so waiting for those stores to complete
+//    (vmcnt 0) before a device-scope atomic publishes them; an agent-scope
+//    release fence would also write back every dirty line of this XCD's L2,
+//    which costs several microseconds and is not needed here;
 //  * waits a bounded number of polls for the other splits; the last to
-//    arrive never waits;
+//    arrive never waits. Readers then take the agent-scope acquire (cache
+//    invalidation) before loading the partials;
 //  * a split that saw everyone arrive merges its own row slice (slice j of
-//    the block belongs to split j). One that stopped waiting marks itself in
-//    the give-up mask and looks once more; the last arrival merges its own
-//    slice and every slice in that mask. Both sides use sequentially
-//    consistent operations, so at least one of them covers each slice; a
-//    slice merged twice is written twice with the same bytes;
+//    the block belongs to split j). One that stopped waiting sets its bit in
+//    the give-up mask, waits for that atomic to complete and looks once
+//    more; the last arrival completes its count-in before reading the mask
+//    and merges its own slice and every slice marked there. All these
+//    atomics are performed at one coherence point in the order each side
+//    completes them, so at least one side sees the other: every slice is
+//    merged, and a slice merged twice is written twice with the same bytes;
 //  * counts out; the last one out clears the group's words for the next call.
-template <typename T, int D, int NTH>
+template <typename T, typename PT, int D, int NTH>
 __device__ void split_handoff(const TreeAttnArgs& a, int* s_flags, int* s_mask, int grp, int g, int rb,
                               int split, int tid) {
+  // Every wave waits for its own partial stores to complete before the
+  // barrier (a workgroup barrier does not wait for global stores by itself),
+  // so the whole workgroup's partials have been performed once thread 0
+  // passes it.
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   int* gw = a.ws_cnt + (size_t)grp * 4;  // [0] arrivals, [1] departures, [2] give-up bits
   if (tid == 0) {
-    const int old = __hip_atomic_fetch_add(gw, 1, __ATOMIC_SEQ_CST, __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0);
+    const int old = __hip_atomic_fetch_add(gw, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const bool last = old == a.splits - 1;
     bool all_in = last;
     for (int it = 0; !all_in && it < a.wait_polls; ++it) {
@@ -383,11 +412,13 @@ __device__ void split_handoff(const TreeAttnArgs& a, int* s_flags, int* s_mask, 
       all_in = __hip_atomic_load(gw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.splits;
     }
     if (!all_in) {
-      __hip_atomic_fetch_or(gw + 2, 1 << split, __ATOMIC_SEQ_CST, __HIP_MEMORY_SCOPE_AGENT);
-      all_in = __hip_atomic_load(gw, __ATOMIC_SEQ_CST, __HIP_MEMORY_SCOPE_AGENT) == a.splits;
+      __hip_atomic_fetch_or(gw + 2, 1 << split, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0);  // the mark is performed before looking again
+      all_in = __hip_atomic_load(gw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.splits;
     }
     int others = 0;
-    if (last) others = __hip_atomic_load(gw + 2, __ATOMIC_SEQ_CST, __HIP_MEMORY_SCOPE_AGENT) & ~(1 << split);
+    if (last) others = __hip_atomic_load(gw + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & ~(1 << split);
     if (all_in) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // invalidates this CU's L1 too
     *s_flags = all_in ? 1 : 0;
     *s_mask = others;
@@ -397,7 +428,7 @@ __device__ void split_handoff(const TreeAttnArgs& a, int* s_flags, int* s_mask, 
     const int others = *s_mask;
     for (int j = 0; j < a.splits; ++j)
       if (j == split || ((others >> j) & 1))
-        merge_rows<T, D, NTH>(a, grp, g, rb, j * kBlockRows / a.splits, (j + 1) * kBlockRows / a.splits, tid);
+        merge_rows<T, PT, D, NTH>(a, grp, g, rb, j * kBlockRows / a.splits, (j + 1) * kBlockRows / a.splits, tid);
   }
   __syncthreads();
   if (tid == 0) {
@@ -540,7 +571,7 @@ void tree_attn_kernel(const TreeAttnArgs a) {
 
   // Publish this split's rows (reference max, sum, unnormalised output), then hand off.
   {
-    const PartialSink sink = partial_sink<D>(a, u);
+    const PartialSink sink = partial_sink<D, float>(a, u);
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -549,7 +580,7 @@ void tree_attn_kernel(const TreeAttnArgs a) {
                     f32x4{o[dt][4 * jq], o[dt][4 * jq + 1], o[dt][4 * jq + 2], o[dt][4 * jq + 3]});
     if (half == 0) put_ml(sink, rloc, m_ref, l_tot);
   }
-  split_handoff<T, D, kThreads>(a, &s_flags, &s_taken, grp, g, rb, split, tid);
+  split_handoff<T, float, D, kThreads>(a, &s_flags, &s_taken, grp, g, rb, split, tid);
 }
 
 // ============================================================================
@@ -1182,23 +1213,37 @@ void tree_attn_bf16_kernel(const TreeAttnArgs a) {
           }
       }
     } else {
-      const PartialSink sink = partial_sink<D>(a, u);
+      // Row-normalised fp16 partials: the stored values are O / g with g the
+      // row's largest |O|, in [-1, 1]; g moves into the (max, sum) pair
+      // (m + log2 g, l / g), so the merge formula is unchanged.
+      const PartialSink sink = partial_sink<D, _Float16>(a, u);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const int t = NT * rg + nt;  // 32-row tile of the block
+        float gm = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) gm = vmax(gm, __builtin_fabsf(w.o[nt][dt][j]));
+        float g_lo = gm, g_hi = gm;
+        swap32(g_lo, g_hi);  // the row's values sit in lanes l32 and l32 + 32
+        gm = vmax(g_lo, g_hi);
+        const float f = gm > 0.f ? 1.f / gm : 1.f;
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
           for (int jq = 0; jq < 4; ++jq)
-            put_partial(sink, ((t * (D / 32) + dt) * 4 + jq) * 64 + lane,
-                        f32x4{w.o[nt][dt][4 * jq], w.o[nt][dt][4 * jq + 1], w.o[nt][dt][4 * jq + 2],
-                              w.o[nt][dt][4 * jq + 3]});
-        if (half == 0) put_ml(sink, 32 * t + l32, w.m_ref[nt], l_tot[nt]);
+            put_partial_h(sink, ((t * (D / 32) + dt) * 4 + jq) * 64 + lane,
+                          f32x4{w.o[nt][dt][4 * jq], w.o[nt][dt][4 * jq + 1], w.o[nt][dt][4 * jq + 2],
+                                w.o[nt][dt][4 * jq + 3]} * f);
+        if (half == 0)
+          put_ml(sink, 32 * t + l32, gm > 0.f ? w.m_ref[nt] + __builtin_amdgcn_logf(gm) : w.m_ref[nt],
+                 l_tot[nt] * f);
       }
     }
   }
   if (a.splits == 1) return;
-  split_handoff<__bf16, D, kBfThreads<NT>>(a, &s_flags, &s_taken, grp, g, rb, split, tid);
+  split_handoff<__bf16, _Float16, D, kBfThreads<NT>>(a, &s_flags, &s_taken, grp, g, rb, split, tid);
 }
 
 }  // namespace
