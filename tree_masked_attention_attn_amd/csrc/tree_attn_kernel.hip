@@ -343,23 +343,25 @@ __device__ void merge_rows(const TreeAttnArgs& a, int grp, int g, int rb, int r0
     float M = kNegInf, L = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int s0 = 0; s0 < S; s0 += 8) {
+      // All 16 loads first, unconditionally (indices past the last split
+      // re-read split S - 1 and are ignored below): one round trip.
       float2 ml[8];
       f32x4 o[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        if (s0 + k < S) {
-          ml[k] = mls[(size_t)(s0 + k) * kBlockRows + br];
-          const V4 x = src[(size_t)(s0 + k) * kBlockRows * C4];
-          o[k] = f32x4{static_cast<float>(x[0]), static_cast<float>(x[1]), static_cast<float>(x[2]),
-                       static_cast<float>(x[3])};
-        }
+        const int sk = s0 + k < S ? s0 + k : S - 1;
+        ml[k] = mls[(size_t)sk * kBlockRows + br];
+        const V4 x = src[(size_t)sk * kBlockRows * C4];
+        o[k] = f32x4{static_cast<float>(x[0]), static_cast<float>(x[1]), static_cast<float>(x[2]),
+                     static_cast<float>(x[3])};
       }
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        if (s0 + k >= S || ml[k].x == kNegInf) continue;  // a split with no visible key adds nothing
-        const float Mn = fmaxf(M, ml[k].x);
+        // a split past the end, or one with no visible key for this row, adds nothing
+        const bool ok = s0 + k < S && ml[k].x != kNegInf;
+        const float Mn = ok ? fmaxf(M, ml[k].x) : M;
         const float sa = M == kNegInf ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
-        const float sb = __builtin_amdgcn_exp2f(ml[k].x - Mn);
+        const float sb = ok ? __builtin_amdgcn_exp2f(ml[k].x - Mn) : 0.f;
         acc = acc * sa + o[k] * sb;
         L = L * sa + ml[k].y * sb;
         M = Mn;
