@@ -11,8 +11,10 @@ sets are cycled so that the working set exceeds twice the 256 MB Infinity
 Cache (each set is one layer's K/V, as in a real step where the other layers
 have evicted it). A short device sleep is queued first so the host runs ahead
 and the kernels execute back to back. HIP events on the launch stream bracket
-the whole timed region (-> ms_per_step) and every kernel in it (-> the
-per-kernel means the roofline uses). Prints ONE JSON line.
+the timed region of K whole steps (-> ms_per_step), then K launches of each
+kernel alone (-> its mean launch duration, which the roofline uses), then the
+same launches each between their own events (-> the spread). Prints ONE JSON
+line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
 
@@ -305,65 +307,70 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    def step(i, ev=None):
+    def attn(i):
         s = sets[i % rotate]
-        if ev is not None:
-            ev[0].record(stream)
         ta.tree_attn(s["q"], s["k"], s["v"], P, parent, out=s["out"], workspace=ws)
-        if ev is not None:
-            ev[1].record(stream)
+
+    def reroot(i):
+        s = sets[i % rotate]
         ta.kv_reroot(s["k"], s["v"], P, parent, path, surv)
-        if ev is not None:
-            ev[2].record(stream)
+
+    def step(i):
+        attn(i)
+        reroot(i)
+
+    def queue_ahead(ms):
+        # a device sleep so that the host enqueues everything behind it and
+        # the kernels then execute back to back
+        torch.cuda._sleep(int(2.4e9 * ms * 1e-3))
+
+    def timed(fn, count, each=False):
+        """Run fn(0..count-1) on the stream between two HIP events; with
+        each=True also bracket every call with its own pair."""
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(count if each else 0)]
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        queue_ahead(20 * max(1, count / 200))
+        wall = time.perf_counter()
+        t0.record(stream)
+        for i in range(count):
+            if each:
+                evs[i][0].record(stream)
+            fn(i)
+            if each:
+                evs[i][1].record(stream)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall
+        return t0.elapsed_time(t1) * 1e3, [a.elapsed_time(b) * 1e3 for a, b in evs], wall
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
-    # Timed region: K steps, bracketed by synchronize on both sides.
+    # Timed region: K whole steps back to back, bracketed by synchronize on
+    # both sides and by HIP events on the launch stream.
     K = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    torch.cuda._sleep(int(2.4e9 * 0.02 * max(1, K / 200)))  # ~20 ms per 200 steps: the host runs ahead
-    t_wall = time.perf_counter()
-    t_start.record(stream)
-    for i in range(K):
-        step(i, evs[i])
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
-    attn_us = [evs[i][0].elapsed_time(evs[i][1]) * 1e3 for i in range(K)]
-    reroot_us = [evs[i][1].elapsed_time(evs[i][2]) * 1e3 for i in range(K)]
-    total_us = t_start.elapsed_time(t_end) * 1e3
+    total_us, _, t_wall = timed(step, K)
 
-    # The same tree_attn launches back to back with no events between them
-    # (cross-checks the per-launch event figure), and once with one input
-    # set (L2/MALL warm), both labelled as such.
-    def attn_only(i):
-        s = sets[i % rotate]
-        ta.tree_attn(s["q"], s["k"], s["v"], P, parent, out=s["out"], workspace=ws)
-
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda._sleep(int(2.4e9 * 0.01))
-    e0.record(stream)
-    for i in range(100):
-        attn_only(i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    b2b_us = e0.elapsed_time(e1) * 1e3 / 100
-    hot = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(50)]
-    torch.cuda._sleep(int(2.4e9 * 0.01))
-    for i in range(50):
-        step(0, hot[i])
-    torch.cuda.synchronize()
-    hot_us = statistics.median(hot[i][0].elapsed_time(hot[i][1]) * 1e3 for i in range(50))
+    # Per-kernel figures, on the same stream and inputs: K launches of one
+    # kernel back to back between two events gives its average launch
+    # duration (what the roofline uses; it agrees with a kernel trace); the
+    # same launches each between their own events give the spread (each such
+    # interval also holds the event packets' dispatch, a few microseconds).
+    attn_b2b, _, _ = timed(attn, K)
+    _, attn_us, _ = timed(attn, K, each=True)
+    _, reroot_us, _ = timed(reroot, K, each=True)
+    rr_b2b, _, _ = timed(reroot, K)
+    # One input set only (L2 / Infinity Cache warm), labelled as such.
+    _, hot, _ = timed(lambda i: attn(0), 50, each=True)
+    hot_us = statistics.median(hot)
 
     nbytes, flops, anc = tree_attn_work(cfg, parent)
     rr_bytes = reroot_bytes(cfg, src_rows, P)
-    attn_mean = statistics.fmean(attn_us)
-    rr_mean = statistics.fmean(reroot_us)
+    attn_mean = attn_b2b / K
+    rr_mean = rr_b2b / K
     hbm_gbs = nbytes / (attn_mean * 1e-6) / 1e9
     tflops = flops / (attn_mean * 1e-6) / 1e12
     traffic = load_traffic(cfg)
@@ -395,13 +402,13 @@ def main():
                    "visible_tree_pairs": anc, "accepted_path": len(path), "survivors": len(surv),
                    "rotated_sets": rotate, "splits": ta.tree_attn_num_splits(sets[0]["k"], sets[0]["v"],
                                                                               cfg["n_q_heads"], P, cfg["n_tree"])},
-        "tree_attn": {"us_mean": round(attn_mean, 2), "us_p10": round(pct(attn_us, 10), 2),
-                      "us_p50": round(pct(attn_us, 50), 2), "us_p90": round(pct(attn_us, 90), 2),
-                      "us_back_to_back": round(b2b_us, 2), "hot_cache_us_p50": round(hot_us, 2),
+        "tree_attn": {"us_mean": round(attn_mean, 2), "us_event_p10": round(pct(attn_us, 10), 2),
+                      "us_event_p50": round(pct(attn_us, 50), 2), "us_event_p90": round(pct(attn_us, 90), 2),
+                      "hot_cache_us_event_p50": round(hot_us, 2),
                       "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
                       "hbm_GBs": round(hbm_gbs, 1), "hbm_frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
                       "TFLOPs": round(tflops, 1), "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4)},
-        "kv_reroot": {"us_mean": round(rr_mean, 2), "us_p50": round(pct(reroot_us, 50), 2),
+        "kv_reroot": {"us_mean": round(rr_mean, 2), "us_event_p50": round(pct(reroot_us, 50), 2),
                       "algorithmic_bytes": rr_bytes, "GBs": round(rr_bytes / (rr_mean * 1e-6) / 1e9, 2)},
         "wall_s_timed_region": round(t_wall, 4),
         "kernel_source_sha": kernel_source_sha(),

@@ -623,34 +623,45 @@ template <int NT>
 constexpr int kBfThreads = 64 * kBfWaves<NT>;
 constexpr int kRing = 4;  // slots per ring (K and V each)
 
-// LDS layout. Rows are stored with padding rather than swizzling, so that
-// every fragment read of a wave is one base address plus compile-time
-// offsets. LDS has 64 banks of 4 bytes: 16 sixteen-byte bank groups per
+// LDS layout. LDS has 64 banks of 4 bytes: 16 sixteen-byte bank groups per
 // 256 bytes, served to 16 lanes of a ds_read_b128 or 32 lanes of a
-// ds_read_b64_tr_b16 at a time.
-//  * K (and Q) rows: stride KS = D/8 + 1 chunks. A K read has 16 lanes on 16
-//    consecutive rows at one chunk c: groups (KS r + c) mod 16 are distinct
-//    because KS is odd.
-//  * V rows: stride VS chunks, VS = 4 mod 16 (D = 128) or 12 mod 16 (D = 64).
-//    A transposed read has 32 lanes on rows r0 + e (e < 4) and chunks
-//    4t + j (j < 4): groups (VS e + j + const) mod 16 are all distinct.
+// ds_read_b64_tr_b16 at a time. K, Q and V rows are stored unpadded, with
+// their 16-byte chunks permuted by XOR within the row:
+//  * K (and Q): chunk c of row r sits at c ^ bf_ksw(r), bf_ksw(r) = r mod 16
+//    (D = 128) or (r / 2) mod 8 (D = 64). A K fragment read has 16 lanes on
+//    16 consecutive rows at one chunk: their bank groups are all distinct.
+//  * V: chunk c of row r sits at c ^ 4 bf_vsw(r), bf_vsw(r) = r mod 4
+//    (D = 128) or (r / 2) mod 2 (D = 64). A transposed read has 32 lanes on
+//    rows r0 + e (e < 4, r0 a multiple of 4) and chunks 4t + j (j < 4):
+//    their bank groups are all distinct.
+// A 64-key slot is D/8 DMA instructions of 64 lanes x 16 bytes, KOPS per
+// wave. Each instruction covers whole rows, and instruction o of a wave
+// starts o * 8 KiB after its first; both swizzles repeat within that
+// distance, so one per-lane source offset serves all of a wave's
+// instructions (the rest is a wave-uniform addition).
 template <int D>
 struct BfGeo {
   static constexpr int CPR = D / 8;                   // 16-byte chunks per row
-  static constexpr int ROWB = D * 2;                  // bytes per row in HBM
-  static constexpr int KS = CPR + 1;                  // K / Q row stride in LDS, chunks
-  static constexpr int VS = D == 128 ? 20 : 12;       // V row stride in LDS, chunks
-  static constexpr int KSLOT = 64 * KS * 16;          // one 64-key K stage
-  static constexpr int VSLOT = 64 * VS * 16;          // one 64-key V stage
-  // A slot of row stride S is filled by S 64-lane DMA instructions.
-  static constexpr int VRING = kRing * KSLOT;         // the V ring follows the K ring
-  static constexpr int QSTAGE0 = 3 * KSLOT;           // Q rows 0-63 wait in K slot 3,
-  static constexpr int QSTAGE1 = VRING + 3 * VSLOT;   // rows 64-127 in V slot 3 (K layout)
-  static constexpr int ANC = kRing * (KSLOT + VSLOT); // ancestor table (64 x u64) + DMA spill
-  static constexpr int LDS = ANC + 1024;
-  static_assert(kBlockRows == 128 && VS >= CPR && VS % 16 == (D == 128 ? 4 : 12), "layout");
+  static constexpr int ROWB = D * 2;                  // bytes per row, in HBM and in LDS
+  static constexpr int SLOT = 64 * ROWB;              // one 64-key K or V stage
+  static constexpr int KOPS = CPR / 8;                // DMA instructions per wave per slot
+  static constexpr int VRING = kRing * SLOT;          // the V ring follows the K ring
+  static constexpr int QSTAGE0 = 3 * SLOT;            // Q rows 0-63 wait in K slot 3
+  static constexpr int ANC = 2 * kRing * SLOT;        // ancestor table (64 x u64) + DMA spill
+  static constexpr int QSTAGE1 = ANC + 1024;          // Q rows 64-127
+  static constexpr int LDS = QSTAGE1 + SLOT;
+  static_assert(kBlockRows == 128 && CPR % 8 == 0, "layout");
   static_assert(LDS <= 160 * 1024, "LDS");
 };
+
+template <int D>
+__device__ __forceinline__ int bf_ksw(int r) {
+  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int bf_vsw(int r) {
+  return D == 128 ? (r & 3) : ((r >> 1) & 1);
+}
 
 // vmcnt(n) with every other counter left alone (gfx9 encoding).
 #define TA_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(0x0F70 | ((n) & 15) | (((n) >> 4) << 14))
@@ -694,48 +705,50 @@ __device__ __forceinline__ i32x4 bf_rsrc(const void* base, int bytes) {
 // compiler neither sees an LDS write nor inserts waits for it; every wait on
 // these loads is explicit (TA_WAIT_VM), and the barriers order them against
 // the LDS reads.
-__device__ __forceinline__ void bf_dma16(i32x4 rsrc, const char* lds, int voff) {
-  const unsigned addr = static_cast<unsigned>(
-      reinterpret_cast<unsigned long>((__attribute__((address_space(3))) const char*)lds));
+__device__ __forceinline__ void bf_dma16(i32x4 rsrc, unsigned lds, int voff) {
   asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
                :
-               : "v"(voff), "s"(__builtin_amdgcn_readfirstlane(addr)), "s"(rsrc)
+               : "v"(voff), "s"(__builtin_amdgcn_readfirstlane(lds)), "s"(rsrc)
                : "memory", "m0");
 }
 
-// Per-lane source offsets of the DMA instructions that fill one slot of row
-// stride S chunks: instruction op (op = 4 o + wave) covers LDS positions
-// [64 op, 64 op + 64) of the slot, position p = row * S + chunk; padding
-// chunks read out of range (zeros). The same for every stage.
-template <int D, int S, int W, int NW>
-__device__ __forceinline__ void bf_dma_offsets(int (&off)[W], int wave, int lane) {
-  using G = BfGeo<D>;
-#pragma unroll
-  for (int o = 0; o < W; ++o) {
-    const int p = (o * NW + wave) * 64 + lane;
-    const int row = p / S, ch = p % S;
-    off[o] = ch < G::CPR ? row * G::ROWB + ch * 16 : (1 << 30);
-  }
+// ... with a wave-uniform byte offset `add` on every lane's source. It goes
+// into the per-lane offset, not the scalar one, so that the raw-buffer range
+// check (which covers only the per-lane and instruction offsets) sees it.
+__device__ __forceinline__ void bf_dma16(i32x4 rsrc, unsigned lds, int voff, int add) {
+  bf_dma16(rsrc, lds, voff + add);
 }
 
-// DMA keys [k0, k0 + 64) of one head's K (or V) into a slot of row stride S.
-template <int D, int S, int W, int NW>
-__device__ __forceinline__ void bf_dma_slot(char* slot, const __bf16* head, int k0, int total_keys,
-                                            const int (&off)[W], int wave) {
+// Per-lane source offset (within a 64-key stage) of a wave's first DMA
+// instruction into a K slot (KEY) or a V slot: LDS position
+// p = 64 wave + lane = row * D/8 + physical chunk holds chunk
+// (physical chunk) ^ swizzle(row) of the row. The wave's instruction o reads
+// o * 8 KiB further on (the swizzles of row and row + 32 o agree).
+template <int D, bool KEY>
+__device__ __forceinline__ int bf_dma_offset(int wave, int lane) {
   using G = BfGeo<D>;
-  const i32x4 r = bf_rsrc(head + (size_t)k0 * D, (total_keys - k0) * G::ROWB);
+  const int p = wave * 64 + lane;
+  const int row = p / G::CPR, pc = p % G::CPR;
+  const int ch = KEY ? pc ^ bf_ksw<D>(row) : pc ^ (4 * bf_vsw<D>(row));
+  return row * G::ROWB + ch * 16;
+}
+
+// DMA keys [k0, k0 + 64) of one head's K (or V) into a slot; `off` from
+// bf_dma_offset.
+template <int D, int NW>
+__device__ __forceinline__ void bf_dma_slot(unsigned slot, const __bf16* head, int k0, int total_keys, int off,
+                                            int wave) {
+  using G = BfGeo<D>;
+  const i32x4 r = bf_rsrc(head + (size_t)k0 * D, max(total_keys - k0, 0) * G::ROWB);
 #pragma unroll
-  for (int o = 0; o < W; ++o) {
-    const int op = o * NW + wave;
-    if (op < S) bf_dma16(r, slot + op * 1024, off[o]);
-  }
+  for (int o = 0; o < G::KOPS; ++o) bf_dma16(r, slot + (o * NW + wave) * 1024, off, o * NW * 1024);
 }
 
 // DMA the block's 128 query rows (K layout; rows 0-63 into K slot 3, rows
-// 64-127 into V slot 3; rows past the head's rows and padding read as zeros)
-// and, from the kernel arguments, the ancestor table.
+// 64-127 into their own area; rows past the head's rows read as zeros) and,
+// from the kernel arguments, the ancestor table.
 template <int D, int NW>
-__device__ __forceinline__ void bf_dma_q_anc(char* lds, const TreeAttnArgs& a, int g, int rb, int wave,
+__device__ __forceinline__ void bf_dma_q_anc(unsigned lds, const TreeAttnArgs& a, int g, int rb, int wave,
                                              int lane) {
   using G = BfGeo<D>;
   const int qbytes = a.n_tree * a.n_q_heads * G::ROWB;
@@ -743,15 +756,13 @@ __device__ __forceinline__ void bf_dma_q_anc(char* lds, const TreeAttnArgs& a, i
 #pragma unroll
   for (int h = 0; h < 2; ++h)
 #pragma unroll
-    for (int o = 0; o < (G::KS + NW - 1) / NW; ++o) {
+    for (int o = 0; o < G::KOPS; ++o) {
       const int op = o * NW + wave;
-      if (op >= G::KS) continue;
       const int p = op * 64 + lane;
-      const int row = 64 * h + p / G::KS, ch = p % G::KS;
-      const int hr = rb * kBlockRows + row;
+      const int row = p / G::CPR, ch = (p % G::CPR) ^ bf_ksw<D>(row);
+      const int hr = rb * kBlockRows + 64 * h + row;
       int off = qbytes;  // out of range: zeros
-      if (ch < G::CPR && hr < a.rows_per_head)
-        off = ((hr / a.group) * a.n_q_heads + g * a.group + hr % a.group) * G::ROWB + ch * 16;
+      if (hr < a.rows_per_head) off = ((hr / a.group) * a.n_q_heads + g * a.group + hr % a.group) * G::ROWB + ch * 16;
       bf_dma16(r, lds + (h ? G::QSTAGE1 : G::QSTAGE0) + op * 1024, off);
     }
   if (wave == 0) {
@@ -817,36 +828,47 @@ __device__ __forceinline__ void bf_rescale(BfWave<D, NT>& w) {
   }
 }
 
-// K fragments of the wave's 32-key half: K rows 32 kh + l32, chunk 2 cc + half.
+// K fragments of the wave's 32-key half: K rows 32 kh + l32, chunk 2 cc + half
+// (also the Q fragments, from a Q staging area). Under the swizzle the
+// chunk sits at 2 (cc ^ s1) + (half ^ s0), s = bf_ksw(row): fragment cc of
+// every lane is at (its fragment-0 address) ^ 32 cc.
 template <int D>
-__device__ __forceinline__ void bf_read_k(bf16x8 (&kf)[D / 16], const char* slot, int kh, int lane) {
+__device__ __forceinline__ void bf_read_k(bf16x8 (&kf)[D / 16], unsigned slot, int kh, int lane) {
   using G = BfGeo<D>;
-  const char* base = slot + (32 * kh + (lane & 31)) * (G::KS * 16) + (lane >> 5) * 16;
+  const int row = 32 * kh + (lane & 31), sw = bf_ksw<D>(row);
+  const unsigned base = slot + row * G::ROWB + 32 * (sw >> 1) + 16 * ((lane >> 5) ^ (sw & 1));
 #pragma unroll
-  for (int cc = 0; cc < D / 16; ++cc) kf[cc] = *reinterpret_cast<const bf16x8*>(base + 32 * cc);
+  for (int cc = 0; cc < D / 16; ++cc)
+    kf[cc] = *(__attribute__((address_space(3))) const bf16x8*)(unsigned long)(base ^ (32u * cc));
 }
 
 // V^T fragments (A operand of O^T += V^T P^T, 32 head_dim rows x 16 keys) of
 // the wave's half, from two transposed reads each: lane (g = lane/16,
 // j = lane%16) of a 16-lane group points at V[key e = j/4][head_dim
 // 16 (g%2) + 4 (j%4) ..] and receives, for head_dim 16 (g%2) + j, the 4 keys
-// the group pointed at.
+// the group pointed at. The rows a read touches share bf_vsw, and the
+// swizzle only moves 64-byte column blocks, so head_dim block dt of every
+// lane is at (its block-0 address) ^ 64 dt; rows further down are
+// compile-time offsets.
 template <int D>
-__device__ __forceinline__ void bf_read_v(bf16x8 (&vf)[2][D / 32], const char* slot, int kh, int lane) {
+__device__ __forceinline__ void bf_read_v(bf16x8 (&vf)[2][D / 32], unsigned slot, int kh, int lane) {
   using G = BfGeo<D>;
-  constexpr int RS = G::VS * 16;  // row stride, bytes
+  constexpr int RS = G::ROWB;  // row stride, bytes
   const int half = lane >> 5, e = (lane & 15) >> 2, q = lane & 3, g1 = (lane >> 4) & 1;
-  const char* base = slot + (32 * kh + 4 * half + e) * RS + (2 * g1 + (q >> 1)) * 16 + (q & 1) * 8;
+  const int row = 32 * kh + 4 * half + e;
+  const unsigned base = slot + row * RS + 64 * bf_vsw<D>(row) + (2 * g1 + (q >> 1)) * 16 + (q & 1) * 8;
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
+  for (int dt = 0; dt < D / 32; ++dt) {
+    const unsigned at = base ^ (64u * dt);
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) {
+    for (int ks = 0; ks < 2; ++ks) {
       const bf16x4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-          (__attribute__((address_space(3))) bf16x4v*)(base + 16 * ks * RS + 64 * dt));
+          (__attribute__((address_space(3))) bf16x4v*)(unsigned long)(at + 16 * ks * RS));
       const bf16x4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-          (__attribute__((address_space(3))) bf16x4v*)(base + (16 * ks + 8) * RS + 64 * dt));
+          (__attribute__((address_space(3))) bf16x4v*)(unsigned long)(at + (16 * ks + 8) * RS));
       vf[ks][dt] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     }
+  }
 }
 
 // S^T = K Q^T for the wave's row tiles (keys = M, rows = N, head_dim = K): after
@@ -891,86 +913,39 @@ __device__ __forceinline__ uint32_t visible32(uint64_t anc, int kb, int prefix_l
 // end) set to -inf. The mask is a uniform branch taken only by stages that
 // reach the tree.
 template <int D, int NT>
+__device__ __forceinline__ void bf_mask(const BfWave<D, NT>& w, float (&x)[NT][16], int kb, int half,
+                                        const TreeAttnArgs& a) {
+  if (kb + 32 > a.prefix_len) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const uint32_t vis = visible32(w.anc[nt], kb, a.prefix_len) >> (4 * half);  // then constant bit tests
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (!((vis >> (8 * (j >> 2) + (j & 3))) & 1u)) x[nt][j] = kNegInf;
+    }
+  }
+}
+
+template <int D, int NT>
 __device__ __forceinline__ void bf_scores(const BfWave<D, NT>& w, const f32x16 (&sc)[NT], float (&x)[NT][16],
                                           int kb, int half, const TreeAttnArgs& a) {
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
     for (int j = 0; j < 16; ++j) x[nt][j] = sc[nt][j];
-  if (kb + 32 > a.prefix_len) {
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const uint32_t vis = visible32(w.anc[nt], kb, a.prefix_len);
-#pragma unroll
-      for (int j = 0; j < 16; ++j)
-        if (!((vis >> (8 * (j >> 2) + 4 * half + (j & 3))) & 1u)) x[nt][j] = kNegInf;
-    }
-  }
+  bf_mask<D, NT>(w, x, kb, half, a);
 }
 
-// One pipeline iteration on stage j (QK, PV, VN select the parts that exist):
-//  * settle the rescale softmax(j - 1) owes O, then PV(j - 1) from the V
-//    fragments `vf` (read from LDS at the end of the previous iteration) and
-//    the weights `pp`;
-//  * softmax(j) of the scores `sc` -> weights, left in `pp`: the reference
-//    max is raised lazily (only when a score exceeds it by more than
-//    2^kSlack), and the factors alpha that rescale O wait in the wave state;
-//  * QK(j + 1) from the K slot `knext` -> `sc`;
-//  * read V(j) from `vcur` into `vf` for the next iteration's PV, so that the
-//    PV MFMAs never wait for LDS.
-// A wave issues in order, so MFMA and VALU work overlap only where they
-// alternate in the instruction stream: the softmax is cut into steps, and
-// after each step the next MFMAs of the iteration are issued (PV first, its
-// operands are already in registers; then QK, whose K fragments have been in
-// flight since the top). sched_barrier keeps the compiler from regrouping.
-template <int D, int NT, bool QK, bool PV, bool VN>
-__device__ __forceinline__ void bf_iter(BfWave<D, NT>& w, f32x16 (&sc)[NT], bf16x8 (&pp)[NT][2],
-                                        bf16x8 (&vf)[2][D / 32], const char* knext, const char* vcur, int kb,
-                                        int kh, int lane, const TreeAttnArgs& a) {
-  constexpr int NPV = PV ? 2 * (D / 32) * NT : 0;  // k-steps x head_dim tiles x row tiles
-  constexpr int NQK = QK ? (D / 16) * NT : 0;      // k-steps x row tiles
-  constexpr int NM = NPV + NQK;
-  constexpr int NSTEP = 7 * NT + 2;
-  bf16x8 kf[D / 16];
-  float x[NT][16];
-  // The two branches (rare rescale, tree mask) come first.
-  if constexpr (PV) bf_rescale<D, NT>(w);
-  bf_scores<D, NT>(w, sc, x, kb, lane >> 5, a);
-  if constexpr (QK) bf_read_k<D>(kf, knext, kh, lane);
-
-  f32x16 sn[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) sn[nt] = f32x16{};
-  int issued = 0;
-  auto mfma_upto = [&](int target) {
-#pragma unroll
-    for (int i = 0; i < NM; ++i) {
-      if (i < issued || i >= target) continue;
-      if (i < NPV) {
-        const int ks = i / ((D / 32) * NT), dt = (i / NT) % (D / 32), nt = i % NT;
-        w.o[nt][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ks][dt], pp[nt][ks], w.o[nt][dt], 0, 0, 0);
-      } else {
-        const int k = i - NPV, cc = k / NT, nt = k % NT;
-        sn[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[cc], w.qf[nt][cc], sn[nt], 0, 0, 0);
-      }
-    }
-    issued = target > issued ? target : issued;
-  };
-  int step = 0;
-  auto step_done = [&]() {  // after each softmax step: the MFMAs up to its share
-    ++step;
-    mfma_upto((NM * step) / NSTEP);
-    __builtin_amdgcn_sched_barrier(0);
-  };
-
-  const float c = a.scale_log2;
+// Online softmax of one stage: scores x (masked) -> bf16 weights pn. The
+// reference max is raised lazily (only when a score exceeds it by more than
+// 2^kSlack); the factors alpha that rescale O then wait in the wave state
+// until the next PV.
+template <int D, int NT>
+__device__ __forceinline__ void bf_softmax(BfWave<D, NT>& w, float (&x)[NT][16], bf16x8 (&pn)[NT][2], float c) {
   float mx[NT], nm[NT];
   // Row maxima over this lane's 16 keys, then over both lane halves.
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    mx[nt] = max16(x[nt]);
-    step_done();
-  }
+  for (int nt = 0; nt < NT; ++nt) mx[nt] = max16(x[nt]);
   if constexpr (NT == 2) {
     swap32(mx[0], mx[1]);
     float mt = vmax(mx[0], mx[1]), mt2 = mt;  // lanes 0-31: tile 0's max; 32-63: tile 1's
@@ -993,40 +968,138 @@ __device__ __forceinline__ void bf_iter(BfWave<D, NT>& w, f32x16 (&sc)[NT], bf16
     bump_any |= bump;
     nm[nt] = w.m_ref[nt] == kNegInf ? 0.f : -w.m_ref[nt];
   }
-  step_done();
-  // The weights, 4 per step.
-#pragma unroll
-  for (int e = 0; e < 4 * NT; ++e) {
-    const int nt = e / 4, j0 = 4 * (e % 4);
-#pragma unroll
-    for (int j = j0; j < j0 + 4; ++j) x[nt][j] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[nt][j], c, nm[nt]));
-    step_done();
-  }
-  // Row sums, bf16 weights, the rescale flag.
-  bf16x8 pn[NT][2];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) x[nt][j] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[nt][j], c, nm[nt]));
     w.l_run[nt] = w.l_run[nt] * w.alpha[nt] + sum16(x[nt]);
-    step_done();
-  }
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int q = 0; q < 8; ++q) pn[nt][ks][q] = static_cast<__bf16>(x[nt][8 * ks + q]);
-    step_done();
   }
   w.pend = __ballot(bump_any) != 0;
-  step_done();
-  mfma_upto(NM);
+}
+
+// The MFMAs of one iteration, PV first (its operands are in registers since
+// the previous iteration), then QK into sn, with the wave's NOPS DMA
+// instructions spread evenly between them: a stall on a busy load path then
+// costs nothing while the MFMA pipe is full.
+template <int D, int NT, bool QK, bool PV, int NOPS, typename Dma>
+__device__ __forceinline__ void bf_mfma_block(BfWave<D, NT>& w, f32x16 (&sn)[NT], const bf16x8 (&kf)[D / 16],
+                                              const bf16x8 (&vf)[2][D / 32], const bf16x8 (&pp)[NT][2], Dma&& dma) {
+  constexpr int NPV = PV ? 2 * (D / 32) * NT : 0;  // k-steps x head_dim tiles x row tiles
+  constexpr int NQK = QK ? (D / 16) * NT : 0;      // k-steps x row tiles
+  constexpr int NM = NPV + NQK;
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    pp[nt][0] = pn[nt][0];
-    pp[nt][1] = pn[nt][1];
-    if constexpr (QK) sc[nt] = sn[nt];
+  for (int nt = 0; nt < NT; ++nt) sn[nt] = f32x16{};
+  static_assert(NOPS <= NM, "one DMA instruction per MFMA at most");
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    if (i < NPV) {
+      const int ks = i / ((D / 32) * NT), dt = (i / NT) % (D / 32), nt = i % NT;
+      w.o[nt][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ks][dt], pp[nt][ks], w.o[nt][dt], 0, 0, 0);
+    } else {
+      const int k = i - NPV, cc = k / NT, nt = k % NT;
+      sn[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[cc], w.qf[nt][cc], sn[nt], 0, 0, 0);
+    }
+    if ((i * NOPS) % NM == 0 && i * NOPS / NM < NOPS) {  // spread evenly, kept in place
+      __builtin_amdgcn_sched_barrier(0);
+      dma(i * NOPS / NM);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
-  if constexpr (VN) bf_read_v<D>(vf, vcur, kh, lane);
+}
+
+// A uniform true that the compiler cannot see through. Code under it keeps
+// a basic block of its own, so instruction selection cannot interleave it
+// with the code around it.
+__device__ __forceinline__ bool bf_opaque_true() {
+  int one;
+  asm volatile("s_mov_b32 %0, 1" : "=s"(one));
+  return one != 0;
+}
+
+// Values pinned here are final at this point of the instruction stream (the
+// compiler can neither sink their computation below nor hoist later uses
+// above). Empty asm; the operands only carry the dependence.
+template <typename T>
+__device__ __forceinline__ void bf_pin(T& x) {
+  static_assert(sizeof(T) == 4, "one register");
+  asm volatile("" : "+v"(x));
+}
+template <int NT>
+__device__ __forceinline__ void bf_pin_scores(float (&x)[NT][16]) {
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) bf_pin(x[nt][j]);
+}
+template <int NT>
+__device__ __forceinline__ void bf_pin_weights(bf16x8 (&p)[NT][2]) {
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      u32x4 u = __builtin_bit_cast(u32x4, p[nt][ks]);
+      asm volatile("" : "+v"(u));
+      p[nt][ks] = __builtin_bit_cast(bf16x8, u);
+    }
+}
+
+// One pipeline iteration on stage j (QK, PV, VN select the parts that exist):
+//  * settle the rescale softmax(j - 1) owes O;
+//  * PV(j - 1) from the V fragments `vf` and the weights `pp`, and QK(j + 1)
+//    from the K slot `knext` (its fragments are read first) -> new scores;
+//  * softmax(j) of the scores `sc` -> the weights for PV(j);
+//  * read V(j) from `vcur` into `vf` for the next iteration's PV.
+// The two waves that share a SIMD run these in opposite orders: one issues
+// its MFMAs first and then the softmax, the other the softmax first. Between
+// the workgroup barriers that start each iteration, the matrix core then
+// works for one wave while the vector ALU works for the other, instead of
+// both waves contending for the same unit at the same time.
+template <bool MFMA_FIRST, int D, int NT, bool QK, bool PV, bool VN, int NOPS, typename Dma>
+__device__ __forceinline__ void bf_iter(BfWave<D, NT>& w, f32x16 (&sc)[NT], bf16x8 (&pp)[NT][2],
+                                        bf16x8 (&vf)[2][D / 32], unsigned knext, unsigned vcur, int kb,
+                                        int kh, int lane, const TreeAttnArgs& a, Dma&& dma) {
+  bf16x8 kf[D / 16];
+  float x[NT][16];
+  if constexpr (PV) bf_rescale<D, NT>(w);
+  if constexpr (MFMA_FIRST) {
+    // K fragments first: the PV MFMAs cover their latency
+    if constexpr (QK) bf_read_k<D>(kf, knext, kh, lane);
+    f32x16 sn[NT];
+    if (bf_opaque_true()) bf_mfma_block<D, NT, QK, PV, NOPS>(w, sn, kf, vf, pp, dma);
+    if constexpr (VN) bf_read_v<D>(vf, vcur, kh, lane);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) x[nt][j] = sc[nt][j];
+    bf_pin_scores<NT>(x);  // the softmax starts only here
+    bf_mask<D, NT>(w, x, kb, lane >> 5, a);
+    bf_softmax<D, NT>(w, x, pp, a.scale_log2);
+    if constexpr (QK) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) sc[nt] = sn[nt];
+    }
+  } else {
+    bf16x8 pn[NT][2];
+    bf_scores<D, NT>(w, sc, x, kb, lane >> 5, a);
+    bf_softmax<D, NT>(w, x, pn, a.scale_log2);
+    bf_pin_weights<NT>(pn);  // the softmax is done before the MFMAs
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) bf_pin(w.l_run[nt]);
+    // K fragments only now (not live through the softmax); the PV MFMAs
+    // cover their latency
+    if constexpr (QK) bf_read_k<D>(kf, knext, kh, lane);
+    if (bf_opaque_true()) bf_mfma_block<D, NT, QK, PV, NOPS>(w, sc, kf, vf, pp, dma);
+    if constexpr (VN) bf_read_v<D>(vf, vcur, kh, lane);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      pp[nt][0] = pn[nt][0];
+      pp[nt][1] = pn[nt][1];
+    }
+  }
 }
 
 template <int D, int NT>
@@ -1036,6 +1109,7 @@ void tree_attn_bf16_kernel(const TreeAttnArgs a) {
   using G = BfGeo<D>;
   __shared__ __attribute__((aligned(1024))) char lds[G::LDS];
   __shared__ int s_flags, s_taken;
+  __shared__ int s_pair[4];  // waves seen per SIMD
 
   const int b = blockIdx.x;
   const int u = (a.n_units % 8 == 0) ? (b % 8) * (a.n_units / 8) + b / 8 : b;
@@ -1047,45 +1121,48 @@ void tree_attn_bf16_kernel(const TreeAttnArgs a) {
   const int t1 = (int)((long long)(split + 1) * a.n_tiles / a.splits);
   const int n = t1 - t0;  // >= 1
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // wave is uniform: readfirstlane lets the compiler keep it (and all that
+  // derives from it) in scalar registers, with scalar branches
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31;
   constexpr int NW = kBfWaves<NT>, RW = NW / 2;  // waves, row groups
   const int rg = wave % RW, kh = wave / RW;      // row group, key half
   const __bf16* kh_ptr = static_cast<const __bf16*>(a.k) + (size_t)g * a.kv_head_stride;
   const __bf16* vh_ptr = static_cast<const __bf16*>(a.v) + (size_t)g * a.kv_head_stride;
-  char* const kring = lds;
-  char* const vring = lds + G::VRING;
-  auto kslot = [&](int j) { return kring + (j & (kRing - 1)) * G::KSLOT; };
-  auto vslot = [&](int j) { return vring + (j & (kRing - 1)) * G::VSLOT; };
-  constexpr int KW = (G::KS + NW - 1) / NW, VW = (G::VS + NW - 1) / NW;  // DMA ops per wave (at most)
-  int koff[KW], voff[VW];
-  bf_dma_offsets<D, G::KS, KW, NW>(koff, wave, lane);
-  bf_dma_offsets<D, G::VS, VW, NW>(voff, wave, lane);
+  // LDS byte addresses (the space the DMA and the fragment reads take)
+  const unsigned lds0 = static_cast<unsigned>(
+      reinterpret_cast<unsigned long>((__attribute__((address_space(3))) char*)lds));
+  auto kslot = [&](int j) { return lds0 + (j & (kRing - 1)) * G::SLOT; };
+  auto vslot = [&](int j) { return lds0 + G::VRING + (j & (kRing - 1)) * G::SLOT; };
+  static_assert(NW == 8, "a slot is D/8 instructions, D/64 per wave");
+  const int koff = bf_dma_offset<D, true>(wave, lane);
+  const int voff = bf_dma_offset<D, false>(wave, lane);
   auto dma_k = [&](int j) {
-    bf_dma_slot<D, G::KS, KW, NW>(kslot(j), kh_ptr, (t0 + j) * 64, a.total_keys, koff, wave);
+    bf_dma_slot<D, NW>(kslot(j), kh_ptr, (t0 + j) * 64, a.total_keys, koff, wave);
   };
   auto dma_v = [&](int j) {
-    bf_dma_slot<D, G::VS, VW, NW>(vslot(j), vh_ptr, (t0 + j) * 64, a.total_keys, voff, wave);
+    bf_dma_slot<D, NW>(vslot(j), vh_ptr, (t0 + j) * 64, a.total_keys, voff, wave);
   };
+
+  if (tid < 4) s_pair[tid] = 0;
 
   // DMA issue order (j = stage index within the split): Q and ancestors, K0,
   // K1, K2, V0, V1, V2; iteration 0 issues K3, K4, V3 (over the Q staging
   // areas, after Q has been read); iteration j >= 1 issues K(j+4), V(j+3).
   // Iteration j needs K(j+1) and V(j); each wait counts the DMA instructions
   // issued after the newest of those, which may stay in flight.
-  bf_dma_q_anc<D, NW>(lds, a, g, rb, wave, lane);
+  bf_dma_q_anc<D, NW>(lds0, a, g, rb, wave, lane);
 #pragma unroll
   for (int j = 0; j < 3; ++j)
     if (j < n) dma_k(j);
 #pragma unroll
   for (int j = 0; j < 3; ++j)
     if (j < n) dma_v(j);
-  // DMA instructions this wave issues per K (V) stage: ops NW o + wave < KS (VS).
-  const int KO = (G::KS - wave + NW - 1) / NW;
-  const int VO = (G::VS - wave + NW - 1) / NW;
-  auto iter_ops = [&](int j) {  // DMA instructions iteration j issues
+  // DMA instructions each wave issues per K (V) stage.
+  constexpr int KO = G::KOPS, VO = G::KOPS;
+  auto iter_ops = [&](int j) {  // DMA instructions iteration j < n - 1 issues
     if (j == 0) return KO * ((3 < n) + (4 < n)) + VO * (3 < n);
-    return KO * (j + 4 < n) + VO * (j + 3 < n);
+    return KO + VO;
   };
 
   BfWave<D, NT> w;
@@ -1108,12 +1185,15 @@ void tree_attn_bf16_kernel(const TreeAttnArgs a) {
   // Q, the ancestors and K0 have landed: read Q and the ancestor bits, QK(0).
   wait_vm_atmost(KO * ((n > 1) + (n > 2)) + VO * (1 + (n > 1) + (n > 2)));
   bf_barrier();
+  // The first wave to get here on each SIMD issues its MFMAs before its
+  // softmax in every iteration, the second one after (SIMD_ID: HW_ID bits 5:4).
+  int seen = 0;
+  if (lane == 0) seen = atomicAdd(&s_pair[(__builtin_amdgcn_s_getreg(4 | (4 << 6) | (1 << 11))) & 3], 1);
+  const bool mfma_first = (__builtin_amdgcn_readfirstlane(seen) & 1) == 0;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int row = 32 * (NT * rg + nt) + l32;
-    const char* qr = lds + (row < 64 ? G::QSTAGE0 : G::QSTAGE1) + (row & 63) * (G::KS * 16) + half * 16;
-#pragma unroll
-    for (int cc = 0; cc < D / 16; ++cc) w.qf[nt][cc] = *reinterpret_cast<const bf16x8*>(qr + 32 * cc);
+    bf_read_k<D>(w.qf[nt], lds0 + (row < 64 ? G::QSTAGE0 : G::QSTAGE1), (row >> 5) & 1, lane);
     w.anc[nt] = row_ok[nt] ? reinterpret_cast<const uint64_t*>(lds + G::ANC)[node[nt]] : 0;
   }
   f32x16 sc[NT];
@@ -1126,36 +1206,64 @@ void tree_attn_bf16_kernel(const TreeAttnArgs a) {
   }
   auto kb_of = [&](int j) { return (t0 + j) * 64 + 32 * kh; };
 
-  // Iteration 0: softmax(0), QK(1), read V(0); no PV yet. Needs K1 and V0.
-  wait_vm_atmost(VO * ((n > 1) + (n > 2)));
-  bf_barrier();  // Q has been read by every wave: its staging slots are free
-  if (3 < n) dma_k(3);
-  if (4 < n) dma_k(4);
-  if (3 < n) dma_v(3);
-  if (n > 1)
-    bf_iter<D, NT, true, false, true>(w, sc, pp, vf, kslot(1), vslot(0), kb_of(0), kh, lane, a);
-  else
-    bf_iter<D, NT, false, false, true>(w, sc, pp, vf, nullptr, vslot(0), kb_of(0), kh, lane, a);
-  // Steady state: iteration j needs K(j+1) and V(j).
-  for (int j = 1; j < n - 1; ++j) {
-    int after;  // DMA instructions issued after the newest one needed
-    if (j == 1) after = VO * (n > 2) + iter_ops(0);
-    else if (j == 2) after = (n > 3 ? KO * (n > 4) + VO : 0) + iter_ops(1);
-    else after = iter_ops(j - 2) + iter_ops(j - 1);
-    wait_vm_atmost(after);
-    bf_barrier();
-    if (j + 4 < n) dma_k(j + 4);
-    if (j + 3 < n) dma_v(j + 3);
-    bf_iter<D, NT, true, true, true>(w, sc, pp, vf, kslot(j + 1), vslot(j), kb_of(j), kh, lane, a);
-  }
-  // Last iteration (j = n - 1): PV(n-2), softmax(n-1), read V(n-1); no DMA left.
-  if (n > 1) {
-    TA_WAIT_VM(0);
-    bf_barrier();
-    bf_iter<D, NT, false, true, true>(w, sc, pp, vf, nullptr, vslot(n - 1), kb_of(n - 1), kh, lane, a);
-  }
-  bf_rescale<D, NT>(w);
-  bf_pv<D, NT>(w, vf, pp);
+  // The pipeline, compiled once per order (each copy keeps its own registers).
+  auto pipeline = [&](auto order) {
+    constexpr bool MF = decltype(order)::value;
+    // Iteration 0: softmax(0), QK(1), read V(0); no PV yet. Needs K1 and V0.
+    wait_vm_atmost(VO * ((n > 1) + (n > 2)));
+    bf_barrier();  // Q has been read by every wave: its staging slots are free
+    if (3 < n) dma_k(3);
+    if (4 < n) dma_k(4);
+    if (3 < n) dma_v(3);
+    auto no_dma = [](int) {};
+    if (n > 1)
+      bf_iter<MF, D, NT, true, false, true, 0>(w, sc, pp, vf, kslot(1), vslot(0), kb_of(0), kh, lane, a, no_dma);
+    else
+      bf_iter<MF, D, NT, false, false, true, 0>(w, sc, pp, vf, 0u, vslot(0), kb_of(0), kh, lane, a, no_dma);
+    // Steady iteration j: needs K(j+1) and V(j), loads K(j+4) and V(j+3), one
+    // DMA instruction after every few MFMAs. Past the split's last stage the
+    // loads still run, with an empty range (zeros, no memory traffic), into
+    // slots that nothing reads any more (K(j) and V(j-1) are consumed): every
+    // steady iteration issues the same instructions, and no branch splits the
+    // MFMAs.
+    const int end_keys = min(a.total_keys, t1 * 64);  // loads never reach the next split
+    auto steady = [&](int j) {
+      const int k4 = (t0 + j + 4) * 64, v3 = (t0 + j + 3) * 64;
+      const i32x4 rk = bf_rsrc(kh_ptr + (size_t)k4 * D, max(end_keys - k4, 0) * G::ROWB);
+      const i32x4 rv = bf_rsrc(vh_ptr + (size_t)v3 * D, max(end_keys - v3, 0) * G::ROWB);
+      const unsigned ks4 = kslot(j + 4);
+      const unsigned vs3 = vslot(j + 3);
+      auto dma = [&](int i) {
+        if (i < G::KOPS) bf_dma16(rk, ks4 + (i * NW + wave) * 1024, koff, i * NW * 1024);
+        else bf_dma16(rv, vs3 + ((i - G::KOPS) * NW + wave) * 1024, voff, (i - G::KOPS) * NW * 1024);
+      };
+      bf_iter<MF, D, NT, true, true, true, 2 * G::KOPS>(w, sc, pp, vf, kslot(j + 1), vslot(j), kb_of(j), kh, lane,
+                                                        a, dma);
+    };
+    for (int j = 1; j < n - 1; ++j) {
+      // DMA instructions issued after the newest one needed: from j = 3 on,
+      // the two previous iterations' (a constant)
+      if (j >= 3) {
+        static_assert(2 * (KO + VO) <= 15, "vmcnt");
+        TA_WAIT_VM(2 * (KO + VO));
+      } else {
+        wait_vm_atmost(j == 1 ? VO * (n > 2) + iter_ops(0) : (n > 3 ? KO * (n > 4) + VO : 0) + iter_ops(1));
+      }
+      bf_barrier();
+      steady(j);
+    }
+    // Last iteration (j = n - 1): PV(n-2), softmax(n-1), read V(n-1); no DMA left.
+    if (n > 1) {
+      TA_WAIT_VM(0);
+      bf_barrier();
+      bf_iter<MF, D, NT, false, true, true, 0>(w, sc, pp, vf, 0u, vslot(n - 1), kb_of(n - 1), kh, lane, a,
+                                               no_dma);
+    }
+    bf_rescale<D, NT>(w);
+    bf_pv<D, NT>(w, vf, pp);
+  };
+  if (mfma_first) pipeline(std::true_type{});
+  else pipeline(std::false_type{});
   __syncthreads();  // every wave is done with the rings: reuse them below
 
   // Merge the two key halves: waves kh = 1 hand (m, l, O) to waves kh = 0
