@@ -72,11 +72,11 @@ typedef struct {
  * The workspace carries split-softmax partial results and the hand-off
  * counters of the cross-workgroup combine. The counters always occupy the
  * first 64 KiB, whatever the shape; that region must be zero-filled once
- * before the first use, and every completed call leaves it zero again, so one
- * workspace can serve calls of any shapes in sequence with no clearing. One
- * workspace must not be used by two calls that can run at the same time (two
- * streams, or graph replays that overlap). Returns 0 and records an error
- * message if the shape is invalid.
+ * before the first use, and every completed call leaves it ready for the next
+ * (its arrival counts back at zero), so one workspace can serve calls of any
+ * shapes in sequence with no clearing. One workspace must not be used by two
+ * calls that can run at the same time (two streams, or graph replays that
+ * overlap). Returns 0 and records an error message if the shape is invalid.
  */
 size_t ta_tree_attn_workspace_bytes(const ta_kv_cache* cache, int32_t n_q_heads,
                                     int32_t prefix_len, int32_t n_tree);

@@ -138,8 +138,9 @@ _ws_lock = threading.Lock()
 def _workspace(device, nbytes):
     """A zero-filled workspace per device, grown on demand and kept for reuse.
 
-    The kernel leaves its counters at zero after every call, so reuse needs no
-    clearing; it does assume calls on one device are ordered (one stream).
+    Every call leaves the counters ready for the next (arrival counts back at
+    zero), so reuse needs no clearing; it does assume calls on one device are
+    ordered (one stream).
     """
     if nbytes == 0:
         return None

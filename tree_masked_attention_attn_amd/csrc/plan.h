@@ -40,7 +40,7 @@ struct AttnPlan {
   // at offset 0 in a fixed-size region, whatever the shape, so a workspace
   // that calls of different shapes share never finds partial data of an
   // earlier call where it expects a counter.
-  size_t ws_cnt_offset = 0;    // int32 x4 per group: arrivals, departures, give-up bits, pad
+  size_t ws_cnt_offset = 0;    // int32 x4 per group: arrivals, pad, give-up bits, pad
   size_t ws_ml_offset = 0;     // fp32 (max, sum) pairs [units][kRowsPerBlock][2]
   size_t ws_o_offset = 0;      // partial outputs [units][kRowsPerBlock][head_dim]: fp32, or fp16 for bf16
   size_t ws_bytes = 0;

@@ -333,13 +333,22 @@ __device__ void merge_rows(const TreeAttnArgs& a, int grp, int g, int rb, int r0
   using V4 = std::conditional_t<std::is_same_v<PT, float>, f32x4, f16x4>;
   const int S = a.splits, nr = r1 - r0;
   const size_t u0 = (size_t)grp * S;
-  const V4* parts = reinterpret_cast<const V4*>(a.ws_o) + u0 * kBlockRows * C4;
-  const float2* mls = a.ws_ml + u0 * kBlockRows;
+  // Device-scope loads (cache policy sc1), like the count that announced
+  // the partials: they do not return lines cached before the partials were
+  // written.
+  const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<V4*>(reinterpret_cast<const V4*>(a.ws_o) + u0 * kBlockRows * C4), 0,
+      S * kBlockRows * C4 * (int)sizeof(V4), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float2*>(a.ws_ml + u0 * kBlockRows), 0, S * kBlockRows * 8, 0x00020000);
   for (int it = tid; it < nr * C4; it += NTH) {
-    const int br = r0 + it / C4, c = it % C4;  // block row, float4 column
+    // block row, float4 column: consecutive threads take consecutive rows,
+    // which are consecutive in the lane-ordered partials (a wave's load
+    // touches a few cache lines instead of one per lane pair)
+    const int br = r0 + it % nr, c = it / nr;
     const int hrow = rb * kBlockRows + br;
     if (hrow >= a.rows_per_head) continue;
-    const V4* src = parts + part_index<D>(br, c);
+    const int pi = part_index<D>(br, c);
     float M = kNegInf, L = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int s0 = 0; s0 < S; s0 += 8) {
@@ -350,8 +359,15 @@ __device__ void merge_rows(const TreeAttnArgs& a, int grp, int g, int rb, int r0
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const int sk = s0 + k < S ? s0 + k : S - 1;
-        ml[k] = mls[(size_t)sk * kBlockRows + br];
-        const V4 x = src[(size_t)sk * kBlockRows * C4];
+        ml[k] = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(rm, (sk * kBlockRows + br) * 8, 0,
+                                                                                kWriteThrough));
+        V4 x;
+        if constexpr (std::is_same_v<PT, float>)
+          x = __builtin_bit_cast(V4, __builtin_amdgcn_raw_buffer_load_b128(
+                                         rp, (sk * kBlockRows * C4 + pi) * 16, 0, kWriteThrough));
+        else
+          x = __builtin_bit_cast(V4, __builtin_amdgcn_raw_buffer_load_b64(
+                                         rp, (sk * kBlockRows * C4 + pi) * 8, 0, kWriteThrough));
         o[k] = f32x4{static_cast<float>(x[0]), static_cast<float>(x[1]), static_cast<float>(x[2]),
                      static_cast<float>(x[3])};
       }
@@ -373,25 +389,33 @@ __device__ void merge_rows(const TreeAttnArgs& a, int grp, int g, int rb, int r0
 }
 
 // Cross-workgroup hand-off of one split, after its partial rows and (max,
-// sum) pairs are in the workspace (no grid barrier, no second launch). One
+// sum) pairs are in the workspace (no grid barrier, no second launch). Each
+// row-block group has an arrival count and a word of give-up bits. One
 // thread per workgroup:
-//  * counts in. Everything the split shares was written with device-scope
-//    stores (through L2 to memory), so waiting for those stores to complete
+//  * counts in with a wrapping increment: the count goes 0, 1, .., and back
+//    to 0 at the last arrival, which leaves it ready for the next call.
+//    Everything the split shares was written with device-scope stores
+//    (through L2 to memory), so waiting for those stores to complete
 //    (vmcnt 0) before a device-scope atomic publishes them; an agent-scope
 //    release fence would also write back every dirty line of this XCD's L2,
 //    which costs several microseconds and is not needed here;
-//  * waits a bounded number of polls for the other splits; the last to
-//    arrive never waits. Readers then take the agent-scope acquire (cache
-//    invalidation) before loading the partials;
-//  * a split that saw everyone arrive merges its own row slice (slice j of
-//    the block belongs to split j). One that stopped waiting sets its bit in
-//    the give-up mask, waits for that atomic to complete and looks once
-//    more; the last arrival completes its count-in before reading the mask
-//    and merges its own slice and every slice marked there. All these
-//    atomics are performed at one coherence point in the order each side
-//    completes them, so at least one side sees the other: every slice is
-//    merged, and a slice merged twice is written twice with the same bytes;
-//  * counts out; the last one out clears the group's words for the next call.
+//  * the others poll the count a bounded number of times until it has
+//    wrapped (it is at most their own arrival number again). Readers then
+//    load the partials with device-scope loads, which see memory as the
+//    count does, so no acquire fence (which would invalidate the whole L2
+//    of the XCD under the workgroups still streaming K and V) is needed;
+//  * a split that saw the wrap merges its own row slice (slice j of the
+//    block belongs to split j). One that stopped waiting sets its bit in the
+//    give-up bits, waits for that atomic to complete and looks at the count
+//    once more. The last arrival takes (and clears) the give-up bits after
+//    its increment has been performed, merges its own slice while that
+//    exchange is in flight, then every slice marked there. These atomics
+//    are performed at one coherence point in the order each side completes
+//    them: a bit set before the exchange is merged by the last arrival, one
+//    set after it sees the wrap and is merged by its owner. A slice merged
+//    twice is written twice with the same bytes, and a bit left set for a
+//    later call only makes that call's last arrival merge a slice that is
+//    already complete.
 template <typename T, typename PT, int D, int NTH>
 __device__ void split_handoff(const TreeAttnArgs& a, int* s_flags, int* s_mask, int grp, int g, int rb,
                               int split, int tid) {
@@ -402,44 +426,44 @@ __device__ void split_handoff(const TreeAttnArgs& a, int* s_flags, int* s_mask, 
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  int* gw = a.ws_cnt + (size_t)grp * 4;  // [0] arrivals, [1] departures, [2] give-up bits
+  unsigned* gw = reinterpret_cast<unsigned*>(a.ws_cnt) + (size_t)grp * 4;  // [0] arrivals, [2] give-up bits
+  unsigned others = 0;
   if (tid == 0) {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(0);
-    const int old = __hip_atomic_fetch_add(gw, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const bool last = old == a.splits - 1;
-    bool all_in = last;
-    for (int it = 0; !all_in && it < a.wait_polls; ++it) {
-      __builtin_amdgcn_s_sleep(2);
-      all_in = __hip_atomic_load(gw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.splits;
+    const unsigned old = __builtin_amdgcn_atomic_inc32(gw, a.splits - 1, __ATOMIC_RELAXED, "agent");
+    int flag;
+    if (old == (unsigned)a.splits - 1) {
+      // the last arrival; the exchange result is first needed after its merge
+      others = __hip_atomic_exchange(gw + 2, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      flag = 2;
+    } else {
+      bool all_in = false;
+      for (int it = 0; !all_in && it < a.wait_polls; ++it) {
+        __builtin_amdgcn_s_sleep(2);
+        all_in = __hip_atomic_load(gw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <= old;
+      }
+      if (!all_in) {
+        __hip_atomic_fetch_or(gw + 2, 1u << split, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(0);  // the mark is performed before looking again
+        all_in = __hip_atomic_load(gw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <= old;
+      }
+      flag = all_in ? 1 : 0;
     }
-    if (!all_in) {
-      __hip_atomic_fetch_or(gw + 2, 1 << split, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_waitcnt(0);  // the mark is performed before looking again
-      all_in = __hip_atomic_load(gw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.splits;
-    }
-    int others = 0;
-    if (last) others = __hip_atomic_load(gw + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & ~(1 << split);
-    if (all_in) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // invalidates this CU's L1 too
-    *s_flags = all_in ? 1 : 0;
-    *s_mask = others;
+    *s_flags = flag;
   }
   __syncthreads();
-  if (*s_flags) {
-    const int others = *s_mask;
+  const int flag = *s_flags;
+  if (flag) merge_rows<T, PT, D, NTH>(a, grp, g, rb, split * kBlockRows / a.splits,
+                                      (split + 1) * kBlockRows / a.splits, tid);
+  if (flag == 2) {
+    if (tid == 0) *s_mask = static_cast<int>(others & ~(1u << split));
+    __syncthreads();
+    const unsigned marked = static_cast<unsigned>(*s_mask);
     for (int j = 0; j < a.splits; ++j)
-      if (j == split || ((others >> j) & 1))
+      if ((marked >> j) & 1u)
         merge_rows<T, PT, D, NTH>(a, grp, g, rb, j * kBlockRows / a.splits, (j + 1) * kBlockRows / a.splits, tid);
-  }
-  __syncthreads();
-  if (tid == 0) {
-    const int old = __hip_atomic_fetch_add(gw + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (old == a.splits - 1) {
-      __hip_atomic_store(gw, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(gw + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(gw + 2, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
   }
 }
 
