@@ -12,9 +12,9 @@ Cache (each set is one layer's K/V, as in a real step where the other layers
 have evicted it). A short device sleep is queued first so the host runs ahead
 and the kernels execute back to back. HIP events on the launch stream bracket
 the timed region of K whole steps (-> ms_per_step), then K launches of each
-kernel alone (-> its mean launch duration, which the roofline uses), then the
-same launches each between their own events (-> the spread). Prints ONE JSON
-line.
+kernel alone, each between its own events (-> its mean launch duration, which
+the roofline uses, and the spread), then the same launches back to back
+(-> the launch period, dispatch gaps included). Prints ONE JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
 
@@ -355,12 +355,13 @@ def main():
     total_us, _, t_wall = timed(step, K)
 
     # Per-kernel figures, on the same stream and inputs: K launches of one
-    # kernel back to back between two events gives its average launch
-    # duration (what the roofline uses; it agrees with a kernel trace); the
-    # same launches each between their own events give the spread (each such
-    # interval also holds the event packets' dispatch, a few microseconds).
-    attn_b2b, _, _ = timed(attn, K)
+    # kernel, each between its own pair of events, give its average launch
+    # duration (what the roofline uses; a kernel trace of the same run gives
+    # the same figure to within the event packets' own cost); the same K
+    # launches back to back between two events give the launch period, which
+    # also holds the dispatch gap between consecutive kernels.
     _, attn_us, _ = timed(attn, K, each=True)
+    attn_b2b, _, _ = timed(attn, K)
     _, reroot_us, _ = timed(reroot, K, each=True)
     rr_b2b, _, _ = timed(reroot, K)
     # One input set only (L2 / Infinity Cache warm), labelled as such.
@@ -369,8 +370,8 @@ def main():
 
     nbytes, flops, anc = tree_attn_work(cfg, parent)
     rr_bytes = reroot_bytes(cfg, src_rows, P)
-    attn_mean = attn_b2b / K
-    rr_mean = rr_b2b / K
+    attn_mean = statistics.fmean(attn_us)
+    rr_mean = statistics.fmean(reroot_us)
     hbm_gbs = nbytes / (attn_mean * 1e-6) / 1e9
     tflops = flops / (attn_mean * 1e-6) / 1e12
     traffic = load_traffic(cfg)
@@ -402,13 +403,15 @@ def main():
                    "visible_tree_pairs": anc, "accepted_path": len(path), "survivors": len(surv),
                    "rotated_sets": rotate, "splits": ta.tree_attn_num_splits(sets[0]["k"], sets[0]["v"],
                                                                               cfg["n_q_heads"], P, cfg["n_tree"])},
-        "tree_attn": {"us_mean": round(attn_mean, 2), "us_event_p10": round(pct(attn_us, 10), 2),
-                      "us_event_p50": round(pct(attn_us, 50), 2), "us_event_p90": round(pct(attn_us, 90), 2),
-                      "hot_cache_us_event_p50": round(hot_us, 2),
+        "tree_attn": {"us_mean": round(attn_mean, 2), "us_p10": round(pct(attn_us, 10), 2),
+                      "us_p50": round(pct(attn_us, 50), 2), "us_p90": round(pct(attn_us, 90), 2),
+                      "us_launch_period_back_to_back": round(attn_b2b / K, 2),
+                      "hot_cache_us_p50": round(hot_us, 2),
                       "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
                       "hbm_GBs": round(hbm_gbs, 1), "hbm_frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
                       "TFLOPs": round(tflops, 1), "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4)},
-        "kv_reroot": {"us_mean": round(rr_mean, 2), "us_event_p50": round(pct(reroot_us, 50), 2),
+        "kv_reroot": {"us_mean": round(rr_mean, 2), "us_p50": round(pct(reroot_us, 50), 2),
+                      "us_launch_period_back_to_back": round(rr_b2b / K, 2),
                       "algorithmic_bytes": rr_bytes, "GBs": round(rr_bytes / (rr_mean * 1e-6) / 1e9, 2)},
         "wall_s_timed_region": round(t_wall, 4),
         "kernel_source_sha": kernel_source_sha(),
