@@ -21,6 +21,13 @@ namespace {
 // row block before leaving its rows to the last arrival.
 std::atomic<int32_t> g_wait_polls{20000};
 
+// floor(2^32 / d) + 1 (0 for d = 1): the kernels divide x < 2^17 by d < 2^15
+// as the high word of x times this (the product overshoots x / d by less
+// than 2^-15 < 1 / d, so its integer part is the quotient).
+uint32_t div_rcp(int32_t d) {
+  return d <= 1 ? 0u : static_cast<uint32_t>((uint64_t{1} << 32) / static_cast<uint64_t>(d) + 1);
+}
+
 ta_status device_error(hipError_t e, const char* what) {
   return fail(TA_ERR_DEVICE, std::string(what) + ": " + hipGetErrorString(e));
 }
@@ -127,6 +134,11 @@ ta_status ta_tree_attn(const void* q, const ta_kv_cache* cache, int32_t layer,
   a.n_units = plan.n_units;
   a.wait_polls = g_wait_polls.load();
   a.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(cache->head_dim)));
+  a.splits_rcp = div_rcp(plan.splits);
+  a.row_blocks_rcp = div_rcp(plan.row_blocks);
+  a.group_rcp = div_rcp(plan.group);
+  a.split_stages = plan.n_tiles / plan.splits;
+  a.split_extra = plan.n_tiles % plan.splits;
   hipError_t e = launch_tree_attn(a, cache->dtype, cache->head_dim, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return device_error(e, "tree_attn launch");
   return TA_OK;

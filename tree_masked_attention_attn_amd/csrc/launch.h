@@ -29,6 +29,15 @@ struct TreeAttnArgs {
   int32_t n_units;
   int32_t wait_polls;       // bound of the wait for the other splits of a group
   float scale_log2;         // log2(e) / sqrt(D)
+  // Reciprocals for the kernels' small divisions: floor(2^32 / d) + 1 for a
+  // divisor d > 1, 0 for d = 1 (see div_small in the kernel source).
+  uint32_t splits_rcp;
+  uint32_t row_blocks_rcp;
+  uint32_t group_rcp;
+  // Split s covers stages [s * split_stages + min(s, split_extra), ...) and
+  // one stage more than split_stages when s < split_extra.
+  int32_t split_stages;     // n_tiles / splits
+  int32_t split_extra;      // n_tiles % splits
   uint64_t anc[64];         // ancestor-or-self bitset per tree node
 };
 

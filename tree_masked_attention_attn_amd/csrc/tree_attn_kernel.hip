@@ -51,6 +51,33 @@ constexpr int kStage = kTile * kSub;
 constexpr int kBlockRows = 128;
 constexpr float kNegInf = -__builtin_huge_valf();
 
+// x / d for 0 <= x < 2^17 and 1 <= d < 2^15, rcp as TreeAttnArgs documents:
+// x * rcp / 2^32 exceeds x / d by less than 2^-15 < 1 / d, so its integer
+// part is the quotient. Two instructions instead of a division sequence.
+__device__ __forceinline__ int div_small(int x, int d, uint32_t rcp) {
+  return d == 1 ? x : static_cast<int>(__umulhi(static_cast<uint32_t>(x), rcp));
+}
+
+// The work unit of workgroup b: its split, (KV head, row block) group and
+// stage range. Consecutive workgroup ids go round-robin over the 8 XCDs, so
+// each XCD gets a contiguous run of units: the row blocks and splits of one
+// KV head then share that XCD's L2.
+struct Unit {
+  int u, split, grp, rb, g, t0, t1;
+};
+
+__device__ __forceinline__ Unit unit_of(const TreeAttnArgs& a, int b) {
+  Unit w;
+  w.u = (a.n_units % 8 == 0) ? (b % 8) * (a.n_units / 8) + b / 8 : b;
+  w.grp = div_small(w.u, a.splits, a.splits_rcp);
+  w.split = w.u - w.grp * a.splits;
+  w.g = div_small(w.grp, a.row_blocks, a.row_blocks_rcp);
+  w.rb = w.grp - w.g * a.row_blocks;
+  w.t0 = w.split * a.split_stages + min(w.split, a.split_extra);
+  w.t1 = w.t0 + a.split_stages + (w.split < a.split_extra ? 1 : 0);
+  return w;
+}
+
 // Position of key `k` (0..31 within a sub-tile) inside a transposed V row in
 // LDS. The PV MFMA reads, per lane half and k-slot, the keys that the S^T
 // accumulator gave that lane; this permutation makes those keys contiguous so
@@ -331,7 +358,7 @@ template <typename T, typename PT, int D, int NTH>
 __device__ void merge_rows(const TreeAttnArgs& a, int grp, int g, int rb, int r0, int r1, int tid) {
   constexpr int C4 = D / 4;  // chunks of 4 values per row
   using V4 = std::conditional_t<std::is_same_v<PT, float>, f32x4, f16x4>;
-  const int S = a.splits, nr = r1 - r0;
+  const int S = a.splits;
   const size_t u0 = (size_t)grp * S;
   // Device-scope loads (cache policy sc1), like the count that announced
   // the partials: they do not return lines cached before the partials were
@@ -341,11 +368,14 @@ __device__ void merge_rows(const TreeAttnArgs& a, int grp, int g, int rb, int r0
       S * kBlockRows * C4 * (int)sizeof(V4), 0x00020000);
   const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<float2*>(a.ws_ml + u0 * kBlockRows), 0, S * kBlockRows * 8, 0x00020000);
-  for (int it = tid; it < nr * C4; it += NTH) {
-    // block row, float4 column: consecutive threads take consecutive rows,
-    // which are consecutive in the lane-ordered partials (a wave's load
-    // touches a few cache lines instead of one per lane pair)
-    const int br = r0 + it % nr, c = it / nr;
+  // Thread tid takes float4 column c of rows r0 + tid % RPP, + RPP, ...:
+  // consecutive threads take consecutive rows, which are consecutive in the
+  // lane-ordered partials (a wave's load touches a few cache lines instead
+  // of one per lane pair).
+  constexpr int RPP = NTH / C4;  // rows per pass
+  static_assert(RPP * C4 == NTH && (RPP & (RPP - 1)) == 0, "threads per pass");
+  const int c = tid / RPP;
+  for (int br = r0 + tid % RPP; br < r1; br += RPP) {
     const int hrow = rb * kBlockRows + br;
     if (hrow >= a.rows_per_head) continue;
     const int pi = part_index<D>(br, c);
@@ -383,7 +413,7 @@ __device__ void merge_rows(const TreeAttnArgs& a, int grp, int g, int rb, int r0
         M = Mn;
       }
     }
-    const int nd = hrow / a.group, hd = g * a.group + hrow % a.group;
+    const int nd = div_small(hrow, a.group, a.group_rcp), hd = g * a.group + hrow - nd * a.group;
     store4<T>(static_cast<T*>(a.out) + ((size_t)nd * a.n_q_heads + hd) * D + 4 * c, acc * (1.f / L));
   }
 }
@@ -455,15 +485,16 @@ __device__ void split_handoff(const TreeAttnArgs& a, int* s_flags, int* s_mask, 
   }
   __syncthreads();
   const int flag = *s_flags;
-  if (flag) merge_rows<T, PT, D, NTH>(a, grp, g, rb, split * kBlockRows / a.splits,
-                                      (split + 1) * kBlockRows / a.splits, tid);
+  if (flag) merge_rows<T, PT, D, NTH>(a, grp, g, rb, div_small(split * kBlockRows, a.splits, a.splits_rcp),
+                                      div_small((split + 1) * kBlockRows, a.splits, a.splits_rcp), tid);
   if (flag == 2) {
     if (tid == 0) *s_mask = static_cast<int>(others & ~(1u << split));
     __syncthreads();
     const unsigned marked = static_cast<unsigned>(*s_mask);
     for (int j = 0; j < a.splits; ++j)
       if ((marked >> j) & 1u)
-        merge_rows<T, PT, D, NTH>(a, grp, g, rb, j * kBlockRows / a.splits, (j + 1) * kBlockRows / a.splits, tid);
+        merge_rows<T, PT, D, NTH>(a, grp, g, rb, div_small(j * kBlockRows, a.splits, a.splits_rcp),
+                                  div_small((j + 1) * kBlockRows, a.splits, a.splits_rcp), tid);
   }
 }
 
@@ -485,25 +516,17 @@ void tree_attn_kernel(const TreeAttnArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[2 * L::BUF];
   __shared__ int s_flags, s_taken;
 
-  // Work unit. Consecutive workgroup ids go round-robin over the 8 XCDs, so
-  // give each XCD a contiguous run of units: the row blocks and splits of one
-  // KV head then share that XCD's L2.
-  const int b = blockIdx.x;
-  const int u = (a.n_units % 8 == 0) ? (b % 8) * (a.n_units / 8) + b / 8 : b;
-  const int split = u % a.splits;
-  const int grp = u / a.splits;  // (KV head, row block)
-  const int rb = grp % a.row_blocks;
-  const int g = grp / a.row_blocks;
-  const int t0 = (int)((long long)split * a.n_tiles / a.splits);       // in kStage-key stages
-  const int t1 = (int)((long long)(split + 1) * a.n_tiles / a.splits);
+  const Unit un = unit_of(a, blockIdx.x);
+  const int u = un.u, split = un.split, grp = un.grp, rb = un.rb, g = un.g;
+  const int t0 = un.t0, t1 = un.t1;  // in kStage-key stages
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, l32 = lane & 31;
   const int rloc = wave * 32 + l32;          // row within the block
   const int row = rb * kBlockRows + rloc;    // row within the KV head
   const bool row_ok = row < a.rows_per_head;
-  const int node = row_ok ? row / a.group : 0;
-  const int head = g * a.group + (row_ok ? row % a.group : 0);
+  const int node = row_ok ? div_small(row, a.group, a.group_rcp) : 0;
+  const int head = g * a.group + (row_ok ? row - node * a.group : 0);
   const uint64_t anc = row_ok ? a.anc[node] : 0;
 
   const T* kh = static_cast<const T*>(a.k) + (size_t)g * a.kv_head_stride;
@@ -786,7 +809,10 @@ __device__ __forceinline__ void bf_dma_q_anc(unsigned lds, const TreeAttnArgs& a
       const int row = p / G::CPR, ch = (p % G::CPR) ^ bf_ksw<D>(row);
       const int hr = rb * kBlockRows + 64 * h + row;
       int off = qbytes;  // out of range: zeros
-      if (hr < a.rows_per_head) off = ((hr / a.group) * a.n_q_heads + g * a.group + hr % a.group) * G::ROWB + ch * 16;
+      if (hr < a.rows_per_head) {
+        const int nd = div_small(hr, a.group, a.group_rcp);
+        off = (nd * a.n_q_heads + g * a.group + hr - nd * a.group) * G::ROWB + ch * 16;
+      }
       bf_dma16(r, lds + (h ? G::QSTAGE1 : G::QSTAGE0) + op * 1024, off);
     }
   if (wave == 0) {
@@ -1135,15 +1161,10 @@ void tree_attn_bf16_kernel(const TreeAttnArgs a) {
   __shared__ int s_flags, s_taken;
   __shared__ int s_pair[4];  // waves seen per SIMD
 
-  const int b = blockIdx.x;
-  const int u = (a.n_units % 8 == 0) ? (b % 8) * (a.n_units / 8) + b / 8 : b;
-  const int split = u % a.splits;
-  const int grp = u / a.splits;
-  const int rb = grp % a.row_blocks;
-  const int g = grp / a.row_blocks;
-  const int t0 = (int)((long long)split * a.n_tiles / a.splits);  // in 64-key stages
-  const int t1 = (int)((long long)(split + 1) * a.n_tiles / a.splits);
-  const int n = t1 - t0;  // >= 1
+  const Unit un = unit_of(a, blockIdx.x);
+  const int u = un.u, split = un.split, grp = un.grp, rb = un.rb, g = un.g;
+  const int t0 = un.t0, t1 = un.t1;  // in 64-key stages
+  const int n = t1 - t0;             // >= 1
 
   // wave is uniform: readfirstlane lets the compiler keep it (and all that
   // derives from it) in scalar registers, with scalar branches
@@ -1196,8 +1217,8 @@ void tree_attn_bf16_kernel(const TreeAttnArgs a) {
   for (int nt = 0; nt < NT; ++nt) {
     const int row = rb * kBlockRows + 32 * (NT * rg + nt) + l32;
     row_ok[nt] = row < a.rows_per_head;
-    node[nt] = row_ok[nt] ? row / a.group : 0;
-    head[nt] = g * a.group + (row_ok[nt] ? row % a.group : 0);
+    node[nt] = row_ok[nt] ? div_small(row, a.group, a.group_rcp) : 0;
+    head[nt] = g * a.group + (row_ok[nt] ? row - node[nt] * a.group : 0);
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) w.o[nt][dt] = f32x16{};
     w.m_ref[nt] = kNegInf;
