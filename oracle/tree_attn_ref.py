@@ -76,12 +76,14 @@ def _as_f64(x):
     return np.asarray(x, dtype=np.float64)
 
 
-def _check_shapes(q, k_layer, v_layer, prefix_len, n_tree, n_kv_heads):
+def _check_shapes(q, k_layer, v_layer, prefix_len, n_tree, n_kv_heads, q_first=0):
     if q.ndim != 3 or k_layer.ndim != 3 or v_layer.shape != k_layer.shape:
-        raise ValueError("q must be [n_tree, n_q_heads, head_dim]; k, v [n_kv_heads, capacity, head_dim]")
+        raise ValueError("q must be [n_rows, n_q_heads, head_dim]; k, v [n_kv_heads, capacity, head_dim]")
     n, hq, d = q.shape
-    if n != n_tree:
-        raise ValueError("q rows must equal the number of tree nodes")
+    if not 0 <= q_first <= n_tree:
+        raise ValueError("q_first must be in [0, n_tree]")
+    if n != n_tree - q_first:
+        raise ValueError("q rows must equal the number of tree nodes from q_first on")
     if k_layer.shape[0] != n_kv_heads or k_layer.shape[2] != d:
         raise ValueError("k/v head count or head_dim mismatch")
     if hq % n_kv_heads:
@@ -90,11 +92,12 @@ def _check_shapes(q, k_layer, v_layer, prefix_len, n_tree, n_kv_heads):
         raise ValueError("prefix_len + n_tree exceeds the cache capacity")
 
 
-def tree_attn_ref(q, k_layer, v_layer, prefix_len, parent, n_kv_heads):
+def tree_attn_ref(q, k_layer, v_layer, prefix_len, parent, n_kv_heads, q_first=0):
     """Tree-masked attention of every (node, query head), one at a time.
 
     Arguments:
-        q: ``[n_tree, n_q_heads, head_dim]`` queries of the tree tokens.
+        q: ``[n_tree - q_first, n_q_heads, head_dim]``: row ``r`` is the query
+            of tree node ``q_first + r``.
         k_layer, v_layer: ``[n_kv_heads, capacity, head_dim]``: one layer of the
             cache. Slot ``t < prefix_len`` holds verified token ``t``; slot
             ``prefix_len + j`` holds tree node ``j``. Slots at or beyond
@@ -103,46 +106,51 @@ def tree_attn_ref(q, k_layer, v_layer, prefix_len, parent, n_kv_heads):
         parent: ``parent[i]`` in ``{-1} U [0, i)``.
         n_kv_heads: KV heads; query head ``h`` uses KV head
             ``h // (n_q_heads // n_kv_heads)``.
+        q_first: the first tree node that has a query (0: all of them). The
+            draft-expansion step queries only the newest nodes; the keys are
+            the whole prefix and tree either way.
 
-    Returns ``[n_tree, n_q_heads, head_dim]`` float64. For node ``i`` and head
+    Returns ``[n_tree - q_first, n_q_heads, head_dim]`` float64. For node ``i`` and head
     ``h`` with KV head ``g``: scores ``s_t = <q[i,h], K[g,t]> / sqrt(head_dim)``
     over the key set ``{0..prefix_len-1} U {prefix_len + j : j in anc*(i)}``,
     weights ``exp(s - max s)``, output the weighted mean of ``V[g, t]``.
     """
     par = check_parent(parent)
     q = _as_f64(q)
-    _check_shapes(q, k_layer, v_layer, prefix_len, len(par), n_kv_heads)
+    _check_shapes(q, k_layer, v_layer, prefix_len, len(par), n_kv_heads, q_first)
     n, hq, d = q.shape
     group = hq // n_kv_heads
     scale = 1.0 / math.sqrt(d)
     out = np.empty((n, hq, d), dtype=np.float64)
-    for i in range(n):
+    for r in range(n):
+        i = q_first + r
         keys = list(range(prefix_len)) + [prefix_len + j for j in ancestors_inclusive(par, i)]
         for h in range(hq):
             g = h // group
             kk = _as_f64(k_layer[g, keys])
             vv = _as_f64(v_layer[g, keys])
-            s = (kk @ q[i, h]) * scale
+            s = (kk @ q[r, h]) * scale
             w = np.exp(s - s.max())
-            out[i, h] = (w @ vv) / w.sum()
+            out[r, h] = (w @ vv) / w.sum()
     return out
 
 
-def tree_attn_dense_ref(q, k_layer, v_layer, prefix_len, parent, n_kv_heads):
+def tree_attn_dense_ref(q, k_layer, v_layer, prefix_len, parent, n_kv_heads, q_first=0):
     """Same result as ``tree_attn_ref``, computed as dense masked softmax.
 
     The mask over the ``prefix_len + n_tree`` visible slots is all-True on the
-    prefix and ``visibility_matrix(parent)`` on the tree block. Masked scores
-    are set to ``-inf`` before the softmax, so their weights are exactly 0.
+    prefix and ``visibility_matrix(parent)`` on the tree block (its rows from
+    ``q_first`` on). Masked scores are set to ``-inf`` before the softmax, so
+    their weights are exactly 0.
     """
     par = check_parent(parent)
     q = _as_f64(q)
-    _check_shapes(q, k_layer, v_layer, prefix_len, len(par), n_kv_heads)
+    _check_shapes(q, k_layer, v_layer, prefix_len, len(par), n_kv_heads, q_first)
     n, hq, d = q.shape
     group = hq // n_kv_heads
-    total = prefix_len + n
+    total = prefix_len + len(par)
     mask = np.ones((n, total), dtype=bool)
-    mask[:, prefix_len:] = visibility_matrix(par)
+    mask[:, prefix_len:] = visibility_matrix(par)[q_first:]
     out = np.empty((n, hq, d), dtype=np.float64)
     for g in range(n_kv_heads):
         kk = _as_f64(k_layer[g, :total])

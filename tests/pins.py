@@ -76,6 +76,28 @@ def pin_chain_causal(attn, rng, prefix_len=37, n=9, hq=8, hkv=2, d=16):
     return float(np.abs(got - want).max())
 
 
+def pin_chain_frontier_causal(attn, rng, prefix_len=29, n=12, w=4, hq=4, hkv=2, d=8):
+    """Frontier-only queries on a chain tree are the last rows of causal attention.
+
+    Only the newest ``w`` nodes of the chain have queries (``q_first = n - w``);
+    the keys are the whole prefix and chain, so those rows must equal torch's
+    causal attention over the sequence of length ``prefix_len + n`` at its
+    last ``w`` positions.
+    """
+    L = prefix_len + n
+    q_seq = rand(rng, L, hq, d)
+    k_seq = rand(rng, L, hkv, d)
+    v_seq = rand(rng, L, hkv, d)
+    want = sdpa_causal(q_seq, k_seq, v_seq)[L - w:]
+    cap = L + 3
+    k = np.full((hkv, cap, d), np.nan)
+    v = np.full((hkv, cap, d), np.nan)
+    k[:, :L] = k_seq.transpose(1, 0, 2)
+    v[:, :L] = v_seq.transpose(1, 0, 2)
+    got = attn(q_seq[L - w:], k, v, prefix_len, chain_parent(n), hkv, q_first=n - w)
+    return float(np.abs(got - want).max())
+
+
 def pin_root_only_decode(attn, rng, prefix_len=50, hq=4, hkv=4, d=32):
     """A single node under the virtual root is plain one-token decode attention."""
     L = prefix_len + 1

@@ -122,6 +122,26 @@ def test_prefix_off_by_one_is_caught():
     assert attention_pins(bad) > 1e-3
 
 
+def test_frontier_rows_taken_from_the_wrong_nodes_are_caught():
+    """Frontier queries placed on the first tree nodes, or one node early."""
+    assert pins.pin_chain_frontier_causal(oracle.tree_attn_ref, np.random.default_rng(6)) < 1e-12
+
+    def first_nodes(q, k, v, P, parent, hkv, q_first=0):
+        n, w = len(parent), len(parent) - q_first
+        qq = np.zeros((n,) + np.shape(q)[1:])
+        qq[:w] = q
+        return oracle.tree_attn_dense_ref(qq, k, v, P, parent, hkv)[:w]
+
+    def one_early(q, k, v, P, parent, hkv, q_first=0):
+        n, w = len(parent), len(parent) - q_first
+        qq = np.zeros((n,) + np.shape(q)[1:])
+        qq[q_first - 1:n - 1] = q
+        return oracle.tree_attn_dense_ref(qq, k, v, P, parent, hkv)[q_first - 1:n - 1]
+
+    for bad in (first_nodes, one_early):
+        assert pins.pin_chain_frontier_causal(bad, np.random.default_rng(6)) > 1e-3
+
+
 def test_reroot_plan_slips_are_caught(monkeypatch):
     assert pins.pin_reroot_golden(oracle.reroot_plan_ref) == 0
     orig = reroot_mod.reroot_plan_ref

@@ -76,6 +76,35 @@ def test_bruteforce_every_node_of_every_small_tree_is_causal_after_reroot(n):
             assert err < TIGHT, (parent, x)
 
 
+@pytest.mark.parametrize("attn", [oracle.tree_attn_ref, oracle.tree_attn_dense_ref])
+@pytest.mark.parametrize("shape", [(29, 12, 4, 4, 2, 8), (0, 8, 8, 2, 1, 16), (5, 3, 1, 2, 2, 4)])
+def test_chain_frontier_queries_are_causal_attention(attn, shape):
+    P, n, w, hq, hkv, d = shape
+    assert pins.pin_chain_frontier_causal(attn, np.random.default_rng(15), P, n, w, hq, hkv, d) < TIGHT
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
+def test_bruteforce_frontier_rows_do_not_depend_on_other_queries(n):
+    """For every small tree and every q_first: both formulations give the
+    full tree's rows from q_first on, whatever the earlier nodes' queries are."""
+    rng = np.random.default_rng(300 + n)
+    P, hq, hkv, d = 2, 2, 1, 4
+    for parent in all_parent_arrays(n):
+        parent = list(parent)
+        k = rng.standard_normal((hkv, P + n, d))
+        v = rng.standard_normal((hkv, P + n, d))
+        q = rng.standard_normal((n, hq, d))
+        full = oracle.tree_attn_dense_ref(q, k, v, P, parent, hkv)
+        for qf in range(n + 1):
+            q2 = q.copy()
+            q2[:qf] = rng.standard_normal((qf, hq, d))  # the other nodes' queries change
+            for attn in (oracle.tree_attn_ref, oracle.tree_attn_dense_ref):
+                got = attn(q2[qf:], k, v, P, parent, hkv, q_first=qf)
+                assert got.shape == (n - qf, hq, d)
+                if n - qf:
+                    assert np.abs(got - full[qf:]).max() < TIGHT, (parent, qf)
+
+
 def test_constant_values_give_that_constant():
     rng = np.random.default_rng(14)
     P, n, hq, hkv, d = 20, 12, 6, 3, 8
