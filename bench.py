@@ -72,15 +72,16 @@ def tree_attn_work(cfg, parent):
     pairs (ancestors and self).
     """
     P, n, hq, hkv, d = cfg["prefix"], cfg["n_tree"], cfg["n_q_heads"], cfg["n_kv_heads"], cfg["head_dim"]
+    qf = cfg.get("q_first", 0)  # query rows: nodes qf .. n-1
     es = 4 if cfg["dtype"] == "f32" else 2
     anc = 0
-    for i in range(n):
+    for i in range(qf, n):
         j = i
         while j != -1:
             anc += 1
             j = parent[j]
-    nbytes = 2 * hkv * d * es * (P + n) + 2 * n * hq * d * es + 4 * n
-    flops = 4 * d * hq * (n * P + anc)
+    nbytes = 2 * hkv * d * es * (P + n) + 2 * (n - qf) * hq * d * es + 4 * n
+    flops = 4 * d * hq * ((n - qf) * P + anc)
     return nbytes, flops, anc
 
 
@@ -123,28 +124,31 @@ def cpu_baseline(cfg, x, path, surv, budget_s):
     k = W.to_f64(x["k"][0])
     v = W.to_f64(x["v"][0])
     P, parent, n = x["prefix_len"], x["parent"], cfg["n_tree"]
+    qf = x.get("q_first", 0)
+    rows = n - qf
     with threadpool_limits(limits=cores):
         t0 = time.perf_counter()
         done = 0
-        # one node at a time (its own ancestors only), until the time budget is spent
-        while done < n and time.perf_counter() - t0 < budget_s:
-            _one_node(oracle, q, k, v, P, parent, done, cfg["n_kv_heads"])
+        # one query node at a time (its own ancestors only), until the time budget is spent
+        while done < rows and time.perf_counter() - t0 < budget_s:
+            _one_node(oracle, q, k, v, P, parent, qf, qf + done, cfg["n_kv_heads"])
             done += 1
         attn_s = (time.perf_counter() - t0) / done
         kb, vb = W.raw_bits(x["k"]), W.raw_bits(x["v"])
         t1 = time.perf_counter()
         oracle.kv_reroot_ref(kb, vb, P, parent, path, surv)
         reroot_s = time.perf_counter() - t1
-    step_us = (attn_s * n + reroot_s) * 1e6
+    step_us = (attn_s * rows + reroot_s) * 1e6
     return {"value": round(step_us, 1), "unit": "us/step", "cores": cores, "kind": "oracle",
-            "sample": f"tree_attn_ref on {done} of {n} tree nodes (all heads, full prefix), scaled x{n / done:.2f} "
-                      f"to the whole tree, plus one kv_reroot_ref of the same cache; numpy fp64"}
+            "sample": f"tree_attn_ref on {done} of {rows} query nodes (all heads, full prefix), scaled "
+                      f"x{rows / done:.2f} to all of them, plus one kv_reroot_ref of the same cache; numpy fp64"}
 
 
-def _one_node(oracle, q, k, v, P, parent, i, hkv):
-    """Output of node i alone: the oracle on the tree truncated after node i
-    (node i's ancestors all precede it), keeping only row i."""
-    return oracle.tree_attn_ref(q[: i + 1], k, v, P, parent[: i + 1], hkv)[i]
+def _one_node(oracle, q, k, v, P, parent, qf, i, hkv):
+    """Output of query node i alone: the oracle on the tree truncated after
+    node i (its ancestors all precede it), with node i as the only query."""
+    r = i - qf
+    return oracle.tree_attn_ref(q[r: r + 1], k, v, P, parent[: i + 1], hkv, q_first=i)[0]
 
 
 # --------------------------------------------------------------------------
@@ -295,7 +299,8 @@ def main():
                          out=torch.empty_like(base["q"], device=dev)))
         if r:  # distinct values per set (cheap perturbation on the GPU)
             sets[-1]["k"].mul_(1.0 + 1e-3 * r)
-    ws_bytes = ta.tree_attn_workspace_bytes(sets[0]["k"], sets[0]["v"], cfg["n_q_heads"], P, cfg["n_tree"])
+    qf = base["q_first"]
+    ws_bytes = ta.tree_attn_workspace_bytes(sets[0]["k"], sets[0]["v"], cfg["n_q_heads"], P, cfg["n_tree"], qf)
     ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
@@ -309,7 +314,7 @@ def main():
 
     def attn(i):
         s = sets[i % rotate]
-        ta.tree_attn(s["q"], s["k"], s["v"], P, parent, out=s["out"], workspace=ws)
+        ta.tree_attn(s["q"], s["k"], s["v"], P, parent, out=s["out"], workspace=ws, q_first=qf)
 
     def reroot(i):
         s = sets[i % rotate]
@@ -399,10 +404,11 @@ def main():
         "dtype": cfg["dtype"],
         "data": "synthetic (seeded Gaussian q/k/v, width-8 max-likelihood tree)",
         "config": {"workload": cfg["name"], "n_q_heads": cfg["n_q_heads"], "n_kv_heads": cfg["n_kv_heads"],
-                   "head_dim": cfg["head_dim"], "prefix_len": P, "n_tree": cfg["n_tree"],
+                   "head_dim": cfg["head_dim"], "prefix_len": P, "n_tree": cfg["n_tree"], "q_first": qf,
                    "visible_tree_pairs": anc, "accepted_path": len(path), "survivors": len(surv),
                    "rotated_sets": rotate, "splits": ta.tree_attn_num_splits(sets[0]["k"], sets[0]["v"],
-                                                                              cfg["n_q_heads"], P, cfg["n_tree"])},
+                                                                              cfg["n_q_heads"], P, cfg["n_tree"],
+                                                                              qf)},
         "tree_attn": {"us_mean": round(attn_mean, 2), "us_p10": round(pct(attn_us, 10), 2),
                       "us_p50": round(pct(attn_us, 50), 2), "us_p90": round(pct(attn_us, 90), 2),
                       "us_launch_period_back_to_back": round(attn_b2b / K, 2),

@@ -107,6 +107,33 @@ ta_status ta_tree_attn(const void* q, const ta_kv_cache* cache, int32_t layer,
                        size_t workspace_bytes, void* stream);
 
 /*
+ * Tree-masked attention of one layer for the tree nodes q_first .. n_tree-1
+ * only: the draft-expansion step, where the queries are the newest leaves and
+ * the keys are the whole [prefix | tree]. Node i (i >= q_first) sees exactly
+ * what it sees in ta_tree_attn; ta_tree_attn is this call with q_first = 0.
+ *
+ * Source: the same passages as ta_tree_attn; the Pith review page,
+ * "Assumptions & free parameters", fixes the expansion width w (the newest
+ * w nodes of the tree are the ones expanded next).
+ *
+ *  q, out   device, [n_tree - q_first][n_q_heads][head_dim]: row r is tree
+ *           node q_first + r
+ *  q_first  0 <= q_first <= n_tree (q_first == n_tree is a no-op returning
+ *           TA_OK); any other value is TA_ERR_ARG
+ * Every other argument, limit and error as ta_tree_attn. The workspace size
+ * and split count of this call are ta_tree_attn_rows_workspace_bytes and
+ * ta_tree_attn_rows_num_splits (0 on an invalid shape).
+ */
+ta_status ta_tree_attn_rows(const void* q, const ta_kv_cache* cache, int32_t layer,
+                            int32_t prefix_len, const int32_t* parent, int32_t n_tree,
+                            int32_t q_first, int32_t n_q_heads, void* out, void* workspace,
+                            size_t workspace_bytes, void* stream);
+size_t ta_tree_attn_rows_workspace_bytes(const ta_kv_cache* cache, int32_t n_q_heads,
+                                         int32_t prefix_len, int32_t n_tree, int32_t q_first);
+int32_t ta_tree_attn_rows_num_splits(const ta_kv_cache* cache, int32_t n_q_heads,
+                                     int32_t prefix_len, int32_t n_tree, int32_t q_first);
+
+/*
  * Re-root every layer of the cache after a verification step.
  *
  *  accepted_path    host, n_accepted >= 0 nodes from a first-level node

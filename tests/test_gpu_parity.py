@@ -39,7 +39,7 @@ def check_close(got, ref, dtype, what=""):
 
 def gpu_attn(x, layer=0):
     q, k, v = x["q"].to(DEV), x["k"].to(DEV), x["v"].to(DEV)
-    out = ta.tree_attn(q, k, v, x["prefix_len"], x["parent"], layer=layer)
+    out = ta.tree_attn(q, k, v, x["prefix_len"], x["parent"], layer=layer, q_first=x.get("q_first", 0))
     torch.cuda.synchronize()
     return W.to_f64(out)
 
@@ -47,7 +47,7 @@ def gpu_attn(x, layer=0):
 def ref_attn(x, hkv, layer=0, dense=True):
     f = oracle.tree_attn_dense_ref if dense else oracle.tree_attn_ref
     return f(W.to_f64(x["q"]), W.to_f64(x["k"][layer]), W.to_f64(x["v"][layer]),
-             x["prefix_len"], x["parent"], hkv)
+             x["prefix_len"], x["parent"], hkv, q_first=x.get("q_first", 0))
 
 
 @pytest.mark.parametrize("name", ["tiny_fp32", "llama3_8b_verify", "llama3_70b_verify", "qwen2_72b_32k_verify"])
@@ -65,6 +65,38 @@ def test_config_parity(name):
         sub = dict(x, q=x["q"][: i + 1], parent=x["parent"][: i + 1])
         one = ref_attn(sub, cfg["n_kv_heads"], dense=False)[i]
         check_close(got[i], one, cfg["dtype"], f"{name} node {i}")
+
+
+@pytest.mark.parametrize("name", ["llama3_70b_verify_bs8", "draft_expand_w8"])
+def test_operating_point_and_frontier_parity(name):
+    """The pages' bs = 8 verify tree, and a draft-expansion step whose queries
+    are only the 8 newest leaves (q_first) against the whole prefix and tree."""
+    cfg = W.config(name)
+    say(f"[parity] {name} seed={cfg['seed']} P={cfg['prefix']} n={cfg['n_tree']} q_first={cfg.get('q_first', 0)}")
+    x = W.make_inputs(cfg)
+    got = gpu_attn(x)
+    ref = ref_attn(x, cfg["n_kv_heads"])
+    check_close(got, ref, cfg["dtype"], name)
+    qf = x["q_first"]
+    for r in sorted({0, got.shape[0] - 1}):
+        i = qf + r  # node i alone: the tree truncated after it, queried from node i on
+        sub = dict(x, q=x["q"][r: r + 1], parent=x["parent"][: i + 1], q_first=i)
+        one = ref_attn(sub, cfg["n_kv_heads"], dense=False)[0]
+        check_close(got[r], one, cfg["dtype"], f"{name} node {i}")
+
+
+def test_frontier_rows_edge_cases():
+    rng = np.random.default_rng(21)
+    cfg = dict(n_q_heads=12, n_kv_heads=4, head_dim=128, dtype="bf16", prefix=700, n_tree=40,
+               capacity=800, seed=0, value_scale=0.5, tree="random")
+    x = W.make_inputs(cfg, rng)
+    for qf in (0, 1, 17, 39):
+        say(f"[frontier] q_first={qf}")
+        sub = dict(x, q=x["q"][qf:], q_first=qf)
+        check_close(gpu_attn(sub), ref_attn(sub, cfg["n_kv_heads"]), "bf16", f"q_first {qf}")
+    q, k, v = x["q"].to(DEV), x["k"].to(DEV), x["v"].to(DEV)
+    empty = ta.tree_attn(q[40:], k, v, 700, x["parent"], q_first=40)  # no query rows: a no-op
+    assert empty.shape[0] == 0
 
 
 @pytest.mark.parametrize("name", ["tiny_fp32", "llama3_8b_verify", "llama3_70b_verify", "draft_loop_1b"])

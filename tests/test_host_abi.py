@@ -124,6 +124,23 @@ def test_empty_tree_is_a_no_op():
     assert _attn(_desc(), parent=[]) == ta.TA_OK
 
 
+def test_frontier_rows_validation():
+    d = _desc()
+    par, n = ta._i32([-1] * 8)
+
+    def rows(q_first, ws=None, ws_len=0):
+        return ta.lib().ta_tree_attn_rows(FAKE, ctypes.byref(d), 0, 8192, par, n, q_first, 64, FAKE, ws, ws_len,
+                                          None)
+    assert rows(-1) == ta.TA_ERR_ARG and rows(9) == ta.TA_ERR_ARG
+    assert rows(8) == ta.TA_OK  # no query rows: nothing is enqueued
+    assert rows(4) == ta.TA_ERR_ARG  # needs a workspace
+    lib = ta.lib()
+    full = lib.ta_tree_attn_rows_workspace_bytes(ctypes.byref(d), 64, 8192, 8, 0)
+    assert full == lib.ta_tree_attn_workspace_bytes(ctypes.byref(d), 64, 8192, 8)
+    assert lib.ta_tree_attn_rows_workspace_bytes(ctypes.byref(d), 64, 8192, 8, 9) == 0
+    assert lib.ta_tree_attn_rows_num_splits(ctypes.byref(d), 64, 8192, 8, 4) >= 1
+
+
 def test_workspace_and_split_plan():
     lib = ta.lib()
     d = _desc()

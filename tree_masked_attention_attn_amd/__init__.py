@@ -72,6 +72,16 @@ def lib():
             L.ta_tree_attn.argtypes = [ctypes.c_void_p, _CP, ctypes.c_int32, ctypes.c_int32, _I32P,
                                        ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_size_t, ctypes.c_void_p]
+            L.ta_tree_attn_rows.restype = ctypes.c_int
+            L.ta_tree_attn_rows.argtypes = [ctypes.c_void_p, _CP, ctypes.c_int32, ctypes.c_int32, _I32P,
+                                            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                            ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+            L.ta_tree_attn_rows_workspace_bytes.restype = ctypes.c_size_t
+            L.ta_tree_attn_rows_workspace_bytes.argtypes = [_CP, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                            ctypes.c_int32]
+            L.ta_tree_attn_rows_num_splits.restype = ctypes.c_int32
+            L.ta_tree_attn_rows_num_splits.argtypes = [_CP, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                       ctypes.c_int32]
             L.ta_kv_reroot.restype = ctypes.c_int
             L.ta_kv_reroot.argtypes = [_CP, ctypes.c_int32, _I32P, ctypes.c_int32, _I32P, ctypes.c_int32,
                                        _I32P, ctypes.c_int32, _I32P, _I32P, ctypes.c_void_p]
@@ -153,24 +163,27 @@ def _workspace(device, nbytes):
     return ws
 
 
-def tree_attn_workspace_bytes(k_cache, v_cache, n_q_heads, prefix_len, n_tree):
+def tree_attn_workspace_bytes(k_cache, v_cache, n_q_heads, prefix_len, n_tree, q_first=0):
     desc = _cache_desc(k_cache, v_cache, need_device=False)
-    return lib().ta_tree_attn_workspace_bytes(ctypes.byref(desc), n_q_heads, prefix_len, n_tree)
+    return lib().ta_tree_attn_rows_workspace_bytes(ctypes.byref(desc), n_q_heads, prefix_len, n_tree, q_first)
 
 
-def tree_attn_num_splits(k_cache, v_cache, n_q_heads, prefix_len, n_tree):
+def tree_attn_num_splits(k_cache, v_cache, n_q_heads, prefix_len, n_tree, q_first=0):
     desc = _cache_desc(k_cache, v_cache, need_device=False)
-    return lib().ta_tree_attn_num_splits(ctypes.byref(desc), n_q_heads, prefix_len, n_tree)
+    return lib().ta_tree_attn_rows_num_splits(ctypes.byref(desc), n_q_heads, prefix_len, n_tree, q_first)
 
 
-def tree_attn(q, k_cache, v_cache, prefix_len, parent, layer=0, out=None, workspace=None):
+def tree_attn(q, k_cache, v_cache, prefix_len, parent, layer=0, out=None, workspace=None, q_first=0):
     """Tree-masked attention of one layer; returns ``out`` (allocated if None).
 
-    ``parent`` is a host sequence of ints. The launch goes on torch's current
-    stream of q's device; nothing is synchronised.
+    ``parent`` is a host sequence of ints. With ``q_first > 0`` the queries
+    (and the output rows) are only the tree nodes ``q_first ..`` (the
+    draft-expansion step): ``q`` is ``[len(parent) - q_first, n_q_heads,
+    head_dim]``. The launch goes on torch's current stream of q's device;
+    nothing is synchronised.
     """
     if q.dim() != 3 or not q.is_contiguous() or not q.is_cuda:
-        raise ValueError("q must be a contiguous [n_tree, n_q_heads, head_dim] GPU tensor")
+        raise ValueError("q must be a contiguous [n_rows, n_q_heads, head_dim] GPU tensor")
     desc = _cache_desc(k_cache, v_cache)
     if q.dtype != k_cache.dtype or q.device != k_cache.device:
         raise ValueError("q must match the cache in dtype and device")
@@ -179,13 +192,19 @@ def tree_attn(q, k_cache, v_cache, prefix_len, parent, layer=0, out=None, worksp
     elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() or out.device != q.device:
         raise ValueError("out must be a contiguous tensor like q")
     par, n = _i32(parent)
-    nbytes = lib().ta_tree_attn_workspace_bytes(ctypes.byref(desc), q.shape[1], prefix_len, n)
+    if q.shape[0] != n - q_first:
+        raise ValueError("q must have one row per tree node from q_first on")
+    nbytes = lib().ta_tree_attn_rows_workspace_bytes(ctypes.byref(desc), q.shape[1], prefix_len, n, q_first)
     if workspace is None:
         workspace = _workspace(q.device, nbytes)
     ws_ptr = None if workspace is None else workspace.data_ptr()
     ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().ta_tree_attn(q.data_ptr(), ctypes.byref(desc), layer, prefix_len, par, n, q.shape[1],
-                              out.data_ptr(), ws_ptr, ws_len, _stream_ptr(q.device)))
+    if q_first == 0:
+        _check(lib().ta_tree_attn(q.data_ptr(), ctypes.byref(desc), layer, prefix_len, par, n, q.shape[1],
+                                  out.data_ptr(), ws_ptr, ws_len, _stream_ptr(q.device)))
+    else:
+        _check(lib().ta_tree_attn_rows(q.data_ptr(), ctypes.byref(desc), layer, prefix_len, par, n, q_first,
+                                       q.shape[1], out.data_ptr(), ws_ptr, ws_len, _stream_ptr(q.device)))
     return out
 
 

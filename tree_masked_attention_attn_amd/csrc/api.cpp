@@ -68,38 +68,56 @@ ta_status ta_kv_reroot_plan(int32_t prefix_len, int32_t capacity, const int32_t*
                         surviving_nodes, n_surviving, src_rows_out, new_parent, new_prefix_len);
 }
 
-size_t ta_tree_attn_workspace_bytes(const ta_kv_cache* cache, int32_t n_q_heads,
-                                    int32_t prefix_len, int32_t n_tree) {
+size_t ta_tree_attn_rows_workspace_bytes(const ta_kv_cache* cache, int32_t n_q_heads,
+                                         int32_t prefix_len, int32_t n_tree, int32_t q_first) {
   clear_error();
   AttnPlan p;
-  if (plan_tree_attn(cache, n_q_heads, prefix_len, n_tree, &p) != TA_OK) return 0;
+  if (plan_tree_attn(cache, n_q_heads, prefix_len, n_tree, q_first, &p) != TA_OK) return 0;
   return p.ws_bytes;
+}
+
+size_t ta_tree_attn_workspace_bytes(const ta_kv_cache* cache, int32_t n_q_heads,
+                                    int32_t prefix_len, int32_t n_tree) {
+  return ta_tree_attn_rows_workspace_bytes(cache, n_q_heads, prefix_len, n_tree, 0);
+}
+
+int32_t ta_tree_attn_rows_num_splits(const ta_kv_cache* cache, int32_t n_q_heads, int32_t prefix_len,
+                                     int32_t n_tree, int32_t q_first) {
+  clear_error();
+  AttnPlan p;
+  if (plan_tree_attn(cache, n_q_heads, prefix_len, n_tree, q_first, &p) != TA_OK) return 0;
+  return p.splits > 0 ? p.splits : 1;
 }
 
 int32_t ta_tree_attn_num_splits(const ta_kv_cache* cache, int32_t n_q_heads, int32_t prefix_len,
                                 int32_t n_tree) {
-  clear_error();
-  AttnPlan p;
-  if (plan_tree_attn(cache, n_q_heads, prefix_len, n_tree, &p) != TA_OK) return 0;
-  return p.splits > 0 ? p.splits : 1;
+  return ta_tree_attn_rows_num_splits(cache, n_q_heads, prefix_len, n_tree, 0);
 }
 
 ta_status ta_tree_attn(const void* q, const ta_kv_cache* cache, int32_t layer,
                        int32_t prefix_len, const int32_t* parent, int32_t n_tree,
                        int32_t n_q_heads, void* out, void* workspace, size_t workspace_bytes,
                        void* stream) {
+  return ta_tree_attn_rows(q, cache, layer, prefix_len, parent, n_tree, 0, n_q_heads, out, workspace,
+                           workspace_bytes, stream);
+}
+
+ta_status ta_tree_attn_rows(const void* q, const ta_kv_cache* cache, int32_t layer,
+                            int32_t prefix_len, const int32_t* parent, int32_t n_tree, int32_t q_first,
+                            int32_t n_q_heads, void* out, void* workspace, size_t workspace_bytes,
+                            void* stream) {
   clear_error();
   ta_status st = check_cache(cache, true);
   if (st != TA_OK) return st;
   AttnPlan plan;
-  st = plan_tree_attn(cache, n_q_heads, prefix_len, n_tree, &plan);
+  st = plan_tree_attn(cache, n_q_heads, prefix_len, n_tree, q_first, &plan);
   if (st != TA_OK) return st;
   if (layer < 0 || layer >= cache->n_layers) return fail(TA_ERR_ARG, "layer out of range");
   TreeAttnArgs a;
   std::memset(&a, 0, sizeof(a));
   st = ancestor_bits(parent, n_tree, a.anc);
   if (st != TA_OK) return st;
-  if (n_tree == 0) return TA_OK;
+  if (plan.rows_per_head == 0) return TA_OK;  // no query rows
   if (q == nullptr || out == nullptr) return fail(TA_ERR_ARG, "q or out is null");
   if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(out)) & 15)
     return fail(TA_ERR_ARG, "q and out must be 16-byte aligned");
@@ -125,6 +143,7 @@ ta_status ta_tree_attn(const void* q, const ta_kv_cache* cache, int32_t layer,
   a.n_q_heads = n_q_heads;
   a.group = plan.group;
   a.n_tree = n_tree;
+  a.q_first = q_first;
   a.prefix_len = prefix_len;
   a.total_keys = plan.total_keys;
   a.rows_per_head = plan.rows_per_head;

@@ -19,10 +19,11 @@ struct TreeAttnArgs {
   int64_t kv_head_stride;   // elements from one KV head to the next (capacity * D)
   int32_t n_q_heads;
   int32_t group;            // query heads per KV head
-  int32_t n_tree;
+  int32_t n_tree;           // tree nodes (all of them are keys)
+  int32_t q_first;          // the query rows are tree nodes q_first .. n_tree-1
   int32_t prefix_len;
   int32_t total_keys;       // prefix_len + n_tree
-  int32_t rows_per_head;    // group * n_tree
+  int32_t rows_per_head;    // group * (n_tree - q_first)
   int32_t row_blocks;
   int32_t splits;
   int32_t n_tiles;

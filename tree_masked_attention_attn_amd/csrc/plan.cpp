@@ -71,13 +71,14 @@ ta_status check_cache(const ta_kv_cache* c, bool need_ptrs) {
 }
 
 ta_status plan_tree_attn(const ta_kv_cache* cache, int32_t n_q_heads, int32_t prefix_len,
-                         int32_t n_tree, AttnPlan* plan) {
+                         int32_t n_tree, int32_t q_first, AttnPlan* plan) {
   ta_status st = check_cache(cache, false);
   if (st != TA_OK) return st;
   if (n_tree < 0 || n_tree > TA_MAX_TREE)
     return fail(n_tree < 0 ? TA_ERR_ARG : TA_ERR_UNSUPPORTED,
                 "n_tree must be in [0, " + std::to_string(TA_MAX_TREE) + "]");
   if (prefix_len < 0) return fail(TA_ERR_ARG, "prefix_len is negative");
+  if (q_first < 0 || q_first > n_tree) return fail(TA_ERR_ARG, "q_first must be in [0, n_tree]");
   if (n_q_heads < 1 || n_q_heads % cache->n_kv_heads != 0)
     return fail(TA_ERR_UNSUPPORTED, "n_q_heads must be a positive multiple of n_kv_heads");
   const int32_t group = n_q_heads / cache->n_kv_heads;
@@ -89,11 +90,11 @@ ta_status plan_tree_attn(const ta_kv_cache* cache, int32_t n_q_heads, int32_t pr
   AttnPlan p;
   p.head_dim = cache->head_dim;
   p.group = group;
-  p.rows_per_head = group * n_tree;
+  p.rows_per_head = group * (n_tree - q_first);
   p.row_blocks = (p.rows_per_head + kRowsPerBlock - 1) / kRowsPerBlock;
   p.total_keys = prefix_len + n_tree;
   p.n_tiles = (p.total_keys + kKeyTile - 1) / kKeyTile;
-  if (n_tree == 0) {
+  if (p.rows_per_head == 0) {  // no query rows: nothing to do
     *plan = p;
     return TA_OK;
   }

@@ -30,7 +30,7 @@ ta_status check_cache(const ta_kv_cache* c, bool need_ptrs);
 struct AttnPlan {
   int32_t head_dim = 0;
   int32_t group = 0;           // query heads per KV head
-  int32_t rows_per_head = 0;   // group * n_tree
+  int32_t rows_per_head = 0;   // group * (n_tree - q_first): query rows per KV head
   int32_t row_blocks = 0;      // ceil(rows_per_head / kRowsPerBlock)
   int32_t total_keys = 0;      // prefix_len + n_tree
   int32_t n_tiles = 0;         // ceil(total_keys / kKeyTile): key stages
@@ -58,7 +58,7 @@ constexpr int32_t kGroupWords = 4;     // arrivals, departures, give-up bits, pa
 constexpr size_t kCounterBytes = kMaxGroups * kGroupWords * sizeof(int32_t);
 
 ta_status plan_tree_attn(const ta_kv_cache* cache, int32_t n_q_heads, int32_t prefix_len,
-                         int32_t n_tree, AttnPlan* plan);
+                         int32_t n_tree, int32_t q_first, AttnPlan* plan);
 
 // Re-root plan: src_rows[k] = prefix_len + order[k], order = path ++ survivors.
 ta_status plan_kv_reroot(int32_t prefix_len, int32_t capacity, const int32_t* parent,

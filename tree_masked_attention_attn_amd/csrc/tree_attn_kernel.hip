@@ -525,9 +525,9 @@ void tree_attn_kernel(const TreeAttnArgs a) {
   const int rloc = wave * 32 + l32;          // row within the block
   const int row = rb * kBlockRows + rloc;    // row within the KV head
   const bool row_ok = row < a.rows_per_head;
-  const int node = row_ok ? div_small(row, a.group, a.group_rcp) : 0;
+  const int node = row_ok ? div_small(row, a.group, a.group_rcp) : 0;  // query row (tree node q_first + node)
   const int head = g * a.group + (row_ok ? row - node * a.group : 0);
-  const uint64_t anc = row_ok ? a.anc[node] : 0;
+  const uint64_t anc = row_ok ? a.anc[a.q_first + node] : 0;
 
   const T* kh = static_cast<const T*>(a.k) + (size_t)g * a.kv_head_stride;
   const T* vh = static_cast<const T*>(a.v) + (size_t)g * a.kv_head_stride;
@@ -798,7 +798,7 @@ template <int D, int NW>
 __device__ __forceinline__ void bf_dma_q_anc(unsigned lds, const TreeAttnArgs& a, int g, int rb, int wave,
                                              int lane) {
   using G = BfGeo<D>;
-  const int qbytes = a.n_tree * a.n_q_heads * G::ROWB;
+  const int qbytes = (a.n_tree - a.q_first) * a.n_q_heads * G::ROWB;
   const i32x4 r = bf_rsrc(a.q, qbytes);
 #pragma unroll
   for (int h = 0; h < 2; ++h)
@@ -1239,7 +1239,7 @@ void tree_attn_bf16_kernel(const TreeAttnArgs a) {
   for (int nt = 0; nt < NT; ++nt) {
     const int row = 32 * (NT * rg + nt) + l32;
     bf_read_k<D>(w.qf[nt], lds0 + (row < 64 ? G::QSTAGE0 : G::QSTAGE1), (row >> 5) & 1, lane);
-    w.anc[nt] = row_ok[nt] ? reinterpret_cast<const uint64_t*>(lds + G::ANC)[node[nt]] : 0;
+    w.anc[nt] = row_ok[nt] ? reinterpret_cast<const uint64_t*>(lds + G::ANC)[a.q_first + node[nt]] : 0;
   }
   f32x16 sc[NT];
   bf16x8 pp[NT][2];

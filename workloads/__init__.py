@@ -37,6 +37,16 @@ CONFIGS = {
     "draft_loop_1b": dict(n_q_heads=32, n_kv_heads=8, head_dim=64, dtype="bf16",
                           prefix=4096, n_tree=64, capacity=8192, seed=4,
                           value_scale=1.0 / 8.0, tree="top8", iterations=100),
+    # The pages' operating point: a verify tree of bs = 8 nodes at 70B shapes
+    # (the 8 most likely nodes of the width-8 expansion; HBM-bound).
+    "llama3_70b_verify_bs8": dict(n_q_heads=64, n_kv_heads=8, head_dim=128, dtype="bf16",
+                                  prefix=8192, n_tree=8, capacity=8192 + 256, seed=5,
+                                  value_scale=1.0 / math.sqrt(128), tree="top8_bs8"),
+    # A draft-expansion step: only the w = 8 newest leaves of the 64-node tree
+    # are queries, against the whole [prefix | tree].
+    "draft_expand_w8": dict(n_q_heads=32, n_kv_heads=8, head_dim=64, dtype="bf16",
+                            prefix=4096, n_tree=64, q_first=56, capacity=4096 + 256, seed=6,
+                            value_scale=1.0 / 8.0, tree="top8"),
 }
 
 TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
@@ -160,10 +170,21 @@ def refill(rng, parent, scores, n_target=64, width=8):
     return parent, scores
 
 
+def best_nodes(parent, scores, k):
+    """The ``k`` highest-scoring nodes (ties: lower index first), renumbered in
+    ascending order. Scores are sums of log-probabilities along the path, so a
+    child never outscores its parent and the kept set is closed under parents."""
+    keep = sorted(sorted(range(len(parent)), key=lambda i: (-scores[i], i))[:k])
+    new = {old: j for j, old in enumerate(keep)}
+    return [new[parent[i]] if parent[i] >= 0 else -1 for i in keep], [scores[i] for i in keep]
+
+
 def make_tree(cfg, rng):
     if cfg["tree"] == "random":
         return random_parent(rng, cfg["n_tree"]), None
     parent, scores = top8_tree(rng)
+    if cfg["tree"] == "top8_bs8":
+        parent, scores = best_nodes(parent, scores, cfg["n_tree"])
     assert len(parent) == cfg["n_tree"]
     return parent, scores
 
@@ -180,7 +201,8 @@ def _draw(rng, shape, scale, dtype):
 def make_inputs(cfg, rng=None, n_layers=1, poison=True, value_scale=None):
     """Seeded q and KV cache for one config; all CPU torch tensors.
 
-    Returns a dict with ``q [n_tree, n_q_heads, head_dim]``,
+    Returns a dict with ``q [n_tree - q_first, n_q_heads, head_dim]`` (the
+    query rows are the tree nodes from ``cfg["q_first"]``, default 0) and
     ``k, v [n_layers, n_kv_heads, capacity, head_dim]``, ``parent``, ``scores``,
     ``prefix_len``. Slots at or beyond ``prefix + n_tree`` are NaN when
     ``poison`` (they must never be read), random otherwise.
@@ -191,14 +213,14 @@ def make_inputs(cfg, rng=None, n_layers=1, poison=True, value_scale=None):
     parent, scores = make_tree(cfg, rng)
     n, hq, hkv, d = cfg["n_tree"], cfg["n_q_heads"], cfg["n_kv_heads"], cfg["head_dim"]
     cap = cfg["capacity"]
-    q = _draw(rng, (n, hq, d), scale, cfg["dtype"])
+    q = _draw(rng, (n - cfg.get("q_first", 0), hq, d), scale, cfg["dtype"])
     k = _draw(rng, (n_layers, hkv, cap, d), scale, cfg["dtype"])
     v = _draw(rng, (n_layers, hkv, cap, d), scale, cfg["dtype"])
     if poison:
         end = cfg["prefix"] + n
         k[:, :, end:] = float("nan")
         v[:, :, end:] = float("nan")
-    return dict(q=q, k=k, v=v, parent=parent, scores=scores, prefix_len=cfg["prefix"])
+    return dict(q=q, k=k, v=v, parent=parent, scores=scores, prefix_len=cfg["prefix"], q_first=cfg.get("q_first", 0))
 
 
 def mask_probe_inputs(cfg, parent, n_layers=1):
