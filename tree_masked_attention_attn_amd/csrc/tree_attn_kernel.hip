@@ -349,8 +349,8 @@ __device__ __forceinline__ void put_ml(const PartialSink& k, int r, float m, flo
 }
 
 // Merge rows [r0, r1) of row block `grp` from all splits and write them to
-// `out` (PT: element type of the partial rows). One memory round trip per 8
-// splits: each thread loads, for its
+// `out` (PT: element type of the partial rows). One memory round trip per
+// batch of splits: each thread loads, for its
 // (row, float4 of head_dim), every split's (max, sum) pair and partial in one
 // batch, then combines them online in split order (deterministic for a
 // given shape): M is the running max, acc and L are rescaled by 2^(M_old - M).
@@ -381,34 +381,38 @@ __device__ void merge_rows(const TreeAttnArgs& a, int grp, int g, int rb, int r0
     const int pi = part_index<D>(br, c);
     float M = kNegInf, L = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < S; s0 += 8) {
-      // All 16 loads first, unconditionally (indices past the last split
-      // re-read split S - 1 and are ignored below): one round trip.
-      float2 ml[8];
-      f32x4 o[8];
+    // Batches of MB splits: all loads of a batch first, unconditionally (a
+    // split index past the last one falls outside the buffer ranges, reads
+    // zeros without a memory access and is ignored below), so that a batch
+    // costs one memory round trip. Eight per batch measured faster than one
+    // batch of 16 or 32 loads for 16 and 32 splits: the wider batches hold
+    // more registers while the loads are in flight.
+    constexpr int MB = 8;
+    for (int s0 = 0; s0 < S; s0 += MB) {
+      float2 ml[MB];
+      V4 o[MB];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int sk = s0 + k < S ? s0 + k : S - 1;
+      for (int k = 0; k < MB; ++k) {
+        const int sk = s0 + k;
         ml[k] = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(rm, (sk * kBlockRows + br) * 8, 0,
                                                                                 kWriteThrough));
-        V4 x;
         if constexpr (std::is_same_v<PT, float>)
-          x = __builtin_bit_cast(V4, __builtin_amdgcn_raw_buffer_load_b128(
-                                         rp, (sk * kBlockRows * C4 + pi) * 16, 0, kWriteThrough));
+          o[k] = __builtin_bit_cast(V4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            rp, (sk * kBlockRows * C4 + pi) * 16, 0, kWriteThrough));
         else
-          x = __builtin_bit_cast(V4, __builtin_amdgcn_raw_buffer_load_b64(
-                                         rp, (sk * kBlockRows * C4 + pi) * 8, 0, kWriteThrough));
-        o[k] = f32x4{static_cast<float>(x[0]), static_cast<float>(x[1]), static_cast<float>(x[2]),
-                     static_cast<float>(x[3])};
+          o[k] = __builtin_bit_cast(V4, __builtin_amdgcn_raw_buffer_load_b64(
+                                            rp, (sk * kBlockRows * C4 + pi) * 8, 0, kWriteThrough));
       }
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
+      for (int k = 0; k < MB; ++k) {
         // a split past the end, or one with no visible key for this row, adds nothing
         const bool ok = s0 + k < S && ml[k].x != kNegInf;
         const float Mn = ok ? fmaxf(M, ml[k].x) : M;
         const float sa = M == kNegInf ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
         const float sb = ok ? __builtin_amdgcn_exp2f(ml[k].x - Mn) : 0.f;
-        acc = acc * sa + o[k] * sb;
+        const f32x4 x = {static_cast<float>(o[k][0]), static_cast<float>(o[k][1]), static_cast<float>(o[k][2]),
+                         static_cast<float>(o[k][3])};
+        acc = acc * sa + x * sb;
         L = L * sa + ml[k].y * sb;
         M = Mn;
       }
@@ -1053,10 +1057,12 @@ __device__ __forceinline__ void bf_mfma_block(BfWave<D, NT>& w, f32x16 (&sn)[NT]
       const int k = i - NPV, cc = k / NT, nt = k % NT;
       sn[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[cc], w.qf[nt][cc], sn[nt], 0, 0, 0);
     }
-    if ((i * NOPS) % NM == 0 && i * NOPS / NM < NOPS) {  // spread evenly, kept in place
-      __builtin_amdgcn_sched_barrier(0);
-      dma(i * NOPS / NM);
-      __builtin_amdgcn_sched_barrier(0);
+    if constexpr (NOPS > 0) {
+      if ((i * NOPS) % NM == 0 && i * NOPS / NM < NOPS) {  // spread evenly, kept in place
+        __builtin_amdgcn_sched_barrier(0);
+        dma(i * NOPS / NM);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
 }
