@@ -52,7 +52,12 @@ constexpr int32_t kRowsPerWave = 32;   // query rows per wave (one 32-wide MFMA 
 constexpr int32_t kRowsPerBlock = kWaves * kRowsPerWave;
 constexpr int32_t kTargetUnits = 512;  // 2 workgroups per CU on a 256-CU part
 constexpr int32_t kMinTilesPerSplit = 2;
-constexpr int32_t kMaxSplits = 32;     // one give-up bit per split in a 32-bit word
+// At most 16 splits per row block (the give-up word would have room for 32):
+// past 16, the hand-off and merge of the extra partials cost more than the
+// shorter key ranges save, also when that leaves CUs idle (measured on a
+// bs=8 verify step and a one-row-block draft expansion: 16 splits beat 32 by
+// 10 to 25 percent).
+constexpr int32_t kMaxSplits = 16;
 constexpr int32_t kMaxGroups = 4096;   // (KV head, row block) groups with counters
 constexpr int32_t kGroupWords = 4;     // arrivals, departures, give-up bits, pad
 constexpr size_t kCounterBytes = kMaxGroups * kGroupWords * sizeof(int32_t);
