@@ -27,10 +27,15 @@ gather (re-root). Points the pages leave open are taken as follows:
 * the whole accepted path moves into the prefix; survivors keep ascending
   original order.
 
+Tree verification (``tree_verify_ref``) reads the acceptance rule as greedy:
+a drafted token is accepted when it equals the target's arg-max at its parent
+and every ancestor was accepted; the deepest such node ends the accepted path.
+
 Parity pinning: every function here is pinned by ``-m "not gpu"`` tests
 against torch's CPU ``scaled_dot_product_attention`` (causal and decode special
 cases), hand-derived golden fixtures, closed forms and brute force over all
-trees of up to six nodes. No function is "parity unpinned".
+trees of up to six nodes; verification against a top-down walk of the tree
+that consumes the target's tokens one at a time. No function is "parity unpinned".
 """
 
 from .tree_attn_ref import (  # noqa: F401
@@ -41,3 +46,4 @@ from .tree_attn_ref import (  # noqa: F401
     visibility_matrix,
 )
 from .kv_reroot_ref import check_reroot_args, kv_reroot_ref, reroot_plan_ref  # noqa: F401
+from .tree_verify_ref import row_argmax, tree_verify_ref  # noqa: F401

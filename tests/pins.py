@@ -181,3 +181,103 @@ def pin_reroot_golden(plan):
 
 def scale_of(d):
     return 1.0 / math.sqrt(d)
+
+
+# ---------------------------------------------------------------------------
+# Tree verification (greedy acceptance). The pins below compute the target's
+# choices with a plain loop and find the accepted path by walking DOWN from
+# the virtual root along matching children, the way speculative decoding
+# consumes the target's tokens one at a time; the oracle instead checks every
+# node's root path bottom-up.
+
+
+def loop_argmax(row):
+    """First index of the maximum, by a plain scan (-0.0 == +0.0 as floats)."""
+    best = 0
+    for j in range(1, len(row)):
+        if float(row[j]) > float(row[best]):
+            best = j
+    return best
+
+
+def walk_accepted(choice, tokens, parent):
+    """Deepest node reachable from the virtual root through matching children.
+
+    Explores every matching child (siblings may share a token), so the result
+    is the deepest such node, the lowest index among equally deep ones.
+    """
+    n = len(parent)
+    children = {-1: []}
+    for i in range(n):
+        children.setdefault(i, [])
+        children[int(parent[i])].append(i)
+    best = (0, 0, [])  # (depth, -index, path)
+    stack = [(-1, [])]
+    while stack:
+        node, path = stack.pop()
+        want = choice[0 if node < 0 else 1 + node]
+        for c in children[node]:
+            if int(tokens[c]) == want:
+                p = path + [c]
+                if (len(p), -c) > best[:2]:
+                    best = (len(p), -c, p)
+                stack.append((c, p))
+    path = best[2]
+    bonus = choice[0 if not path else 1 + path[-1]]
+    return path, bonus
+
+
+def golden_verify_cases():
+    cases = load_golden("verify_cases.json")["cases"]
+    for c in cases:
+        c = dict(c)
+        c["logits"] = np.array([[float(v) for v in row] for row in c["logits"]], dtype=np.float32)
+        yield c
+
+
+def pin_verify_golden(verify):
+    """Number of hand-worked cases whose path, bonus or choices differ."""
+    bad = 0
+    for c in golden_verify_cases():
+        path, bonus, choice = verify(c["logits"], c["tokens"], c["parent"])
+        bad += (list(path) != c["path"]) or (int(bonus) != c["bonus"]) or (list(map(int, choice)) != c["choice"])
+    return bad
+
+
+def pin_verify_walk(verify, parents, rng, vocab=3, draws=3):
+    """Mismatches against the top-down walk over the given trees.
+
+    Logits are small integers (many equal maxima) and tokens come from a tiny
+    vocabulary (siblings often share one), so ties decide many cases.
+    """
+    bad = 0
+    for parent in parents:
+        n = len(parent)
+        for _ in range(draws):
+            logits = rng.integers(-2, 3, size=(n + 1, vocab)).astype(np.float32)
+            choice = [loop_argmax(r) for r in logits]
+            # bias tokens toward the target's choice so paths get long
+            tokens = [choice[0 if parent[i] < 0 else 1 + parent[i]] if rng.random() < 0.7
+                      else int(rng.integers(0, vocab)) for i in range(n)]
+            want_path, want_bonus = walk_accepted(choice, tokens, parent)
+            path, bonus, got_choice = verify(logits, tokens, parent)
+            bad += (list(path) != want_path) or (int(bonus) != want_bonus) or (list(map(int, got_choice)) != choice)
+    return bad
+
+
+def pin_verify_chain(verify, rng, n=12, vocab=50):
+    """Chain tree whose drafted tokens agree with the target for exactly k
+    steps: the accepted length is k and the bonus is the target's choice at
+    node k - 1 (a planted unique maximum per row)."""
+    bad = 0
+    parent = chain_parent(n)
+    for k in range(n + 1):
+        planted = rng.integers(0, vocab, size=n + 1)
+        logits = rng.standard_normal((n + 1, vocab)).astype(np.float32)
+        logits[np.arange(n + 1), planted] = 10.0
+        tokens = [int(planted[i]) for i in range(n)]  # node i follows row i
+        if k < n:
+            tokens[k] = int((planted[k] + 1) % vocab)
+        path, bonus, _ = verify(logits, tokens, parent)
+        bad += (list(path) != list(range(k))) or (int(bonus) != int(planted[k]))
+    return bad

@@ -6,6 +6,8 @@ least one pin reports an error far above its tolerance.
 """
 
 import importlib
+import itertools
+import os
 import math
 
 import numpy as np
@@ -174,3 +176,48 @@ def test_reroot_gather_slip_is_caught(monkeypatch):
     parent = [-1, -1, 1, 2]
     errs = [pins.pin_path_reroot_causal(oracle.tree_attn_ref, bad_reroot, parent, x, rng) for x in range(4)]
     assert max(errs) > 1e-3
+
+
+# ---------------------------------------------------------------------------
+# Tree verification: each mutant is the oracle's source with one slip.
+
+_VERIFY_SRC = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                                "oracle", "tree_verify_ref.py")).read()
+
+
+def _verify_mutant(old, new):
+    assert _VERIFY_SRC.count(old) == 1, old
+    ns = {"__name__": "oracle.tree_verify_mutant", "__package__": "oracle"}
+    exec(compile(_VERIFY_SRC.replace(old, new), "tree_verify_mutant", "exec"), ns)
+    return ns["tree_verify_ref"]
+
+
+def verify_pins(verify):
+    rng = np.random.default_rng(9)
+    parents = [list(p) for n in (3, 4) for p in itertools.product(*[range(-1, i) for i in range(n)])]
+    return (pins.pin_verify_golden(verify) + pins.pin_verify_walk(verify, parents, rng)
+            + pins.pin_verify_chain(verify, rng))
+
+
+def test_unmutated_verify_passes_every_pin():
+    assert verify_pins(oracle.tree_verify_ref) == 0
+
+
+VERIFY_SLIPS = {
+    "own_row_instead_of_parent_row": ("0 if par[i] < 0 else 1 + par[i]", "1 + i"),
+    "matches_without_ancestors": ("all(matches[a] for a in chain)", "matches[i]"),
+    "ties_to_highest_index": ("len(chain) > best_depth", "len(chain) >= best_depth"),
+    "bonus_from_parent_row": ("bonus = int(choice[0 if best < 0 else 1 + best])",
+                              "bonus = int(choice[0 if best < 0 else 1 + par[best]])"),
+    "argmax_last_of_equal_maxima": ("return np.argmax(x, axis=1).astype(np.int64)",
+                                    "return (x.shape[1] - 1 - np.argmax(x[:, ::-1], axis=1)).astype(np.int64)"),
+    "path_leaf_to_root": ("path = sorted(ancestors_inclusive(par, best))",
+                          "path = sorted(ancestors_inclusive(par, best), reverse=True)"),
+    "argmax_on_bit_patterns": ("x = np.asarray(logits, dtype=np.float64)",
+                               "x = np.asarray(logits, dtype=np.float32).view(np.int32).astype(np.float64)"),
+}
+
+
+@pytest.mark.parametrize("slip", list(VERIFY_SLIPS))
+def test_verify_slip_is_caught(slip):
+    assert verify_pins(_verify_mutant(*VERIFY_SLIPS[slip])) > 0

@@ -274,3 +274,43 @@ def test_reroot_works_on_raw_bf16_words():
     assert k2.dtype == np.uint16 and new_p == 6 and new_par == [-1, -1]
     assert np.array_equal(k2[:, :, 6], k[:, :, 7]) and np.array_equal(k2[:, :, 7], k[:, :, 8])
     assert np.array_equal(k2[:, :, 8:], k[:, :, 8:])
+
+
+# ---------------------------------------------------------------------------
+# Tree verification
+
+def test_verify_hand_worked_cases():
+    assert pins.pin_verify_golden(oracle.tree_verify_ref) == 0
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
+def test_verify_bruteforce_all_small_trees_match_the_top_down_walk(n):
+    rng = np.random.default_rng(100 + n)
+    parents = [list(p) for p in all_parent_arrays(n)]
+    assert pins.pin_verify_walk(oracle.tree_verify_ref, parents, rng) == 0
+
+
+def test_verify_random_larger_trees_match_the_top_down_walk():
+    rng = np.random.default_rng(7)
+    parents = [[-1] + [int(rng.integers(-1, i)) for i in range(1, n)] for n in (16, 33, 64) for _ in range(20)]
+    assert pins.pin_verify_walk(oracle.tree_verify_ref, parents, rng, vocab=4, draws=2) == 0
+
+
+def test_verify_chain_accepts_exactly_the_agreeing_prefix():
+    assert pins.pin_verify_chain(oracle.tree_verify_ref, np.random.default_rng(8)) == 0
+
+
+def test_row_argmax_is_the_first_maximum_and_ignores_the_sign_of_zero():
+    x = np.array([[1, 3, 3, 0], [-np.inf] * 4, [-0.0, 0.0, -1, 0.0], [2, 1, 2, np.inf]], dtype=np.float32)
+    assert list(oracle.row_argmax(x)) == [1, 0, 0, 3]
+    bf = np.array([[0x3F80, 0x4000, 0x4000]], dtype=np.uint16)  # bf16 words 1, 2, 2
+    assert list(oracle.row_argmax((bf.astype(np.uint32) << 16).view(np.float32))) == [1]
+
+
+def test_verify_rejects_malformed_inputs():
+    with pytest.raises(ValueError):
+        oracle.tree_verify_ref(np.zeros((2, 4)), [0, 0], [-1, 0])  # one row short
+    with pytest.raises(ValueError):
+        oracle.tree_verify_ref(np.zeros((3, 4)), [0], [-1, 0])  # one token short
+    with pytest.raises(ValueError):
+        oracle.tree_verify_ref(np.zeros((3, 4)), [0, 0], [-1, 1])  # parent not before the node
