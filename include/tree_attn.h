@@ -1,13 +1,15 @@
 /*
  * tree_attn.h — C ABI of the MI355X (gfx950) tree-attention library.
  *
- * Two device operations sit behind this header:
+ * Three device operations sit behind this header:
  *
- *   ta_tree_attn  tree-masked attention of a token tree against a KV cache
- *                 laid out as [verified prefix | tree tokens];
- *   ta_kv_reroot  re-root of that cache after verification: the accepted
- *                 path joins the prefix and the surviving subtree is packed
- *                 contiguously right after it.
+ *   ta_tree_attn    tree-masked attention of a token tree against a KV cache
+ *                   laid out as [verified prefix | tree tokens];
+ *   ta_tree_verify  greedy verification of the tree against the target's
+ *                   logits: the accepted path and the bonus token;
+ *   ta_kv_reroot    re-root of that cache after verification: the accepted
+ *                   path joins the prefix and the surviving subtree is packed
+ *                   contiguously right after it.
  *
  * Source: SwiftSpec (arXiv 2506.11309), Pith review page, sections
  * "What carries the argument" (prefix/tree cache invariant, re-root at the
@@ -157,7 +159,47 @@ ta_status ta_kv_reroot(const ta_kv_cache* cache, int32_t prefix_len,
                        int32_t* new_parent, int32_t* new_prefix_len, void* stream);
 
 /*
- * Host-only planning steps of the two calls above (no device work; usable
+ * Greedy verification of a draft tree (temperature-0 acceptance). Source:
+ * SwiftSpec, Pith review page, "What carries the argument" and the referee
+ * report's summary (the target checks the draft tree, the verified tokens
+ * join the prefix, the tree re-roots at the last verified token), with
+ * tree-based verification as in SpecInfer (the page's reference list): the
+ * target scores the virtual root and every tree node in one pass.
+ *
+ *   choice[r] = arg-max of logits row r (the lowest token id among equal
+ *               maxima; -0.0 and +0.0 are equal). Row 0 is the target at the
+ *               last verified token, row 1 + i at tree node i.
+ *   node i matches when tokens[i] == choice[parent[i] + 1]; it is accepted
+ *   when it and every ancestor match. The accepted path a_0 .. a_{m-1} is the
+ *   root path of the deepest accepted node (the lowest index among equally
+ *   deep ones); m = 0 when no first-level node matches. The bonus token is
+ *   choice[a_{m-1} + 1] (choice[0] when m = 0).
+ *
+ *  logits      device, n_tree + 1 rows of `vocab` values of `dtype` (TA_F32 or
+ *              TA_BF16), row r at logits + r * row_stride elements; 16-byte
+ *              aligned, row_stride >= vocab, row_stride * element size a
+ *              multiple of 16; 1 <= vocab < 2^31. NaN values are undefined.
+ *  tokens      device, n_tree int32: the drafted token of each node (may be
+ *              NULL when n_tree == 0). Any values; they are only compared.
+ *  parent      host, as for ta_tree_attn; 0 <= n_tree <= TA_MAX_TREE.
+ *  choice_out  device, n_tree + 1 int32.
+ *  result_out  device, n_tree + 2 int32: [m, bonus, a_0 .. a_{m-1}, then -1
+ *              up to the end].
+ *  workspace   device, >= ta_tree_verify_workspace_bytes(n_tree) bytes,
+ *              256-byte aligned; zero-filled once before its first use, and
+ *              every completed call leaves it zero again. Not shared with a
+ *              call that can run at the same time (nor with ta_tree_attn).
+ * One launch on `stream`; nothing is synchronised: the outputs are valid
+ * once the stream reaches that point.
+ */
+size_t ta_tree_verify_workspace_bytes(int32_t n_tree);
+ta_status ta_tree_verify(const void* logits, int32_t dtype, int64_t vocab, int64_t row_stride,
+                         const int32_t* tokens, const int32_t* parent, int32_t n_tree,
+                         int32_t* choice_out, int32_t* result_out, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/*
+ * Host-only planning steps of ta_tree_attn and ta_kv_reroot (no device work; usable
  * without a GPU).
  *
  * ta_tree_ancestor_bits: bits_out[i] has bit j set iff node j is i itself or

@@ -191,3 +191,40 @@ def test_package_does_not_import_the_oracle():
             if f.endswith((".py", ".cpp", ".hip", ".h")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text
+
+
+def _verify_call(logits=FAKE, dtype=ta.TA_BF16, vocab=1000, stride=1000, tokens=FAKE, parent=(-1, 0),
+                 choice=FAKE, result=FAKE, ws=FAKE, ws_len=4096):
+    par, n = ta._i32(parent)
+    return ta.lib().ta_tree_verify(logits, dtype, vocab, stride, tokens, par, n, choice, result, ws, ws_len, None)
+
+
+@pytest.mark.parametrize("kwargs, status", [
+    (dict(dtype=7), ta.TA_ERR_UNSUPPORTED),
+    (dict(vocab=0, stride=8), ta.TA_ERR_ARG),
+    (dict(vocab=1 << 31, stride=1 << 31), ta.TA_ERR_ARG),
+    (dict(stride=999), ta.TA_ERR_ARG),
+    (dict(vocab=1001, stride=1001), ta.TA_ERR_ARG),  # rows not 16-byte aligned in bf16
+    (dict(dtype=ta.TA_F32, vocab=1002, stride=1002), ta.TA_ERR_ARG),
+    (dict(logits=None), ta.TA_ERR_ARG),
+    (dict(tokens=None), ta.TA_ERR_ARG),
+    (dict(choice=None), ta.TA_ERR_ARG),
+    (dict(result=None), ta.TA_ERR_ARG),
+    (dict(logits=FAKE + 8), ta.TA_ERR_ARG),
+    (dict(result=FAKE + 2), ta.TA_ERR_ARG),
+    (dict(ws=None), ta.TA_ERR_ARG),
+    (dict(ws_len=16), ta.TA_ERR_ARG),
+    (dict(ws=FAKE + 16), ta.TA_ERR_ARG),
+    (dict(parent=(0,)), ta.TA_ERR_TREE),
+    (dict(parent=(-1,) * 65), ta.TA_ERR_UNSUPPORTED),
+])
+def test_tree_verify_rejects_before_enqueueing(kwargs, status):
+    assert _verify_call(**kwargs) == status
+    assert ta.lib().ta_last_error()
+
+
+def test_tree_verify_workspace_bytes():
+    L = ta.lib()
+    sizes = {L.ta_tree_verify_workspace_bytes(n) for n in range(65)}
+    assert len(sizes) == 1 and 0 < sizes.pop() <= 4096
+    assert L.ta_tree_verify_workspace_bytes(65) == 0 and L.ta_tree_verify_workspace_bytes(-1) == 0

@@ -6,6 +6,7 @@ memory and for the current HIP stream. There is no CPU fallback: if the
 library has not been built, importing works but every call raises.
 
     tree_attn(q, k_cache, v_cache, prefix_len, parent, layer=0, out=None)
+    tree_verify(logits, tokens, parent) -> (choice, result) device tensors
     kv_reroot(k_cache, v_cache, prefix_len, parent, accepted_path, surviving_nodes)
     tree_attn_workspace_bytes / tree_attn_num_splits / tree_ancestor_bits / kv_reroot_plan
 
@@ -85,6 +86,12 @@ def lib():
             L.ta_kv_reroot.restype = ctypes.c_int
             L.ta_kv_reroot.argtypes = [_CP, ctypes.c_int32, _I32P, ctypes.c_int32, _I32P, ctypes.c_int32,
                                        _I32P, ctypes.c_int32, _I32P, _I32P, ctypes.c_void_p]
+            L.ta_tree_verify_workspace_bytes.restype = ctypes.c_size_t
+            L.ta_tree_verify_workspace_bytes.argtypes = [ctypes.c_int32]
+            L.ta_tree_verify.restype = ctypes.c_int
+            L.ta_tree_verify.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
+                                         ctypes.c_void_p, _I32P, ctypes.c_int32, ctypes.c_void_p,
+                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
             L.ta_set_split_wait_limit.restype = None
             L.ta_set_split_wait_limit.argtypes = [ctypes.c_int32]
             L.ta_tree_ancestor_bits.restype = ctypes.c_int
@@ -145,20 +152,21 @@ _workspaces = {}
 _ws_lock = threading.Lock()
 
 
-def _workspace(device, nbytes):
-    """A zero-filled workspace per device, grown on demand and kept for reuse.
+def _workspace(device, nbytes, kind="attn"):
+    """A zero-filled workspace per device and kind, grown on demand and kept
+    for reuse.
 
     Every call leaves the counters ready for the next (arrival counts back at
     zero), so reuse needs no clearing; it does assume calls on one device are
-    ordered (one stream).
+    ordered (one stream). Attention and verification keep separate ones.
     """
     if nbytes == 0:
         return None
-    key = torch.device(device).index
+    key = (kind, torch.device(device).index)
     with _ws_lock:
         ws = _workspaces.get(key)
         if ws is None or ws.numel() < nbytes:
-            ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+            ws = torch.zeros(max(nbytes, 1 << 20 if kind == "attn" else 4096), dtype=torch.uint8, device=device)
             _workspaces[key] = ws
     return ws
 
@@ -206,6 +214,52 @@ def tree_attn(q, k_cache, v_cache, prefix_len, parent, layer=0, out=None, worksp
         _check(lib().ta_tree_attn_rows(q.data_ptr(), ctypes.byref(desc), layer, prefix_len, par, n, q_first,
                                        q.shape[1], out.data_ptr(), ws_ptr, ws_len, _stream_ptr(q.device)))
     return out
+
+
+def tree_verify(logits, tokens, parent, choice=None, result=None, workspace=None):
+    """Greedy verification of a draft tree; returns ``(choice, result)``.
+
+    ``logits`` is a GPU tensor ``[n_tree + 1, vocab]`` (float32 or bfloat16;
+    rows may be strided, elements contiguous): row 0 is the target at the
+    last verified token, row ``1 + i`` at tree node ``i``. ``tokens`` is an
+    int32 GPU tensor ``[n_tree]`` of drafted tokens; ``parent`` a host
+    sequence. ``choice`` ``[n_tree + 1]`` receives each row's arg-max and
+    ``result`` ``[n_tree + 2]`` receives ``[m, bonus, path..., -1...]``
+    (both int32 on the GPU, allocated if None). Enqueued on torch's current
+    stream; nothing is synchronised (``accepted`` reads the result back).
+    """
+    if logits.dim() != 2 or not logits.is_cuda or logits.stride(1) != 1:
+        raise ValueError("logits must be a [n_tree + 1, vocab] GPU tensor with contiguous rows")
+    par, n = _i32(parent)
+    if logits.shape[0] != n + 1:
+        raise ValueError("logits must have one row for the root and one per tree node")
+    if tokens.dtype != torch.int32 or tokens.shape != (n,) or not tokens.is_contiguous() or \
+            tokens.device != logits.device:
+        raise ValueError("tokens must be a contiguous int32 tensor [n_tree] on the logits' device")
+    dev = logits.device
+    if choice is None:
+        choice = torch.empty(n + 1, dtype=torch.int32, device=dev)
+    if result is None:
+        result = torch.empty(n + 2, dtype=torch.int32, device=dev)
+    for name, t, size in (("choice", choice, n + 1), ("result", result, n + 2)):
+        if t.dtype != torch.int32 or t.shape != (size,) or not t.is_contiguous() or t.device != dev:
+            raise ValueError(f"{name} must be a contiguous int32 tensor [{size}] on the logits' device")
+    nbytes = lib().ta_tree_verify_workspace_bytes(n)
+    if nbytes == 0:
+        _check(TA_ERR_UNSUPPORTED)
+    if workspace is None:
+        workspace = _workspace(dev, nbytes, kind="verify")
+    ws_len = workspace.numel() * workspace.element_size()
+    _check(lib().ta_tree_verify(logits.data_ptr(), _dtype_code(logits), logits.shape[1], logits.stride(0),
+                                tokens.data_ptr() if n else None, par, n, choice.data_ptr(), result.data_ptr(),
+                                workspace.data_ptr(), ws_len, _stream_ptr(dev)))
+    return choice, result
+
+
+def accepted(result):
+    """``(path, bonus)`` from a ``tree_verify`` result (copies it to the host)."""
+    r = result.cpu().tolist()
+    return r[2:2 + r[0]], r[1]
 
 
 def kv_reroot(k_cache, v_cache, prefix_len, parent, accepted_path, surviving_nodes):

@@ -7,6 +7,7 @@
 
 #include <atomic>
 #include <cmath>
+#include <cstdint>
 #include <cstring>
 #include <string>
 
@@ -24,6 +25,10 @@ std::atomic<int32_t> g_wait_polls{20000};
 // floor(2^32 / d) + 1 (0 for d = 1): the kernels divide x < 2^17 by d < 2^15
 // as the high word of x times this (the product overshoots x / d by less
 // than 2^-15 < 1 / d, so its integer part is the quotient).
+// Verification workspace: the arrival count at offset 0, one 8-byte slot
+// per logits row from offset 256.
+constexpr size_t kVerifyWsBytes = 256 + kMaxVerifyRows * 8;
+
 uint32_t div_rcp(int32_t d) {
   return d <= 1 ? 0u : static_cast<uint32_t>((uint64_t{1} << 32) / static_cast<uint64_t>(d) + 1);
 }
@@ -160,6 +165,57 @@ ta_status ta_tree_attn_rows(const void* q, const ta_kv_cache* cache, int32_t lay
   a.split_extra = plan.n_tiles % plan.splits;
   hipError_t e = launch_tree_attn(a, cache->dtype, cache->head_dim, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return device_error(e, "tree_attn launch");
+  return TA_OK;
+}
+
+size_t ta_tree_verify_workspace_bytes(int32_t n_tree) {
+  clear_error();
+  if (n_tree < 0 || n_tree > TA_MAX_TREE) {
+    fail(TA_ERR_UNSUPPORTED, "n_tree must be in [0, " + std::to_string(TA_MAX_TREE) + "]");
+    return 0;
+  }
+  return kVerifyWsBytes;
+}
+
+ta_status ta_tree_verify(const void* logits, int32_t dtype, int64_t vocab, int64_t row_stride,
+                         const int32_t* tokens, const int32_t* parent, int32_t n_tree,
+                         int32_t* choice_out, int32_t* result_out, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  clear_error();
+  VerifyArgs a;
+  std::memset(&a, 0, sizeof(a));
+  ta_status st = ancestor_bits(parent, n_tree, a.anc);
+  if (st != TA_OK) return st;
+  const size_t es = dtype_bytes(dtype);
+  if (es == 0) return fail(TA_ERR_UNSUPPORTED, "dtype must be TA_F32 or TA_BF16");
+  if (vocab < 1 || vocab > INT32_MAX) return fail(TA_ERR_ARG, "vocab must be in [1, 2^31)");
+  if (row_stride < vocab) return fail(TA_ERR_ARG, "row_stride is smaller than vocab");
+  if ((static_cast<uint64_t>(row_stride) * es) % 16 != 0)
+    return fail(TA_ERR_ARG, "row_stride * element size must be a multiple of 16 bytes");
+  if (logits == nullptr || choice_out == nullptr || result_out == nullptr || (n_tree > 0 && tokens == nullptr))
+    return fail(TA_ERR_ARG, "logits, tokens, choice_out or result_out is null");
+  if (reinterpret_cast<uintptr_t>(logits) & 15) return fail(TA_ERR_ARG, "logits must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(tokens) | reinterpret_cast<uintptr_t>(choice_out) |
+       reinterpret_cast<uintptr_t>(result_out)) & 3)
+    return fail(TA_ERR_ARG, "tokens, choice_out and result_out must be 4-byte aligned");
+  if (workspace == nullptr || workspace_bytes < kVerifyWsBytes)
+    return fail(TA_ERR_ARG, "workspace too small: need " + std::to_string(kVerifyWsBytes) + " bytes, got " +
+                                std::to_string(workspace_bytes));
+  if (reinterpret_cast<uintptr_t>(workspace) & 255) return fail(TA_ERR_ARG, "workspace must be 256-byte aligned");
+  for (int32_t i = 0; i < n_tree; ++i) a.parent[i] = static_cast<int8_t>(parent[i]);
+  char* ws = static_cast<char*>(workspace);
+  a.logits = logits;
+  a.row_stride = row_stride;
+  a.vocab = vocab;
+  a.rows = n_tree + 1;
+  a.n_tree = n_tree;
+  a.tokens = tokens;
+  a.choice = choice_out;
+  a.result = result_out;
+  a.count = reinterpret_cast<unsigned*>(ws);
+  a.keys = reinterpret_cast<unsigned long long*>(ws + 256);
+  hipError_t e = launch_tree_verify(a, dtype, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_error(e, "tree_verify launch");
   return TA_OK;
 }
 

@@ -59,4 +59,24 @@ struct RerootArgs {
 
 hipError_t launch_kv_reroot(const RerootArgs& a, hipStream_t stream);
 
+// Rows of one verification: the virtual root and up to 64 tree nodes.
+constexpr int kMaxVerifyRows = 65;
+
+struct VerifyArgs {
+  const void* logits;       // rows of the target's logits, row_stride elements apart
+  int64_t row_stride;       // elements; row_stride * element size is a multiple of 16
+  int64_t vocab;            // values per row, < 2^31
+  int32_t rows;             // n_tree + 1
+  int32_t n_tree;
+  const int32_t* tokens;    // [n_tree] drafted token per node
+  int32_t* choice;          // [rows] arg-max per row
+  int32_t* result;          // [n_tree + 2]: m, bonus, accepted path, -1 padding
+  unsigned long long* keys; // [rows] workspace slots (zero between calls)
+  unsigned* count;          // workspace arrival count (zero between calls)
+  uint64_t anc[64];         // ancestor-or-self bitset per tree node
+  int8_t parent[64];
+};
+
+hipError_t launch_tree_verify(const VerifyArgs& a, int32_t dtype, hipStream_t stream);
+
 }  // namespace ta

@@ -1,0 +1,211 @@
+// Greedy tree verification for gfx950: per-row arg-max of the target's
+// logits and the accepted path of the draft tree, in one launch.
+//
+// SwiftSpec (arXiv 2506.11309), Pith review page, "What carries the argument"
+// and the referee report's summary: the target model checks the draft tree as
+// a whole, the verified tokens join the prefix and the tree re-roots at the
+// last verified token. As in tree-based verification (SpecInfer, in the same
+// page's reference list), the target scores every tree node in one pass; its
+// logits row 0 belongs to the virtual root (the last verified token) and row
+// 1 + i to tree node i. Under greedy decoding node i is accepted when its
+// drafted token is the target's arg-max at its parent and every ancestor was
+// accepted; the deepest accepted node (lowest index among equally deep ones)
+// ends the accepted path, and the target's arg-max there is the bonus token.
+//
+// Work split. Reading the logits is the whole cost (HBM-bound: every byte is
+// read once), so the grid is (vocab chunk, row): each workgroup streams one
+// chunk of one row with 16-byte loads, reduces it to one 64-bit key and
+// folds the key into its row's slot with a device-scope atomic max. The key
+// orders candidates by value, then by lowest index, so the maximum key is the
+// row's first maximum whatever order the workgroups finish in. A wrapping
+// arrival count picks the last workgroup, which reads and clears every slot
+// (atomic exchange with zero), writes the arg-max of each row and finds the
+// accepted path with one wave: a ballot of the matching nodes, then each
+// node's ancestor bitset tells whether its whole root path matched.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <type_traits>
+
+#include "launch.h"
+#include "tree_attn.h"
+
+namespace ta {
+namespace {
+
+constexpr int kThreads = 256;
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned long long u64;
+
+// Orderable image of a float: larger float, larger key (-0.0 taken as +0.0,
+// so the two compare equal as they do as floats).
+__device__ __forceinline__ uint32_t order_key(float x) {
+  uint32_t u = __float_as_uint(x);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Key of candidate (x, index): value first, then the lower index. Zero is
+// below every candidate's key (the lowest value key, that of -inf, is
+// 0x007fffff), so zero-filled slots are the identity of the max.
+__device__ __forceinline__ u64 cand_key(float x, uint32_t idx) {
+  return (static_cast<u64>(order_key(x)) << 32) | static_cast<u64>(0xffffffffu - idx);
+}
+
+__device__ __forceinline__ u64 wave_max(u64 k) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const u64 o = __shfl_xor(k, m, 64);
+    k = o > k ? o : k;
+  }
+  return k;
+}
+
+template <typename T>
+__device__ __forceinline__ float to_float(T x) {
+  if constexpr (std::is_same_v<T, float>)
+    return x;
+  else
+    return __uint_as_float(static_cast<uint32_t>(__builtin_bit_cast(uint16_t, x)) << 16);
+}
+
+// Vectors of 16 bytes per thread and chunk: UNR loads in flight per thread.
+constexpr int kUnroll = 8;
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void tree_verify_kernel(const VerifyArgs a) {
+  constexpr int EPV = 16 / sizeof(T);  // elements per 16-byte vector
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int row = blockIdx.y;
+  const T* x = static_cast<const T*>(a.logits) + static_cast<size_t>(row) * a.row_stride;
+  const int64_t full_vecs = a.vocab / EPV;  // whole vectors; the rest is the tail
+  const int64_t v0 = static_cast<int64_t>(blockIdx.x) * kThreads * kUnroll + tid;
+
+  // Each thread scans its elements in ascending index order and keeps the
+  // first maximum; it starts from its first element's index with -inf, which
+  // is right also when all of its elements are -inf.
+  float best = -__builtin_huge_valf();
+  uint32_t bidx = 0;
+  bool any = false;
+  u32x4 buf[kUnroll];
+#pragma unroll
+  for (int j = 0; j < kUnroll; ++j) {
+    const int64_t vi = v0 + j * kThreads;
+    if (vi < full_vecs) buf[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x) + vi);
+  }
+#pragma unroll
+  for (int j = 0; j < kUnroll; ++j) {
+    const int64_t vi = v0 + j * kThreads;
+    if (vi < full_vecs) {
+      if (!any) {
+        any = true;
+        bidx = static_cast<uint32_t>(vi * EPV);
+      }
+      const T* e = reinterpret_cast<const T*>(&buf[j]);
+#pragma unroll
+      for (int t = 0; t < EPV; ++t) {
+        const float f = to_float(e[t]);
+        if (f > best) {
+          best = f;
+          bidx = static_cast<uint32_t>(vi * EPV + t);
+        }
+      }
+    }
+  }
+  // Tail (vocab not a multiple of EPV): the thread that would own vector
+  // full_vecs reads the remaining elements one by one.
+  for (int j = 0; j < kUnroll; ++j) {
+    if (v0 + j * kThreads == full_vecs) {
+      for (int64_t i = full_vecs * EPV; i < a.vocab; ++i) {
+        const float f = to_float(x[i]);
+        if (!any) {
+          any = true;
+          bidx = static_cast<uint32_t>(i);
+        }
+        if (f > best) {
+          best = f;
+          bidx = static_cast<uint32_t>(i);
+        }
+      }
+    }
+  }
+
+  __shared__ u64 s_key[kThreads / 64];
+  __shared__ int s_last;
+  __shared__ int s_choice[kMaxVerifyRows];
+  u64 key = wave_max(any ? cand_key(best, bidx) : 0ull);
+  if (lane == 0) s_key[wave] = key;
+  __syncthreads();
+  if (tid == 0) {
+    key = s_key[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) key = s_key[w] > key ? s_key[w] : key;
+    // Wait for the returning atomic before counting in: the count then
+    // announces a max that is already performed at the device coherence
+    // point, where the last workgroup's exchange reads it.
+    const u64 old = __hip_atomic_fetch_max(a.keys + row, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("" ::"v"(old) : "memory");
+    __builtin_amdgcn_s_waitcnt(0);
+    const unsigned total = gridDim.x * gridDim.y;
+    const unsigned arrived = __builtin_amdgcn_atomic_inc32(a.count, total - 1, __ATOMIC_RELAXED, "agent");
+    s_last = arrived == total - 1;  // the count has wrapped back to zero
+  }
+  __syncthreads();
+  if (!s_last) return;
+
+  // Last workgroup: collect (and clear) every row's key.
+  for (int r = tid; r < a.rows; r += kThreads) {
+    const u64 k = __hip_atomic_exchange(a.keys + r, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int c = static_cast<int>(0xffffffffu - static_cast<uint32_t>(k));
+    s_choice[r] = c;
+    a.choice[r] = c;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  const int n = a.n_tree;
+  const bool live = lane < n;
+  const u64 anc = live ? a.anc[lane] : 0ull;
+  const bool match = live && a.tokens[lane] == s_choice[a.parent[lane] + 1];
+  const u64 matched = __ballot(match);
+  const bool accepted = live && (anc & ~matched) == 0ull;
+  // deepest accepted node, lowest index among equally deep ones
+  int best_node = accepted ? (__popcll(anc) << 8) | (255 - lane) : 0;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) best_node = max(best_node, __shfl_xor(best_node, m, 64));
+  const int depth = best_node >> 8;
+  const int last = depth > 0 ? 255 - (best_node & 255) : -1;
+  const u64 path_bits = last >= 0 ? a.anc[last] : 0ull;
+  // result = [m, bonus, path (root to leaf), -1 ...]: node j on the path goes
+  // to position 2 + (number of path nodes below j); ancestors have lower
+  // indices, so that is root-to-leaf order.
+  if (lane == 0) {
+    a.result[0] = depth;
+    a.result[1] = s_choice[last + 1];
+  }
+  if (live) {
+    const bool on_path = (path_bits >> lane) & 1ull;
+    const int below = __popcll(path_bits & ((1ull << lane) - 1ull));
+    if (on_path) a.result[2 + below] = lane;
+    // positions depth .. n-1 hold -1
+    if (lane >= depth) a.result[2 + lane] = -1;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_tree_verify(const VerifyArgs& a, int32_t dtype, hipStream_t stream) {
+  if (a.rows < 1 || a.rows > kMaxVerifyRows || a.vocab < 1) return hipErrorInvalidValue;
+  const int64_t epv = dtype == TA_F32 ? 4 : 8;
+  const int64_t vecs = (a.vocab + epv - 1) / epv;
+  const int64_t per_block = static_cast<int64_t>(kThreads) * kUnroll;
+  const dim3 grid(static_cast<unsigned>((vecs + per_block - 1) / per_block), static_cast<unsigned>(a.rows));
+  if (dtype == TA_F32)
+    hipLaunchKernelGGL(tree_verify_kernel<float>, grid, dim3(kThreads), 0, stream, a);
+  else if (dtype == TA_BF16)
+    hipLaunchKernelGGL(tree_verify_kernel<__bf16>, grid, dim3(kThreads), 0, stream, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace ta

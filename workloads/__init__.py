@@ -24,30 +24,33 @@ import torch
 # name -> shape/seed recipe. capacity defaults to prefix + 256.
 CONFIGS = {
     "tiny_fp32": dict(n_q_heads=2, n_kv_heads=1, head_dim=64, dtype="f32", prefix=128,
-                      n_tree=15, capacity=256, seed=0, value_scale=1.0, tree="random"),
+                      n_tree=15, capacity=256, seed=0, value_scale=1.0, tree="random", vocab=1000),
     "llama3_8b_verify": dict(n_q_heads=32, n_kv_heads=8, head_dim=128, dtype="bf16",
                              prefix=2048, n_tree=64, capacity=2048 + 256, seed=1,
-                             value_scale=1.0 / math.sqrt(128), tree="top8"),
+                             value_scale=1.0 / math.sqrt(128), tree="top8", vocab=128256),
     "llama3_70b_verify": dict(n_q_heads=64, n_kv_heads=8, head_dim=128, dtype="bf16",
                               prefix=8192, n_tree=64, capacity=8192 + 256, seed=2,
-                              value_scale=1.0 / math.sqrt(128), tree="top8"),
+                              value_scale=1.0 / math.sqrt(128), tree="top8", vocab=128256),
     "qwen2_72b_32k_verify": dict(n_q_heads=64, n_kv_heads=8, head_dim=128, dtype="bf16",
                                  prefix=32768, n_tree=64, capacity=32768 + 256, seed=3,
-                                 value_scale=1.0 / math.sqrt(128), tree="top8"),
+                                 value_scale=1.0 / math.sqrt(128), tree="top8", vocab=152064),
     "draft_loop_1b": dict(n_q_heads=32, n_kv_heads=8, head_dim=64, dtype="bf16",
                           prefix=4096, n_tree=64, capacity=8192, seed=4,
-                          value_scale=1.0 / 8.0, tree="top8", iterations=100),
+                          value_scale=1.0 / 8.0, tree="top8", iterations=100, vocab=128256),
     # The pages' operating point: a verify tree of bs = 8 nodes at 70B shapes
     # (the 8 most likely nodes of the width-8 expansion; HBM-bound).
     "llama3_70b_verify_bs8": dict(n_q_heads=64, n_kv_heads=8, head_dim=128, dtype="bf16",
                                   prefix=8192, n_tree=8, capacity=8192 + 256, seed=5,
-                                  value_scale=1.0 / math.sqrt(128), tree="top8_bs8"),
+                                  value_scale=1.0 / math.sqrt(128), tree="top8_bs8", vocab=128256),
     # A draft-expansion step: only the w = 8 newest leaves of the 64-node tree
     # are queries, against the whole [prefix | tree].
     "draft_expand_w8": dict(n_q_heads=32, n_kv_heads=8, head_dim=64, dtype="bf16",
                             prefix=4096, n_tree=64, q_first=56, capacity=4096 + 256, seed=6,
-                            value_scale=1.0 / 8.0, tree="top8"),
+                            value_scale=1.0 / 8.0, tree="top8", vocab=128256),
 }
+
+# vocab: the model family's vocabulary (Llama 3: 128256 token ids, Qwen2:
+# 152064), the row length of the target's logits in tree verification.
 
 TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
 
@@ -315,3 +318,35 @@ class DraftLoop:
         shape = (n_layers, c["n_kv_heads"], add, c["head_dim"])
         return keep, _draw(self.rng, shape, c["value_scale"], c["dtype"]), \
             _draw(self.rng, shape, c["value_scale"], c["dtype"])
+
+
+def make_verify_inputs(cfg, parent, rng=None, accept=0.8, logit_scale=2.0):
+    """Target logits and drafted tokens for verifying the tree ``parent``.
+
+    Rows (root, then one per node) are N(0, 1) * ``logit_scale`` with one
+    planted maximum per row (its row maximum + 1, at a uniform token id);
+    below each row's owner (the virtual root, or node ``j`` for row ``1 + j``)
+    one uniformly chosen child drafts the planted token with probability
+    ``accept``, every other child drafts a different uniform token. So the
+    accepted depth follows ``accept`` the way a draft model's agreement with
+    the target would. Returns ``logits`` (torch, cfg dtype, CPU) and
+    ``tokens`` (torch int32, CPU).
+    """
+    rng = np.random.default_rng(cfg["seed"] + 1000) if rng is None else rng
+    n, vocab = len(parent), cfg["vocab"]
+    x = rng.standard_normal((n + 1, vocab), dtype=np.float32) * np.float32(logit_scale)
+    planted = rng.integers(0, vocab, size=n + 1)
+    x[np.arange(n + 1), planted] = x.max(axis=1) + np.float32(1.0)
+    kids = children(parent)
+    roots = [i for i in range(n) if parent[i] < 0]
+    tokens = np.empty(n, dtype=np.int32)
+    for owner in [-1] + list(range(n)):
+        c = roots if owner < 0 else kids[owner]
+        if not c:
+            continue
+        want = int(planted[owner + 1])
+        hit = int(rng.integers(0, len(c))) if rng.random() < accept else -1
+        for k, node in enumerate(c):
+            t = int(rng.integers(0, max(vocab - 1, 1)))
+            tokens[node] = want if k == hit else (t if t < want else t + 1)
+    return dict(logits=torch.from_numpy(x).to(TORCH_DTYPE[cfg["dtype"]]), tokens=torch.from_numpy(tokens))
