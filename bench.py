@@ -6,6 +6,12 @@ surviving subtree), i.e. the whole path once. The default workload is the
 Llama-3-70B-shaped verify: 64 query / 8 KV heads, head_dim 128, bf16, prefix
 8192, a 64-node width-8 tree; synthetic seeded inputs.
 
+Labelled extras, outside the step: ``tree_verify`` (greedy verification of the
+same tree against the target's logits over the model's vocabulary) and
+``kv_reroot_all_layers`` (one re-root call over a cache with all of the
+model's layers: the draft side with its survivors, and the target side with
+the accepted rows only).
+
 Timing: inputs are resident in HBM before the timed region. ``--rotate`` input
 sets are cycled so that the working set exceeds twice the 256 MB Infinity
 Cache (each set is one layer's K/V, as in a real step where the other layers
@@ -90,6 +96,13 @@ def reroot_bytes(cfg, src_rows, prefix, n_layers=1):
     es = 4 if cfg["dtype"] == "f32" else 2
     moved = sum(1 for k, s in enumerate(src_rows) if s != prefix + k)
     return 2 * moved * 2 * cfg["n_kv_heads"] * cfg["head_dim"] * es * n_layers
+
+
+def verify_bytes(cfg, n):
+    """Algorithmic bytes of one tree_verify: every logits value once, the
+    drafted tokens, the arg-max and result arrays."""
+    es = 4 if cfg["dtype"] == "f32" else 2
+    return (n + 1) * cfg["vocab"] * es + 4 * n + 4 * (n + 1) + 4 * (n + 2)
 
 
 def pct(xs, p):
@@ -373,6 +386,57 @@ def main():
     _, hot, _ = timed(lambda i: attn(0), 50, each=True)
     hot_us = statistics.median(hot)
 
+    # Verification of the same tree against the target's logits: rotated
+    # logits sets (positive rescales of one draw, so the same tokens apply)
+    # that together exceed twice the Infinity Cache.
+    n = cfg["n_tree"]
+    vx = W.make_verify_inputs(cfg, parent)
+    v_bytes = verify_bytes(cfg, n)
+    vrot = max(2, math.ceil(2 * MALL_BYTES / v_bytes) + 1)
+    v0 = vx["logits"].to(dev)
+    v_sets = [v0 * (1.0 + 1e-3 * r) if r else v0 for r in range(vrot)]
+    v_tok = vx["tokens"].to(dev)
+    v_choice = torch.empty(n + 1, dtype=torch.int32, device=dev)
+    v_result = torch.empty(n + 2, dtype=torch.int32, device=dev)
+    v_ws = torch.zeros(8192, dtype=torch.uint8, device=dev)
+
+    def verify(i):
+        ta.tree_verify(v_sets[i % vrot], v_tok, parent, choice=v_choice, result=v_result, workspace=v_ws)
+
+    for i in range(5):
+        verify(i)
+    _, ver_us, _ = timed(verify, K, each=True)
+    ver_b2b, _, _ = timed(verify, K)
+    v_accepted = ta.accepted(v_result)[0]
+    del v_sets, v0
+
+    # One re-root call over a cache with all of the model's layers. The
+    # prefix position rotates (P, P - n, ...) so that the rows touched by
+    # consecutive calls differ and together exceed twice the Infinity Cache.
+    n_layers = cfg.get("layers", 1)
+    big = (n_layers, cfg["n_kv_heads"], cfg["capacity"], cfg["head_dim"])
+    k_all = torch.zeros(big, dtype=base["k"].dtype, device=dev)
+    v_all = torch.zeros(big, dtype=base["k"].dtype, device=dev)
+    all_layers = {}
+    for side, s_surv in (("draft", surv), ("target", [])):
+        s_src, _, _ = ta.kv_reroot_plan(P, cfg["capacity"], parent, path, s_surv)
+        b = reroot_bytes(cfg, s_src, P, n_layers)
+        rrot = max(1, min(P // n, math.ceil(2 * MALL_BYTES / max(b, 1)) + 1))
+
+        def reroot_all(i, s_surv=s_surv, rrot=rrot):
+            ta.kv_reroot(k_all, v_all, P - (i % rrot) * n, parent, path, s_surv)
+
+        for i in range(3):
+            reroot_all(i)
+        _, ra_us, _ = timed(reroot_all, K, each=True)
+        ra_mean = statistics.fmean(ra_us)
+        all_layers[side] = {"survivors": len(s_surv), "us_mean": round(ra_mean, 2),
+                            "us_p50": round(pct(ra_us, 50), 2), "algorithmic_bytes": b,
+                            "GBs": round(b / (ra_mean * 1e-6) / 1e9, 1),
+                            "hbm_frac": round(b / (ra_mean * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                            "rotated_positions": rrot}
+    del k_all, v_all
+
     nbytes, flops, anc = tree_attn_work(cfg, parent)
     rr_bytes = reroot_bytes(cfg, src_rows, P)
     attn_mean = statistics.fmean(attn_us)
@@ -419,6 +483,13 @@ def main():
         "kv_reroot": {"us_mean": round(rr_mean, 2), "us_p50": round(pct(reroot_us, 50), 2),
                       "us_launch_period_back_to_back": round(rr_b2b / K, 2),
                       "algorithmic_bytes": rr_bytes, "GBs": round(rr_bytes / (rr_mean * 1e-6) / 1e9, 2)},
+        "tree_verify": {"vocab": cfg["vocab"], "rows": n + 1, "accepted_path": len(v_accepted),
+                        "us_mean": round(statistics.fmean(ver_us), 2), "us_p50": round(pct(ver_us, 50), 2),
+                        "us_launch_period_back_to_back": round(ver_b2b / K, 2), "algorithmic_bytes": v_bytes,
+                        "GBs": round(v_bytes / (statistics.fmean(ver_us) * 1e-6) / 1e9, 1),
+                        "hbm_frac": round(v_bytes / (statistics.fmean(ver_us) * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                        "rotated_sets": vrot},
+        "kv_reroot_all_layers": dict(layers=n_layers, accepted_path=len(path), **all_layers),
         "wall_s_timed_region": round(t_wall, 4),
         "kernel_source_sha": kernel_source_sha(),
         "roofline": roof,

@@ -244,6 +244,18 @@ def test_reroot_nothing_accepted_and_target_side():
     reroot_case(cfg, 1, rng, path, [], parent)  # target side: accepted rows only
 
 
+def test_reroot_all_80_layers_target_and_draft_side():
+    """One call moves every layer of a 70B-shaped cache (80 layers, 8 KV
+    heads, head_dim 128): the target side keeps the accepted rows only, the
+    draft side also its surviving subtree. Bit-exact over the whole cache."""
+    cfg = W.config("llama3_70b_verify", prefix=600, capacity=700)
+    rng = np.random.default_rng(80)
+    parent, _ = W.top8_tree(rng)
+    path = W.draft_path(rng, parent)
+    reroot_case(cfg, cfg["layers"], rng, path, [], parent)
+    reroot_case(cfg, cfg["layers"], rng, path, W.descendants(parent, path[-1]), parent)
+
+
 def test_reroot_then_attend_equals_attend_on_gpu():
     """The re-root invariant, measured on the GPU path itself."""
     cfg = W.config("draft_loop_1b")

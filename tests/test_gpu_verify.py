@@ -123,7 +123,7 @@ def test_ties_signed_zeros_and_infinities(dtype):
 def test_repeat_calls_reuse_the_workspace():
     """Calls of different shapes in a row on one workspace; each must match."""
     rng = np.random.default_rng(3)
-    ws = torch.zeros(4096, dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(8192, dtype=torch.uint8, device=DEV)
     for k, (n, vocab, dtype) in enumerate([(64, 128256, "bf16"), (3, 100, "f32"), (0, 80, "bf16"),
                                            (64, 152064, "bf16"), (17, 9000, "f32"), (64, 128256, "bf16")]):
         parent = _rand_parent(rng, n)

@@ -194,7 +194,7 @@ def test_package_does_not_import_the_oracle():
 
 
 def _verify_call(logits=FAKE, dtype=ta.TA_BF16, vocab=1000, stride=1000, tokens=FAKE, parent=(-1, 0),
-                 choice=FAKE, result=FAKE, ws=FAKE, ws_len=4096):
+                 choice=FAKE, result=FAKE, ws=FAKE, ws_len=8192):
     par, n = ta._i32(parent)
     return ta.lib().ta_tree_verify(logits, dtype, vocab, stride, tokens, par, n, choice, result, ws, ws_len, None)
 
@@ -226,5 +226,5 @@ def test_tree_verify_rejects_before_enqueueing(kwargs, status):
 def test_tree_verify_workspace_bytes():
     L = ta.lib()
     sizes = {L.ta_tree_verify_workspace_bytes(n) for n in range(65)}
-    assert len(sizes) == 1 and 0 < sizes.pop() <= 4096
+    assert len(sizes) == 1 and 0 < sizes.pop() <= 8192
     assert L.ta_tree_verify_workspace_bytes(65) == 0 and L.ta_tree_verify_workspace_bytes(-1) == 0

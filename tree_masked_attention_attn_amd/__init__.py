@@ -166,7 +166,7 @@ def _workspace(device, nbytes, kind="attn"):
     with _ws_lock:
         ws = _workspaces.get(key)
         if ws is None or ws.numel() < nbytes:
-            ws = torch.zeros(max(nbytes, 1 << 20 if kind == "attn" else 4096), dtype=torch.uint8, device=device)
+            ws = torch.zeros(max(nbytes, 1 << 20 if kind == "attn" else 8192), dtype=torch.uint8, device=device)
             _workspaces[key] = ws
     return ws
 

@@ -25,9 +25,9 @@ std::atomic<int32_t> g_wait_polls{20000};
 // floor(2^32 / d) + 1 (0 for d = 1): the kernels divide x < 2^17 by d < 2^15
 // as the high word of x times this (the product overshoots x / d by less
 // than 2^-15 < 1 / d, so its integer part is the quotient).
-// Verification workspace: the arrival count at offset 0, one 8-byte slot
-// per logits row from offset 256.
-constexpr size_t kVerifyWsBytes = 256 + kMaxVerifyRows * 8;
+// Verification workspace: the rows' arrival count, then one slot per
+// logits row (key and arrival count), kVerifySlot bytes each.
+constexpr size_t kVerifyWsBytes = kVerifySlot * (1 + kMaxVerifyRows);
 
 uint32_t div_rcp(int32_t d) {
   return d <= 1 ? 0u : static_cast<uint32_t>((uint64_t{1} << 32) / static_cast<uint64_t>(d) + 1);
@@ -212,8 +212,7 @@ ta_status ta_tree_verify(const void* logits, int32_t dtype, int64_t vocab, int64
   a.tokens = tokens;
   a.choice = choice_out;
   a.result = result_out;
-  a.count = reinterpret_cast<unsigned*>(ws);
-  a.keys = reinterpret_cast<unsigned long long*>(ws + 256);
+  a.ws = ws;
   hipError_t e = launch_tree_verify(a, dtype, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return device_error(e, "tree_verify launch");
   return TA_OK;

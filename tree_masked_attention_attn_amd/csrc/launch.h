@@ -61,6 +61,9 @@ hipError_t launch_kv_reroot(const RerootArgs& a, hipStream_t stream);
 
 // Rows of one verification: the virtual root and up to 64 tree nodes.
 constexpr int kMaxVerifyRows = 65;
+// Bytes per row slot of the verification workspace (one slot per cache line
+// pair, so that the rows' atomics do not share lines).
+constexpr int kVerifySlot = 64;
 
 struct VerifyArgs {
   const void* logits;       // rows of the target's logits, row_stride elements apart
@@ -71,8 +74,9 @@ struct VerifyArgs {
   const int32_t* tokens;    // [n_tree] drafted token per node
   int32_t* choice;          // [rows] arg-max per row
   int32_t* result;          // [n_tree + 2]: m, bonus, accepted path, -1 padding
-  unsigned long long* keys; // [rows] workspace slots (zero between calls)
-  unsigned* count;          // workspace arrival count (zero between calls)
+  char* ws;                 // workspace, zero between calls: the arrival count of
+                            // rows at 0, then per row r at kVerifySlot * (1 + r)
+                            // its 8-byte key and its 4-byte arrival count
   uint64_t anc[64];         // ancestor-or-self bitset per tree node
   int8_t parent[64];
 };

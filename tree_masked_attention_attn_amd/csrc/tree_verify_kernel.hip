@@ -17,11 +17,15 @@
 // chunk of one row with 16-byte loads, reduces it to one 64-bit key and
 // folds the key into its row's slot with a device-scope atomic max. The key
 // orders candidates by value, then by lowest index, so the maximum key is the
-// row's first maximum whatever order the workgroups finish in. A wrapping
-// arrival count picks the last workgroup, which reads and clears every slot
-// (atomic exchange with zero), writes the arg-max of each row and finds the
-// accepted path with one wave: a ballot of the matching nodes, then each
-// node's ancestor bitset tells whether its whole root path matched.
+// row's first maximum whatever order the workgroups finish in. Arrival is
+// counted in two levels of wrapping counts: the chunks of a row count in on
+// the row's slot, the last of them counts the row in on one shared count,
+// and the last row's last chunk goes on (one count per address takes a
+// row's chunks or the rows, never the whole grid: device-scope atomics on
+// one address serialise). That workgroup reads and clears every slot (atomic
+// exchange with zero), writes the arg-max of each row and finds the accepted
+// path with one wave: a ballot of the matching nodes, then each node's
+// ancestor bitset tells whether its whole root path matched.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -69,8 +73,11 @@ __device__ __forceinline__ float to_float(T x) {
     return __uint_as_float(static_cast<uint32_t>(__builtin_bit_cast(uint16_t, x)) << 16);
 }
 
-// Vectors of 16 bytes per thread and chunk: UNR loads in flight per thread.
-constexpr int kUnroll = 8;
+// Vectors of 16 bytes per thread and chunk (kUnroll loads in flight per
+// thread): 16 KB chunks, 8 of a 128256-entry bf16 row, ~1000 workgroups for
+// 65 rows. Measured faster than 32, 64 or 256 KB chunks: the latency chain
+// after the loads is fixed, so the loads should finish as early as possible.
+constexpr int kUnroll = 4;
 
 template <typename T>
 __global__ __launch_bounds__(kThreads) void tree_verify_kernel(const VerifyArgs a) {
@@ -80,6 +87,13 @@ __global__ __launch_bounds__(kThreads) void tree_verify_kernel(const VerifyArgs 
   const T* x = static_cast<const T*>(a.logits) + static_cast<size_t>(row) * a.row_stride;
   const int64_t full_vecs = a.vocab / EPV;  // whole vectors; the rest is the tail
   const int64_t v0 = static_cast<int64_t>(blockIdx.x) * kThreads * kUnroll + tid;
+  // Inputs of the path search, loaded early by every workgroup (only the
+  // last one uses them) so that their latency hides under the logits': the
+  // drafted token, ancestor bitset and parent of node `lane`.
+  const bool live = wave == 0 && lane < a.n_tree;
+  const int tok = live ? a.tokens[lane] : 0;
+  const u64 anc = live ? a.anc[lane] : 0ull;
+  const int par = live ? a.parent[lane] : 0;
 
   // Each thread scans its elements in ascending index order and keeps the
   // first maximum; it starts from its first element's index with -inf, which
@@ -142,30 +156,35 @@ __global__ __launch_bounds__(kThreads) void tree_verify_kernel(const VerifyArgs 
     for (int w = 1; w < kThreads / 64; ++w) key = s_key[w] > key ? s_key[w] : key;
     // Wait for the returning atomic before counting in: the count then
     // announces a max that is already performed at the device coherence
-    // point, where the last workgroup's exchange reads it.
-    const u64 old = __hip_atomic_fetch_max(a.keys + row, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // point, where the last workgroup's exchange reads it. Each count is
+    // taken only once the one before it has returned.
+    char* slot = a.ws + kVerifySlot * (1 + row);
+    const u64 old = __hip_atomic_fetch_max(reinterpret_cast<u64*>(slot), key, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
     asm volatile("" ::"v"(old) : "memory");
     __builtin_amdgcn_s_waitcnt(0);
-    const unsigned total = gridDim.x * gridDim.y;
-    const unsigned arrived = __builtin_amdgcn_atomic_inc32(a.count, total - 1, __ATOMIC_RELAXED, "agent");
-    s_last = arrived == total - 1;  // the count has wrapped back to zero
+    int last = 0;
+    const unsigned chunks = gridDim.x, rows = gridDim.y;
+    if (__builtin_amdgcn_atomic_inc32(reinterpret_cast<unsigned*>(slot + 8), chunks - 1, __ATOMIC_RELAXED,
+                                      "agent") == chunks - 1)  // this row is complete (its count wrapped)
+      last = __builtin_amdgcn_atomic_inc32(reinterpret_cast<unsigned*>(a.ws), rows - 1, __ATOMIC_RELAXED,
+                                           "agent") == rows - 1;
+    s_last = last;
   }
   __syncthreads();
   if (!s_last) return;
 
   // Last workgroup: collect (and clear) every row's key.
   for (int r = tid; r < a.rows; r += kThreads) {
-    const u64 k = __hip_atomic_exchange(a.keys + r, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const u64 k = __hip_atomic_exchange(reinterpret_cast<u64*>(a.ws + kVerifySlot * (1 + r)), 0ull,
+                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int c = static_cast<int>(0xffffffffu - static_cast<uint32_t>(k));
     s_choice[r] = c;
     a.choice[r] = c;
   }
   __syncthreads();
   if (wave != 0) return;
-  const int n = a.n_tree;
-  const bool live = lane < n;
-  const u64 anc = live ? a.anc[lane] : 0ull;
-  const bool match = live && a.tokens[lane] == s_choice[a.parent[lane] + 1];
+  const bool match = live && tok == s_choice[par + 1];
   const u64 matched = __ballot(match);
   const bool accepted = live && (anc & ~matched) == 0ull;
   // deepest accepted node, lowest index among equally deep ones
@@ -174,7 +193,7 @@ __global__ __launch_bounds__(kThreads) void tree_verify_kernel(const VerifyArgs 
   for (int m = 32; m >= 1; m >>= 1) best_node = max(best_node, __shfl_xor(best_node, m, 64));
   const int depth = best_node >> 8;
   const int last = depth > 0 ? 255 - (best_node & 255) : -1;
-  const u64 path_bits = last >= 0 ? a.anc[last] : 0ull;
+  const u64 path_bits = last >= 0 ? __shfl(anc, last, 64) : 0ull;
   // result = [m, bonus, path (root to leaf), -1 ...]: node j on the path goes
   // to position 2 + (number of path nodes below j); ancestors have lower
   // indices, so that is root-to-leaf order.

@@ -24,33 +24,36 @@ import torch
 # name -> shape/seed recipe. capacity defaults to prefix + 256.
 CONFIGS = {
     "tiny_fp32": dict(n_q_heads=2, n_kv_heads=1, head_dim=64, dtype="f32", prefix=128,
-                      n_tree=15, capacity=256, seed=0, value_scale=1.0, tree="random", vocab=1000),
+                      n_tree=15, capacity=256, seed=0, value_scale=1.0, tree="random", vocab=1000, layers=2),
     "llama3_8b_verify": dict(n_q_heads=32, n_kv_heads=8, head_dim=128, dtype="bf16",
                              prefix=2048, n_tree=64, capacity=2048 + 256, seed=1,
-                             value_scale=1.0 / math.sqrt(128), tree="top8", vocab=128256),
+                             value_scale=1.0 / math.sqrt(128), tree="top8", vocab=128256, layers=32),
     "llama3_70b_verify": dict(n_q_heads=64, n_kv_heads=8, head_dim=128, dtype="bf16",
                               prefix=8192, n_tree=64, capacity=8192 + 256, seed=2,
-                              value_scale=1.0 / math.sqrt(128), tree="top8", vocab=128256),
+                              value_scale=1.0 / math.sqrt(128), tree="top8", vocab=128256, layers=80),
     "qwen2_72b_32k_verify": dict(n_q_heads=64, n_kv_heads=8, head_dim=128, dtype="bf16",
                                  prefix=32768, n_tree=64, capacity=32768 + 256, seed=3,
-                                 value_scale=1.0 / math.sqrt(128), tree="top8", vocab=152064),
+                                 value_scale=1.0 / math.sqrt(128), tree="top8", vocab=152064, layers=80),
     "draft_loop_1b": dict(n_q_heads=32, n_kv_heads=8, head_dim=64, dtype="bf16",
                           prefix=4096, n_tree=64, capacity=8192, seed=4,
-                          value_scale=1.0 / 8.0, tree="top8", iterations=100, vocab=128256),
+                          value_scale=1.0 / 8.0, tree="top8", iterations=100, vocab=128256, layers=16),
     # The pages' operating point: a verify tree of bs = 8 nodes at 70B shapes
     # (the 8 most likely nodes of the width-8 expansion; HBM-bound).
     "llama3_70b_verify_bs8": dict(n_q_heads=64, n_kv_heads=8, head_dim=128, dtype="bf16",
                                   prefix=8192, n_tree=8, capacity=8192 + 256, seed=5,
-                                  value_scale=1.0 / math.sqrt(128), tree="top8_bs8", vocab=128256),
+                                  value_scale=1.0 / math.sqrt(128), tree="top8_bs8", vocab=128256, layers=80),
     # A draft-expansion step: only the w = 8 newest leaves of the 64-node tree
     # are queries, against the whole [prefix | tree].
     "draft_expand_w8": dict(n_q_heads=32, n_kv_heads=8, head_dim=64, dtype="bf16",
                             prefix=4096, n_tree=64, q_first=56, capacity=4096 + 256, seed=6,
-                            value_scale=1.0 / 8.0, tree="top8", vocab=128256),
+                            value_scale=1.0 / 8.0, tree="top8", vocab=128256, layers=16),
 }
 
 # vocab: the model family's vocabulary (Llama 3: 128256 token ids, Qwen2:
 # 152064), the row length of the target's logits in tree verification.
+# layers: the model's decoder layers (Llama 3 8B: 32, 70B: 80, Qwen2-72B: 80,
+# the Llama 3.2 1B draft: 16), i.e. the depth of the cache that one re-root
+# call moves.
 
 TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
 
