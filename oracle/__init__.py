@@ -27,6 +27,9 @@ gather (re-root). Points the pages leave open are taken as follows:
 * the whole accepted path moves into the prefix; survivors keep ascending
   original order.
 
+Maximum-likelihood expansion (``tree_expand_ref``): the k best (leaf, token)
+candidates by path score plus log-softmax become the new nodes.
+
 Tree verification (``tree_verify_ref``) reads the acceptance rule as greedy:
 a drafted token is accepted when it equals the target's arg-max at its parent
 and every ancestor was accepted; the deepest such node ends the accepted path.
@@ -47,3 +50,4 @@ from .tree_attn_ref import (  # noqa: F401
 )
 from .kv_reroot_ref import check_reroot_args, kv_reroot_ref, reroot_plan_ref  # noqa: F401
 from .tree_verify_ref import row_argmax, tree_verify_ref  # noqa: F401
+from .tree_expand_ref import log_softmax_rows, token_ranking, tree_expand_ref  # noqa: F401

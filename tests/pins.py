@@ -281,3 +281,94 @@ def pin_verify_chain(verify, rng, n=12, vocab=50):
         path, bonus, _ = verify(logits, tokens, parent)
         bad += (list(path) != list(range(k))) or (int(bonus) != int(planted[k]))
     return bad
+
+
+# ---------------------------------------------------------------------------
+# Maximum-likelihood expansion. The pins use scipy's log_softmax (a library
+# routine) and rank EVERY candidate of every leaf in one global sort; the
+# oracle keeps only each leaf's k best tokens before merging.
+
+
+def golden_expand_cases():
+    for c in load_golden("expand_cases.json")["cases"]:
+        c = dict(c)
+        with np.errstate(divide="ignore"):
+            x = np.log(np.array(c["weights"], dtype=np.float64))
+            c["path_scores"] = np.log(np.array(c["path_prob"], dtype=np.float64))
+        if "offsets" in c:
+            x = x + np.array(c["offsets"])[:, None]
+        c["logits"] = x
+        yield c
+
+
+def pin_expand_golden(expand):
+    """Worst deviation over the hand-worked cases: inf on a wrong node list,
+    else the largest score error."""
+    worst = 0.0
+    for c in golden_expand_cases():
+        got = expand(c["logits"], c["path_scores"], c["k"])
+        if [(int(i), int(t)) for i, t, _ in got] != [(i, t) for i, t, _ in c["nodes"]]:
+            return math.inf
+        for (_, _, s), (_, _, p) in zip(got, c["nodes"]):
+            want = math.log(p) if p > 0 else -math.inf
+            err = 0.0 if s == want else abs(s - want)
+            worst = max(worst, err)
+    return worst
+
+
+def expand_bruteforce(logits, path_scores, k):
+    """Every (leaf, token) of every leaf, scored with scipy's log_softmax and
+    ranked in one sort."""
+    from scipy.special import log_softmax
+    x = np.asarray(logits, dtype=np.float64)
+    logp = log_softmax(x, axis=1)
+    w, vocab = x.shape
+    every = []
+    for i in range(w):
+        by_logit = sorted(range(vocab), key=lambda t: (-x[i, t], t))
+        for slot, t in enumerate(by_logit):
+            every.append((path_scores[i] + logp[i, t], i, slot, t))
+    every.sort(key=lambda c: (-c[0], c[1], c[2]))
+    return [(i, t, s) for s, i, slot, t in sorted(every[:k], key=lambda c: (c[1], c[2]))]
+
+
+def pin_expand_bruteforce(expand, rng, trials=60):
+    """Worst deviation from the global brute force on small random frontiers
+    (integer logits, so equal logits and equal scores are common)."""
+    worst = 0.0
+    for _ in range(trials):
+        w, vocab = int(rng.integers(1, 7)), int(rng.integers(1, 41))
+        k = int(rng.integers(1, min(w * vocab, 20) + 1))
+        if rng.random() < 0.5:
+            x = rng.integers(-3, 4, size=(w, vocab)).astype(np.float64)
+            s = rng.integers(-2, 1, size=w).astype(np.float64)
+        else:
+            x = rng.standard_normal((w, vocab)) * 3
+            s = -rng.random(w) * 4
+        got = expand(x, s, k)
+        want = expand_bruteforce(x, s, k)
+        if [(int(i), int(t)) for i, t, _ in got] != [(i, t) for i, t, _ in want]:
+            return math.inf
+        worst = max(worst, max(abs(a[2] - b[2]) for a, b in zip(got, want)))
+    return worst
+
+
+def pin_expand_uniform(expand, rng):
+    """Equal logits within each row: every token of leaf i scores
+    s[i] - ln(vocab); leaves are taken by descending path score, tokens in
+    id order."""
+    worst = 0.0
+    for w, vocab, k in ((3, 5, 7), (8, 16, 8), (1, 9, 9), (4, 2, 8)):
+        s = -rng.permutation(w).astype(np.float64) * 0.75  # distinct
+        x = np.repeat(rng.standard_normal((w, 1)), vocab, axis=1)
+        want = []
+        for i in np.argsort(-s):
+            for t in range(vocab):
+                if len(want) < k:
+                    want.append((int(i), t, s[i] - math.log(vocab)))
+        want.sort()
+        got = expand(x, s, k)
+        if [(int(i), int(t)) for i, t, _ in got] != [(i, t) for i, t, _ in want]:
+            return math.inf
+        worst = max(worst, max(abs(a[2] - b[2]) for a, b in zip(got, want)))
+    return worst

@@ -221,3 +221,47 @@ VERIFY_SLIPS = {
 @pytest.mark.parametrize("slip", list(VERIFY_SLIPS))
 def test_verify_slip_is_caught(slip):
     assert verify_pins(_verify_mutant(*VERIFY_SLIPS[slip])) > 0
+
+
+# ---------------------------------------------------------------------------
+# Maximum-likelihood expansion: each mutant is the oracle's source with one slip.
+
+_EXPAND_SRC = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                                "oracle", "tree_expand_ref.py")).read()
+
+
+def _expand_mutant(old, new):
+    assert _EXPAND_SRC.count(old) == 1, old
+    ns = {"__name__": "oracle.tree_expand_mutant", "__package__": "oracle"}
+    exec(compile(_EXPAND_SRC.replace(old, new), "tree_expand_mutant", "exec"), ns)
+    return ns["tree_expand_ref"]
+
+
+def expand_pins(expand):
+    rng = np.random.default_rng(41)
+    return max(pins.pin_expand_golden(expand), pins.pin_expand_bruteforce(expand, rng, trials=30),
+               pins.pin_expand_uniform(expand, rng))
+
+
+def test_unmutated_expand_passes_every_pin():
+    assert expand_pins(oracle.tree_expand_ref) < 1e-12
+
+
+EXPAND_SLIPS = {
+    "no_path_score": ("cands.append((float(s[i] + logp[i, t])", "cands.append((float(logp[i, t])"),
+    "probability_not_log": ("cands.append((float(s[i] + logp[i, t])", "cands.append((float(s[i] + np.exp(logp[i, t]))"),
+    "raw_logits": ("logp = log_softmax_rows(x)", "logp = x"),
+    "max_not_taken_out": ("return x - (m + np.log(np.exp(x - m).sum(axis=1, keepdims=True)))",
+                          "return x - np.log(np.exp(x).sum(axis=1, keepdims=True))"),
+    "rank_ties_to_higher_id": ("return np.lexsort((np.arange(row.size), -row))",
+                               "return np.lexsort((-np.arange(row.size), -row))"),
+    "score_ties_to_higher_leaf": ("cands.sort(key=lambda c: (-c[0], c[1], c[2]))",
+                                  "cands.sort(key=lambda c: (-c[0], -c[1], c[2]))"),
+    "listed_by_score": ("chosen = sorted(cands[:k], key=lambda c: (c[1], c[2]))", "chosen = cands[:k]"),
+    "one_candidate_per_leaf": ("enumerate(token_ranking(x[i])[:k])", "enumerate(token_ranking(x[i])[:1])"),
+}
+
+
+@pytest.mark.parametrize("slip", list(EXPAND_SLIPS))
+def test_expand_slip_is_caught(slip):
+    assert expand_pins(_expand_mutant(*EXPAND_SLIPS[slip])) > 1e-6

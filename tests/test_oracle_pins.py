@@ -314,3 +314,36 @@ def test_verify_rejects_malformed_inputs():
         oracle.tree_verify_ref(np.zeros((3, 4)), [0], [-1, 0])  # one token short
     with pytest.raises(ValueError):
         oracle.tree_verify_ref(np.zeros((3, 4)), [0, 0], [-1, 1])  # parent not before the node
+
+
+# ---------------------------------------------------------------------------
+# Maximum-likelihood expansion
+
+def test_expand_hand_worked_cases():
+    assert pins.pin_expand_golden(oracle.tree_expand_ref) < 1e-12
+
+
+def test_expand_matches_global_bruteforce_with_library_log_softmax():
+    assert pins.pin_expand_bruteforce(oracle.tree_expand_ref, np.random.default_rng(31)) < 1e-12
+
+
+def test_expand_uniform_rows_closed_form():
+    assert pins.pin_expand_uniform(oracle.tree_expand_ref, np.random.default_rng(32)) < 1e-12
+
+
+def test_log_softmax_rows_normalises_and_matches_the_library():
+    from scipy.special import log_softmax
+    rng = np.random.default_rng(33)
+    x = rng.standard_normal((5, 1000)) * 20 + np.array([[0], [500], [-500], [1e4], [3]])
+    got = oracle.log_softmax_rows(x)
+    assert np.abs(got - log_softmax(x, axis=1)).max() < 1e-9
+    assert np.abs(np.exp(got).sum(axis=1) - 1).max() < 1e-12
+
+
+def test_expand_rejects_malformed_inputs():
+    with pytest.raises(ValueError):
+        oracle.tree_expand_ref(np.zeros((2, 3)), [0.0], 1)
+    with pytest.raises(ValueError):
+        oracle.tree_expand_ref(np.zeros((2, 3)), [0.0, 0.0], 7)
+    with pytest.raises(ValueError):
+        oracle.tree_expand_ref(np.full((1, 3), -np.inf), [0.0], 1)
