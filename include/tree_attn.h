@@ -1,10 +1,12 @@
 /*
  * tree_attn.h — C ABI of the MI355X (gfx950) tree-attention library.
  *
- * Three device operations sit behind this header:
+ * Four device operations sit behind this header:
  *
  *   ta_tree_attn    tree-masked attention of a token tree against a KV cache
  *                   laid out as [verified prefix | tree tokens];
+ *   ta_tree_expand  maximum-likelihood expansion of the draft tree: the k
+ *                   best children of its frontier leaves;
  *   ta_tree_verify  greedy verification of the tree against the target's
  *                   logits: the accepted path and the bonus token;
  *   ta_kv_reroot    re-root of that cache after verification: the accepted
@@ -196,6 +198,40 @@ size_t ta_tree_verify_workspace_bytes(int32_t n_tree);
 ta_status ta_tree_verify(const void* logits, int32_t dtype, int64_t vocab, int64_t row_stride,
                          const int32_t* tokens, const int32_t* parent, int32_t n_tree,
                          int32_t* choice_out, int32_t* result_out, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/*
+ * One maximum-likelihood expansion step of the draft tree. Source: SwiftSpec,
+ * Pith review page, "Assumptions & free parameters" (a path scores the sum of
+ * its tokens' log-softmax probabilities; expansion width w = 8).
+ *
+ * Frontier leaf i (row i of `logits`, the draft model's logits for the token
+ * after it) has path score path_scores[i]. Every (leaf, token) pair is a
+ * candidate child scored path_scores[i] + logits[i][t] - logsumexp(logits[i]);
+ * the k best become the new nodes. Within a leaf the candidates rank by logit
+ * (the lower token id first among equal logits): that rank is the child's
+ * slot. Equal scores go to the lower leaf, then the lower slot. Output entry
+ * j (j < k), in (leaf, slot) order: leaf_out[j] (row index), token_out[j],
+ * score_out[j] (fp32: log-sum-exp accumulated in fp32).
+ *
+ *  logits       device, w rows of `vocab` values of `dtype` (TA_F32, TA_BF16),
+ *               row i at logits + i * row_stride elements; 16-byte aligned,
+ *               row_stride >= vocab, row_stride * element size a multiple
+ *               of 16. 1 <= vocab <= 262144. Every row needs a finite value;
+ *               -inf entries are allowed (probability 0); NaN is undefined.
+ *  path_scores  device, w floats.
+ *  1 <= w <= 64, 1 <= k <= 16, k <= w * vocab.
+ *  leaf_out, token_out, score_out: device, k entries each.
+ *  workspace    device, >= ta_tree_expand_workspace_bytes(w) bytes, 256-byte
+ *               aligned; zero-filled once before its first use, and every
+ *               completed call leaves its counters at zero again. Not shared
+ *               with a call that can run at the same time.
+ * One launch on `stream`; nothing is synchronised.
+ */
+size_t ta_tree_expand_workspace_bytes(int32_t w);
+ta_status ta_tree_expand(const void* logits, int32_t dtype, int64_t vocab, int64_t row_stride,
+                         const float* path_scores, int32_t w, int32_t k, int32_t* leaf_out,
+                         int32_t* token_out, float* score_out, void* workspace,
                          size_t workspace_bytes, void* stream);
 
 /*

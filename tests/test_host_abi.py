@@ -228,3 +228,40 @@ def test_tree_verify_workspace_bytes():
     sizes = {L.ta_tree_verify_workspace_bytes(n) for n in range(65)}
     assert len(sizes) == 1 and 0 < sizes.pop() <= 8192
     assert L.ta_tree_verify_workspace_bytes(65) == 0 and L.ta_tree_verify_workspace_bytes(-1) == 0
+
+
+def _expand_call(logits=FAKE, dtype=ta.TA_BF16, vocab=1000, stride=1000, scores=FAKE, w=8, k=8,
+                 leaf=FAKE, token=FAKE, score=FAKE, ws=FAKE, ws_len=1 << 21):
+    return ta.lib().ta_tree_expand(logits, dtype, vocab, stride, scores, w, k, leaf, token, score, ws, ws_len, None)
+
+
+@pytest.mark.parametrize("kwargs, status", [
+    (dict(dtype=5), ta.TA_ERR_UNSUPPORTED),
+    (dict(w=0), ta.TA_ERR_UNSUPPORTED),
+    (dict(w=65), ta.TA_ERR_UNSUPPORTED),
+    (dict(k=0), ta.TA_ERR_UNSUPPORTED),
+    (dict(k=17), ta.TA_ERR_UNSUPPORTED),
+    (dict(vocab=0, stride=8), ta.TA_ERR_UNSUPPORTED),
+    (dict(vocab=262145, stride=262152), ta.TA_ERR_UNSUPPORTED),
+    (dict(vocab=1, stride=8, w=2, k=3), ta.TA_ERR_ARG),  # k > w * vocab
+    (dict(stride=999), ta.TA_ERR_ARG),
+    (dict(vocab=1001, stride=1001), ta.TA_ERR_ARG),
+    (dict(logits=None), ta.TA_ERR_ARG),
+    (dict(scores=None), ta.TA_ERR_ARG),
+    (dict(score=None), ta.TA_ERR_ARG),
+    (dict(logits=FAKE + 4), ta.TA_ERR_ARG),
+    (dict(token=FAKE + 1), ta.TA_ERR_ARG),
+    (dict(ws=None), ta.TA_ERR_ARG),
+    (dict(ws_len=1024), ta.TA_ERR_ARG),
+    (dict(ws=FAKE + 64), ta.TA_ERR_ARG),
+])
+def test_tree_expand_rejects_before_enqueueing(kwargs, status):
+    assert _expand_call(**kwargs) == status
+    assert ta.lib().ta_last_error()
+
+
+def test_tree_expand_workspace_bytes():
+    L = ta.lib()
+    assert L.ta_tree_expand_workspace_bytes(0) == 0 and L.ta_tree_expand_workspace_bytes(65) == 0
+    sizes = [L.ta_tree_expand_workspace_bytes(w) for w in range(1, 65)]
+    assert all(b > a for a, b in zip(sizes, sizes[1:])) and sizes[-1] <= 2 << 20

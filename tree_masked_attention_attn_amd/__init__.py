@@ -7,6 +7,7 @@ library has not been built, importing works but every call raises.
 
     tree_attn(q, k_cache, v_cache, prefix_len, parent, layer=0, out=None)
     tree_verify(logits, tokens, parent) -> (choice, result) device tensors
+    tree_expand(logits, path_scores, k) -> (leaf, token, score) device tensors
     kv_reroot(k_cache, v_cache, prefix_len, parent, accepted_path, surviving_nodes)
     tree_attn_workspace_bytes / tree_attn_num_splits / tree_ancestor_bits / kv_reroot_plan
 
@@ -92,6 +93,13 @@ def lib():
             L.ta_tree_verify.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
                                          ctypes.c_void_p, _I32P, ctypes.c_int32, ctypes.c_void_p,
                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+            L.ta_tree_expand_workspace_bytes.restype = ctypes.c_size_t
+            L.ta_tree_expand_workspace_bytes.argtypes = [ctypes.c_int32]
+            L.ta_tree_expand.restype = ctypes.c_int
+            L.ta_tree_expand.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
+                                         ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                         ctypes.c_void_p]
             L.ta_set_split_wait_limit.restype = None
             L.ta_set_split_wait_limit.argtypes = [ctypes.c_int32]
             L.ta_tree_ancestor_bits.restype = ctypes.c_int
@@ -254,6 +262,42 @@ def tree_verify(logits, tokens, parent, choice=None, result=None, workspace=None
                                 tokens.data_ptr() if n else None, par, n, choice.data_ptr(), result.data_ptr(),
                                 workspace.data_ptr(), ws_len, _stream_ptr(dev)))
     return choice, result
+
+
+def tree_expand(logits, path_scores, k, leaf=None, token=None, score=None, workspace=None):
+    """One maximum-likelihood expansion step; returns ``(leaf, token, score)``.
+
+    ``logits`` is a GPU tensor ``[w, vocab]`` (float32 or bfloat16; rows may be
+    strided, elements contiguous) of the draft model's logits after each
+    frontier leaf; ``path_scores`` a float32 GPU tensor ``[w]``. The outputs
+    (int32, int32, float32 GPU tensors ``[k]``, allocated if None) list the
+    ``k`` best children by (leaf, slot). Enqueued on torch's current stream;
+    nothing is synchronised.
+    """
+    if logits.dim() != 2 or not logits.is_cuda or logits.stride(1) != 1:
+        raise ValueError("logits must be a [w, vocab] GPU tensor with contiguous rows")
+    w = logits.shape[0]
+    dev = logits.device
+    if path_scores.dtype != torch.float32 or path_scores.shape != (w,) or not path_scores.is_contiguous() or \
+            path_scores.device != dev:
+        raise ValueError("path_scores must be a contiguous float32 tensor [w] on the logits' device")
+    k = int(k)
+    leaf = torch.empty(k, dtype=torch.int32, device=dev) if leaf is None else leaf
+    token = torch.empty(k, dtype=torch.int32, device=dev) if token is None else token
+    score = torch.empty(k, dtype=torch.float32, device=dev) if score is None else score
+    for name, t, dt in (("leaf", leaf, torch.int32), ("token", token, torch.int32), ("score", score, torch.float32)):
+        if t.dtype != dt or t.shape != (k,) or not t.is_contiguous() or t.device != dev:
+            raise ValueError(f"{name} must be a contiguous {dt} tensor [k] on the logits' device")
+    nbytes = lib().ta_tree_expand_workspace_bytes(w)
+    if nbytes == 0:
+        _check(TA_ERR_UNSUPPORTED)
+    if workspace is None:
+        workspace = _workspace(dev, nbytes, kind="expand")
+    ws_len = workspace.numel() * workspace.element_size()
+    _check(lib().ta_tree_expand(logits.data_ptr(), _dtype_code(logits), logits.shape[1], logits.stride(0),
+                                path_scores.data_ptr(), w, k, leaf.data_ptr(), token.data_ptr(), score.data_ptr(),
+                                workspace.data_ptr(), ws_len, _stream_ptr(dev)))
+    return leaf, token, score
 
 
 def accepted(result):

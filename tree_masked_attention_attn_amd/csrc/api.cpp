@@ -218,6 +218,63 @@ ta_status ta_tree_verify(const void* logits, int32_t dtype, int64_t vocab, int64
   return TA_OK;
 }
 
+size_t ta_tree_expand_workspace_bytes(int32_t w) {
+  clear_error();
+  if (w < 1 || w > kExpandMaxRows) {
+    fail(TA_ERR_UNSUPPORTED, "w must be in [1, " + std::to_string(kExpandMaxRows) + "]");
+    return 0;
+  }
+  return static_cast<size_t>(kExpandChunkBase) + static_cast<size_t>(w) * kExpandMaxChunks * kExpandChunkSlot;
+}
+
+ta_status ta_tree_expand(const void* logits, int32_t dtype, int64_t vocab, int64_t row_stride,
+                         const float* path_scores, int32_t w, int32_t k, int32_t* leaf_out,
+                         int32_t* token_out, float* score_out, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  clear_error();
+  const size_t es = dtype_bytes(dtype);
+  if (es == 0) return fail(TA_ERR_UNSUPPORTED, "dtype must be TA_F32 or TA_BF16");
+  if (w < 1 || w > kExpandMaxRows)
+    return fail(TA_ERR_UNSUPPORTED, "w must be in [1, " + std::to_string(kExpandMaxRows) + "]");
+  if (k < 1 || k > kExpandMaxK) return fail(TA_ERR_UNSUPPORTED, "k must be in [1, " + std::to_string(kExpandMaxK) + "]");
+  const int64_t max_vocab = static_cast<int64_t>(kExpandMaxChunks) * kExpandChunk;
+  if (vocab < 1 || vocab > max_vocab)
+    return fail(TA_ERR_UNSUPPORTED, "vocab must be in [1, " + std::to_string(max_vocab) + "]");
+  if (static_cast<int64_t>(k) > static_cast<int64_t>(w) * vocab) return fail(TA_ERR_ARG, "k exceeds w * vocab");
+  if (row_stride < vocab) return fail(TA_ERR_ARG, "row_stride is smaller than vocab");
+  if ((static_cast<uint64_t>(row_stride) * es) % 16 != 0)
+    return fail(TA_ERR_ARG, "row_stride * element size must be a multiple of 16 bytes");
+  if (logits == nullptr || path_scores == nullptr || leaf_out == nullptr || token_out == nullptr ||
+      score_out == nullptr)
+    return fail(TA_ERR_ARG, "logits, path_scores or an output is null");
+  if (reinterpret_cast<uintptr_t>(logits) & 15) return fail(TA_ERR_ARG, "logits must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(path_scores) | reinterpret_cast<uintptr_t>(leaf_out) |
+       reinterpret_cast<uintptr_t>(token_out) | reinterpret_cast<uintptr_t>(score_out)) & 3)
+    return fail(TA_ERR_ARG, "path_scores and the outputs must be 4-byte aligned");
+  const size_t need = ta_tree_expand_workspace_bytes(w);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(TA_ERR_ARG, "workspace too small: need " + std::to_string(need) + " bytes, got " +
+                                std::to_string(workspace_bytes));
+  if (reinterpret_cast<uintptr_t>(workspace) & 255) return fail(TA_ERR_ARG, "workspace must be 256-byte aligned");
+  ExpandArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.logits = logits;
+  a.row_stride = row_stride;
+  a.vocab = vocab;
+  a.path_scores = path_scores;
+  a.w = w;
+  a.k = k;
+  a.chunks = static_cast<int32_t>((vocab + kExpandChunk - 1) / kExpandChunk);
+  a.ws_bytes = static_cast<int32_t>(need);
+  a.leaf_out = leaf_out;
+  a.token_out = token_out;
+  a.score_out = score_out;
+  a.ws = static_cast<char*>(workspace);
+  hipError_t e = launch_tree_expand(a, dtype, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_error(e, "tree_expand launch");
+  return TA_OK;
+}
+
 ta_status ta_kv_reroot(const ta_kv_cache* cache, int32_t prefix_len, const int32_t* parent,
                        int32_t n_tree, const int32_t* accepted_path, int32_t n_accepted,
                        const int32_t* surviving_nodes, int32_t n_surviving, int32_t* new_parent,

@@ -83,4 +83,38 @@ struct VerifyArgs {
 
 hipError_t launch_tree_verify(const VerifyArgs& a, int32_t dtype, hipStream_t stream);
 
+// Maximum-likelihood expansion: up to 64 frontier leaves, k <= 16 new nodes,
+// vocabularies of up to 64 chunks of 4096 logits.
+constexpr int kExpandChunk = 4096;       // logits per workgroup
+constexpr int kExpandMaxK = 16;
+constexpr int kExpandMaxRows = 64;
+constexpr int kExpandMaxChunks = 64;
+// Workspace layout (zero between calls except where written before read):
+// the leaves' arrival count at 0; leaf r's arrival count at
+// kExpandRowCount * (1 + r); leaf r's k (score, token) at kExpandRowBase +
+// r * kExpandRowSlot; chunk c of leaf r's (max, sum) and k keys at
+// kExpandChunkBase + (r * kExpandMaxChunks + c) * kExpandChunkSlot.
+constexpr int kExpandRowCount = 64;
+constexpr int kExpandRowBase = 8192;
+constexpr int kExpandRowSlot = 8 * kExpandMaxK;
+constexpr int kExpandChunkBase = 16384;
+constexpr int kExpandChunkSlot = 256;
+
+struct ExpandArgs {
+  const void* logits;        // w rows of draft logits, row_stride elements apart
+  int64_t row_stride;
+  int64_t vocab;
+  const float* path_scores;  // [w]
+  int32_t w;                 // frontier leaves
+  int32_t k;                 // new nodes
+  int32_t chunks;            // ceil(vocab / kExpandChunk)
+  int32_t ws_bytes;
+  int32_t* leaf_out;         // [k]
+  int32_t* token_out;        // [k]
+  float* score_out;          // [k]
+  char* ws;
+};
+
+hipError_t launch_tree_expand(const ExpandArgs& a, int32_t dtype, hipStream_t stream);
+
 }  // namespace ta

@@ -353,3 +353,18 @@ def make_verify_inputs(cfg, parent, rng=None, accept=0.8, logit_scale=2.0):
             t = int(rng.integers(0, max(vocab - 1, 1)))
             tokens[node] = want if k == hit else (t if t < want else t + 1)
     return dict(logits=torch.from_numpy(x).to(TORCH_DTYPE[cfg["dtype"]]), tokens=torch.from_numpy(tokens))
+
+
+def make_expand_inputs(cfg, w, rng=None, logit_scale=2.0):
+    """Draft logits and path scores of a frontier of ``w`` leaves.
+
+    Logits are N(0, 1) * ``logit_scale`` over the model's vocabulary (cfg
+    dtype); path scores are float32 sums of 1..8 draws of -Exp(1) (a leaf
+    at depth d has d log-probabilities along its path). Returns ``logits``
+    (torch, CPU) and ``path_scores`` (torch float32, CPU).
+    """
+    rng = np.random.default_rng(cfg["seed"] + 2000) if rng is None else rng
+    x = rng.standard_normal((w, cfg["vocab"]), dtype=np.float32) * np.float32(logit_scale)
+    depth = rng.integers(1, 9, size=w)
+    s = np.array([-rng.exponential(1.0, size=d).sum() for d in depth], dtype=np.float32)
+    return dict(logits=torch.from_numpy(x).to(TORCH_DTYPE[cfg["dtype"]]), path_scores=torch.from_numpy(s))
