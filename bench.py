@@ -6,11 +6,13 @@ surviving subtree), i.e. the whole path once. The default workload is the
 Llama-3-70B-shaped verify: 64 query / 8 KV heads, head_dim 128, bf16, prefix
 8192, a 64-node width-8 tree; synthetic seeded inputs.
 
-Labelled extras, outside the step: ``tree_verify`` (greedy verification of the
-same tree against the target's logits over the model's vocabulary) and
+Labelled extras, outside the step (``--no-extras`` skips them): ``tree_verify``
+(greedy verification of the same tree against the target's logits over the
+model's vocabulary), ``tree_expand`` (one maximum-likelihood expansion step:
+8 frontier leaves, 8 new nodes, over the same vocabulary) and
 ``kv_reroot_all_layers`` (one re-root call over a cache with all of the
-model's layers: the draft side with its survivors, and the target side with
-the accepted rows only).
+model's layers, for the path the verification accepted: the draft side with
+its survivors, and the target side with the accepted rows only).
 
 Timing: inputs are resident in HBM before the timed region. ``--rotate`` input
 sets are cycled so that the working set exceeds twice the 256 MB Infinity
@@ -103,6 +105,13 @@ def verify_bytes(cfg, n):
     drafted tokens, the arg-max and result arrays."""
     es = 4 if cfg["dtype"] == "f32" else 2
     return (n + 1) * cfg["vocab"] * es + 4 * n + 4 * (n + 1) + 4 * (n + 2)
+
+
+def expand_bytes(cfg, w, k):
+    """Algorithmic bytes of one tree_expand: every logit once, the path
+    scores and the three k-entry outputs."""
+    es = 4 if cfg["dtype"] == "f32" else 2
+    return w * cfg["vocab"] * es + 4 * w + 12 * k
 
 
 def pct(xs, p):
@@ -262,6 +271,104 @@ def main_traffic(args):
     print(json.dumps(rec))
 
 
+def run_extras(ta, torch, cfg, dev, parent, P, K, timed):
+    """The labelled extras: verification, expansion, all-layer re-root."""
+    # Verification of the same tree against the target's logits: rotated
+    # logits sets (positive rescales of one draw, so the same tokens apply)
+    # that together exceed twice the Infinity Cache.
+    n = cfg["n_tree"]
+    vx = W.make_verify_inputs(cfg, parent)
+    v_bytes = verify_bytes(cfg, n)
+    vrot = max(2, math.ceil(2 * MALL_BYTES / v_bytes) + 1)
+    v0 = vx["logits"].to(dev)
+    v_sets = [v0 * (1.0 + 1e-3 * r) if r else v0 for r in range(vrot)]
+    v_tok = vx["tokens"].to(dev)
+    v_choice = torch.empty(n + 1, dtype=torch.int32, device=dev)
+    v_result = torch.empty(n + 2, dtype=torch.int32, device=dev)
+    v_ws = torch.zeros(8192, dtype=torch.uint8, device=dev)
+
+    def verify(i):
+        ta.tree_verify(v_sets[i % vrot], v_tok, parent, choice=v_choice, result=v_result, workspace=v_ws)
+
+    for i in range(5):
+        verify(i)
+    _, ver_us, _ = timed(verify, K, each=True)
+    ver_b2b, _, _ = timed(verify, K)
+    # logits still in the caches, as when the LM head has just written them
+    _, ver_hot, _ = timed(lambda i: verify(0), 50, each=True)
+    v_path = ta.accepted(v_result)[0]
+    del v_sets, v0
+
+    # One re-root call over a cache with all of the model's layers, for the
+    # path the verification above accepted: the draft side keeps the subtree
+    # below its last node, the target side only the accepted rows. The
+    # prefix position rotates (P, P - n, ...) so that the rows touched by
+    # consecutive calls differ and together exceed twice the Infinity Cache.
+    n_layers = cfg.get("layers", 1)
+    big = (n_layers, cfg["n_kv_heads"], cfg["capacity"], cfg["head_dim"])
+    k_all = torch.zeros(big, dtype=W.TORCH_DTYPE[cfg["dtype"]], device=dev)
+    v_all = torch.zeros(big, dtype=W.TORCH_DTYPE[cfg["dtype"]], device=dev)
+    all_layers = {}
+    v_surv = W.descendants(parent, v_path[-1]) if v_path else list(range(n))
+    for side, s_surv in (("draft", v_surv), ("target", [])):
+        s_src, _, _ = ta.kv_reroot_plan(P, cfg["capacity"], parent, v_path, s_surv)
+        b = reroot_bytes(cfg, s_src, P, n_layers)
+        rrot = max(1, min(P // n, math.ceil(2 * MALL_BYTES / max(b, 1)) + 1))
+
+        def reroot_all(i, s_surv=s_surv, rrot=rrot):
+            ta.kv_reroot(k_all, v_all, P - (i % rrot) * n, parent, v_path, s_surv)
+
+        for i in range(3):
+            reroot_all(i)
+        _, ra_us, _ = timed(reroot_all, K, each=True)
+        ra_mean = statistics.fmean(ra_us)
+        all_layers[side] = {"survivors": len(s_surv), "us_mean": round(ra_mean, 2),
+                            "us_p50": round(pct(ra_us, 50), 2), "algorithmic_bytes": b,
+                            "GBs": round(b / (ra_mean * 1e-6) / 1e9, 1),
+                            "hbm_frac": round(b / (ra_mean * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                            "rotated_positions": rrot}
+    del k_all, v_all
+
+    # One maximum-likelihood expansion step: 8 frontier leaves' draft logits
+    # over the vocabulary (rotated, positively rescaled sets), 8 new nodes.
+    ex_w, ex_k = 8, 8
+    ex = W.make_expand_inputs(cfg, ex_w)
+    e_bytes = expand_bytes(cfg, ex_w, ex_k)
+    erot = max(2, math.ceil(2 * MALL_BYTES / e_bytes) + 1)
+    e0 = ex["logits"].to(dev)
+    e_sets = [e0 * (1.0 + 1e-3 * r) if r else e0 for r in range(erot)]
+    e_scores = ex["path_scores"].to(dev)
+    e_out = [torch.empty(ex_k, dtype=t, device=dev) for t in (torch.int32, torch.int32, torch.float32)]
+    e_ws = torch.zeros(ta.lib().ta_tree_expand_workspace_bytes(ex_w), dtype=torch.uint8, device=dev)
+
+    def expand(i):
+        ta.tree_expand(e_sets[i % erot], e_scores, ex_k, leaf=e_out[0], token=e_out[1], score=e_out[2],
+                       workspace=e_ws)
+
+    for i in range(5):
+        expand(i)
+    _, ex_us, _ = timed(expand, K, each=True)
+    ex_b2b, _, _ = timed(expand, K)
+    _, ex_hot, _ = timed(lambda i: expand(0), 50, each=True)
+    del e_sets, e0
+    ex_mean = statistics.fmean(ex_us)
+    ver_mean = statistics.fmean(ver_us)
+    return {
+        "tree_verify": {"vocab": cfg["vocab"], "rows": n + 1, "accepted_path": len(v_path),
+                        "us_mean": round(ver_mean, 2), "us_p50": round(pct(ver_us, 50), 2),
+                        "us_launch_period_back_to_back": round(ver_b2b / K, 2), "algorithmic_bytes": v_bytes,
+                        "GBs": round(v_bytes / (ver_mean * 1e-6) / 1e9, 1),
+                        "hbm_frac": round(v_bytes / (ver_mean * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                        "hot_cache_us_p50": round(statistics.median(ver_hot), 2), "rotated_sets": vrot},
+        "kv_reroot_all_layers": dict(layers=n_layers, accepted_path=len(v_path), **all_layers),
+        "tree_expand": {"vocab": cfg["vocab"], "w": ex_w, "k": ex_k, "us_mean": round(ex_mean, 2),
+                        "us_p50": round(pct(ex_us, 50), 2), "us_launch_period_back_to_back": round(ex_b2b / K, 2),
+                        "hot_cache_us_p50": round(statistics.median(ex_hot), 2), "algorithmic_bytes": e_bytes,
+                        "GBs": round(e_bytes / (ex_mean * 1e-6) / 1e9, 1),
+                        "hbm_frac": round(e_bytes / (ex_mean * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "rotated_sets": erot},
+    }
+
+
 # --------------------------------------------------------------------------
 
 
@@ -275,6 +382,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib", action="store_true", help="also run one plain device copy (counter calibration)")
+    ap.add_argument("--no-extras", action="store_true", help="skip the labelled extras (verify, expand, all layers)")
     ap.add_argument("--summarize", nargs=2, metavar=("DIR", "OUT"))
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--command", default=None, help="command line recorded in a summary")
@@ -386,56 +494,8 @@ def main():
     _, hot, _ = timed(lambda i: attn(0), 50, each=True)
     hot_us = statistics.median(hot)
 
-    # Verification of the same tree against the target's logits: rotated
-    # logits sets (positive rescales of one draw, so the same tokens apply)
-    # that together exceed twice the Infinity Cache.
-    n = cfg["n_tree"]
-    vx = W.make_verify_inputs(cfg, parent)
-    v_bytes = verify_bytes(cfg, n)
-    vrot = max(2, math.ceil(2 * MALL_BYTES / v_bytes) + 1)
-    v0 = vx["logits"].to(dev)
-    v_sets = [v0 * (1.0 + 1e-3 * r) if r else v0 for r in range(vrot)]
-    v_tok = vx["tokens"].to(dev)
-    v_choice = torch.empty(n + 1, dtype=torch.int32, device=dev)
-    v_result = torch.empty(n + 2, dtype=torch.int32, device=dev)
-    v_ws = torch.zeros(8192, dtype=torch.uint8, device=dev)
+    extras = {} if args.no_extras else run_extras(ta, torch, cfg, dev, parent, P, K, timed)
 
-    def verify(i):
-        ta.tree_verify(v_sets[i % vrot], v_tok, parent, choice=v_choice, result=v_result, workspace=v_ws)
-
-    for i in range(5):
-        verify(i)
-    _, ver_us, _ = timed(verify, K, each=True)
-    ver_b2b, _, _ = timed(verify, K)
-    v_accepted = ta.accepted(v_result)[0]
-    del v_sets, v0
-
-    # One re-root call over a cache with all of the model's layers. The
-    # prefix position rotates (P, P - n, ...) so that the rows touched by
-    # consecutive calls differ and together exceed twice the Infinity Cache.
-    n_layers = cfg.get("layers", 1)
-    big = (n_layers, cfg["n_kv_heads"], cfg["capacity"], cfg["head_dim"])
-    k_all = torch.zeros(big, dtype=base["k"].dtype, device=dev)
-    v_all = torch.zeros(big, dtype=base["k"].dtype, device=dev)
-    all_layers = {}
-    for side, s_surv in (("draft", surv), ("target", [])):
-        s_src, _, _ = ta.kv_reroot_plan(P, cfg["capacity"], parent, path, s_surv)
-        b = reroot_bytes(cfg, s_src, P, n_layers)
-        rrot = max(1, min(P // n, math.ceil(2 * MALL_BYTES / max(b, 1)) + 1))
-
-        def reroot_all(i, s_surv=s_surv, rrot=rrot):
-            ta.kv_reroot(k_all, v_all, P - (i % rrot) * n, parent, path, s_surv)
-
-        for i in range(3):
-            reroot_all(i)
-        _, ra_us, _ = timed(reroot_all, K, each=True)
-        ra_mean = statistics.fmean(ra_us)
-        all_layers[side] = {"survivors": len(s_surv), "us_mean": round(ra_mean, 2),
-                            "us_p50": round(pct(ra_us, 50), 2), "algorithmic_bytes": b,
-                            "GBs": round(b / (ra_mean * 1e-6) / 1e9, 1),
-                            "hbm_frac": round(b / (ra_mean * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                            "rotated_positions": rrot}
-    del k_all, v_all
 
     nbytes, flops, anc = tree_attn_work(cfg, parent)
     rr_bytes = reroot_bytes(cfg, src_rows, P)
@@ -483,13 +543,7 @@ def main():
         "kv_reroot": {"us_mean": round(rr_mean, 2), "us_p50": round(pct(reroot_us, 50), 2),
                       "us_launch_period_back_to_back": round(rr_b2b / K, 2),
                       "algorithmic_bytes": rr_bytes, "GBs": round(rr_bytes / (rr_mean * 1e-6) / 1e9, 2)},
-        "tree_verify": {"vocab": cfg["vocab"], "rows": n + 1, "accepted_path": len(v_accepted),
-                        "us_mean": round(statistics.fmean(ver_us), 2), "us_p50": round(pct(ver_us, 50), 2),
-                        "us_launch_period_back_to_back": round(ver_b2b / K, 2), "algorithmic_bytes": v_bytes,
-                        "GBs": round(v_bytes / (statistics.fmean(ver_us) * 1e-6) / 1e9, 1),
-                        "hbm_frac": round(v_bytes / (statistics.fmean(ver_us) * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                        "rotated_sets": vrot},
-        "kv_reroot_all_layers": dict(layers=n_layers, accepted_path=len(path), **all_layers),
+        **extras,
         "wall_s_timed_region": round(t_wall, 4),
         "kernel_source_sha": kernel_source_sha(),
         "roofline": roof,

@@ -29,6 +29,7 @@
 
 #include "launch.h"
 #include "tree_attn.h"
+#include "wave_ops.h"
 
 namespace ta {
 namespace {
@@ -39,36 +40,9 @@ constexpr int kChunk = kThreads * kPerThread;  // logits per workgroup
 constexpr int kWriteThrough = 16;              // cache policy of workspace traffic (sc1)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_huge_valf();
-typedef unsigned long long u64;
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 static_assert(kChunk == kExpandChunk, "chunk size shared with the host");
-
-// Orderable image of a float (larger float, larger key; -0.0 as +0.0).
-__device__ __forceinline__ uint32_t order_key(float x) {
-  uint32_t u = __float_as_uint(x);
-  if (u == 0x80000000u) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-__device__ __forceinline__ float key_value(uint32_t k) {
-  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
-}
-
-// Candidate key: value first, then the lower id (the low word holds ~id).
-// Zero is below every real candidate (-inf's value key is 0x007fffff).
-__device__ __forceinline__ u64 cand_key(float x, uint32_t id) {
-  return (static_cast<u64>(order_key(x)) << 32) | static_cast<u64>(~id);
-}
-
-__device__ __forceinline__ u64 wave_max(u64 k) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const u64 o = __shfl_xor(k, m, 64);
-    k = o > k ? o : k;
-  }
-  return k;
-}
 
 // (max, sum of exp(x - max)) of the union of two sets; (-inf, 0) is empty.
 __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
@@ -77,6 +51,20 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2
   const float b = m2 == kNegInf ? 0.f : s2 * __builtin_amdgcn_exp2f((m2 - M) * kLog2e);
   m = M;
   s = a + b;
+}
+
+// (max, sum) of the whole wave, returned to every lane.
+__device__ __forceinline__ void lse_wave(float& m, float& s) {
+  lse_merge(m, s, dpp_f32<dpp::kXor1>(m), dpp_f32<dpp::kXor1>(s));
+  lse_merge(m, s, dpp_f32<dpp::kXor2>(m), dpp_f32<dpp::kXor2>(s));
+  lse_merge(m, s, dpp_f32<dpp::kRor4>(m), dpp_f32<dpp::kRor4>(s));
+  lse_merge(m, s, dpp_f32<dpp::kRor8>(m), dpp_f32<dpp::kRor8>(s));
+  float m0 = readlane_f32(m, 0), s0 = readlane_f32(s, 0);
+  lse_merge(m0, s0, readlane_f32(m, 16), readlane_f32(s, 16));
+  lse_merge(m0, s0, readlane_f32(m, 32), readlane_f32(s, 32));
+  lse_merge(m0, s0, readlane_f32(m, 48), readlane_f32(s, 48));
+  m = m0;
+  s = s0;
 }
 
 template <typename T>
@@ -140,8 +128,7 @@ __global__ __launch_bounds__(kThreads) void tree_expand_kernel(const ExpandArgs 
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) s += __builtin_amdgcn_exp2f((v[i] - m) * kLog2e);
   }
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) lse_merge(m, s, __shfl_xor(m, d, 64), __shfl_xor(s, d, 64));
+  lse_wave(m, s);
 
   // The wave's K best keys: K rounds of a wave maximum over each lane's best
   // key below the last winner (keys are unique: they hold the token id).
@@ -153,13 +140,24 @@ __global__ __launch_bounds__(kThreads) void tree_expand_kernel(const ExpandArgs 
   };
   __shared__ u64 s_key[4][kExpandMaxK];
   __shared__ float s_m[4], s_s[4];
-  u64 cand = best_below(~0ull);
+  // The lane's best and second-best keys: a winner moves on to its second
+  // and only re-scans its keys when that one is taken too.
+  u64 cand = 0, alt = 0;
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i) {
+    const u64 q = key[i];
+    alt = q > cand ? cand : (q > alt ? q : alt);
+    cand = q > cand ? q : cand;
+  }
 #pragma unroll
   for (int r = 0; r < kExpandMaxK; ++r) {
     if (r < K) {
-      const u64 w = wave_max(cand);
+      const u64 w = wave_max_u64(cand);
       if (lane == 0) s_key[wave][r] = w;
-      if (cand == w && w != 0) cand = best_below(w);
+      if (cand == w && w != 0) {
+        cand = alt != 0 ? alt : best_below(w);
+        alt = 0;
+      }
     }
   }
   if (lane == 0) {
@@ -175,7 +173,7 @@ __global__ __launch_bounds__(kThreads) void tree_expand_kernel(const ExpandArgs 
 #pragma unroll
   for (int r = 0; r < kExpandMaxK; ++r) {
     if (r < K) {
-      const u64 w = wave_max(c4);
+      const u64 w = wave_max_u64(c4);
       if (lane == r) mine = w;
       if (c4 == w) c4 = 0;
     }
@@ -198,7 +196,7 @@ __global__ __launch_bounds__(kThreads) void tree_expand_kernel(const ExpandArgs 
   if (lane == 0)
     last = __builtin_amdgcn_atomic_inc32(reinterpret_cast<unsigned*>(a.ws + kExpandRowCount * (1 + row)),
                                          a.chunks - 1, __ATOMIC_RELAXED, "agent") == static_cast<unsigned>(a.chunks - 1);
-  if (!__shfl(last, 0, 64)) return;
+  if (!__builtin_amdgcn_readfirstlane(last)) return;
 
   // The leaf's last chunk: lane c reads chunk c's (max, sum) and its K keys
   // (device-scope loads: they see memory as the count did).
@@ -215,8 +213,7 @@ __global__ __launch_bounds__(kThreads) void tree_expand_kernel(const ExpandArgs 
     for (int r = 0; r < kExpandMaxK; ++r)
       if (r < K) kk[r] = __builtin_bit_cast(u64, __builtin_amdgcn_raw_buffer_load_b64(ws, sl + 8 + 8 * r, 0, kWriteThrough));
   }
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) lse_merge(lm, ls, __shfl_xor(lm, d, 64), __shfl_xor(ls, d, 64));
+  lse_wave(lm, ls);
   const float log_sum = __logf(ls);  // logsumexp = lm + log_sum
   // K rounds over the chunks' sorted lists: the lane holding the winner
   // drops its head.
@@ -224,7 +221,7 @@ __global__ __launch_bounds__(kThreads) void tree_expand_kernel(const ExpandArgs 
 #pragma unroll
   for (int r = 0; r < kExpandMaxK; ++r) {
     if (r < K) {
-      const u64 w = wave_max(kk[0]);
+      const u64 w = wave_max_u64(kk[0]);
       if (lane == r) rk = w;
       if (kk[0] == w && w != 0) {
 #pragma unroll
@@ -248,7 +245,7 @@ __global__ __launch_bounds__(kThreads) void tree_expand_kernel(const ExpandArgs 
   if (lane == 0)
     last = __builtin_amdgcn_atomic_inc32(reinterpret_cast<unsigned*>(a.ws), a.w - 1, __ATOMIC_RELAXED,
                                          "agent") == static_cast<unsigned>(a.w - 1);
-  if (!__shfl(last, 0, 64)) return;
+  if (!__builtin_amdgcn_readfirstlane(last)) return;
 
   // The last leaf: lane l holds leaf l's K (score, token) in slot order; K
   // rounds pick the best head (score, then the lower leaf, then the lower
@@ -281,11 +278,11 @@ __global__ __launch_bounds__(kThreads) void tree_expand_kernel(const ExpandArgs 
       const u64 hk = tk[0] >= 0 ? (static_cast<u64>(order_key(sc[0])) << 32) |
                                       static_cast<u64>(~static_cast<uint32_t>((lane << 8) | head))
                                 : 0ull;
-      const u64 w = wave_max(hk);
+      const u64 w = wave_max_u64(hk);
       const uint32_t who = ~static_cast<uint32_t>(w);  // (leaf << 8) | slot
       const int src = static_cast<int>(who >> 8);
-      const int win_tok = __shfl(tk[0], src, 64);
-      const float win_score = __shfl(sc[0], src, 64);
+      const int win_tok = __builtin_amdgcn_readlane(tk[0], src);
+      const float win_score = readlane_f32(sc[0], src);
       if (lane == r) {
         out_leaf = src;
         out_slot = static_cast<int>(who & 255u);
@@ -309,7 +306,7 @@ __global__ __launch_bounds__(kThreads) void tree_expand_kernel(const ExpandArgs 
   int pos = 0;
 #pragma unroll
   for (int j = 0; j < kExpandMaxK; ++j) {
-    if (j < K) pos += __shfl(mykey, j, 64) < mykey ? 1 : 0;
+    if (j < K) pos += __builtin_amdgcn_readlane(mykey, j) < mykey ? 1 : 0;
   }
   if (lane < K) {
     a.leaf_out[pos] = out_leaf;

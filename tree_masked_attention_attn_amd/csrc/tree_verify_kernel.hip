@@ -33,37 +33,13 @@
 
 #include "launch.h"
 #include "tree_attn.h"
+#include "wave_ops.h"
 
 namespace ta {
 namespace {
 
 constexpr int kThreads = 256;
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned long long u64;
-
-// Orderable image of a float: larger float, larger key (-0.0 taken as +0.0,
-// so the two compare equal as they do as floats).
-__device__ __forceinline__ uint32_t order_key(float x) {
-  uint32_t u = __float_as_uint(x);
-  if (u == 0x80000000u) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-// Key of candidate (x, index): value first, then the lower index. Zero is
-// below every candidate's key (the lowest value key, that of -inf, is
-// 0x007fffff), so zero-filled slots are the identity of the max.
-__device__ __forceinline__ u64 cand_key(float x, uint32_t idx) {
-  return (static_cast<u64>(order_key(x)) << 32) | static_cast<u64>(0xffffffffu - idx);
-}
-
-__device__ __forceinline__ u64 wave_max(u64 k) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const u64 o = __shfl_xor(k, m, 64);
-    k = o > k ? o : k;
-  }
-  return k;
-}
 
 template <typename T>
 __device__ __forceinline__ float to_float(T x) {
@@ -147,7 +123,7 @@ __global__ __launch_bounds__(kThreads) void tree_verify_kernel(const VerifyArgs 
   __shared__ u64 s_key[kThreads / 64];
   __shared__ int s_last;
   __shared__ int s_choice[kMaxVerifyRows];
-  u64 key = wave_max(any ? cand_key(best, bidx) : 0ull);
+  u64 key = wave_max_u64(any ? cand_key(best, bidx) : 0ull);
   if (lane == 0) s_key[wave] = key;
   __syncthreads();
   if (tid == 0) {
@@ -188,12 +164,10 @@ __global__ __launch_bounds__(kThreads) void tree_verify_kernel(const VerifyArgs 
   const u64 matched = __ballot(match);
   const bool accepted = live && (anc & ~matched) == 0ull;
   // deepest accepted node, lowest index among equally deep ones
-  int best_node = accepted ? (__popcll(anc) << 8) | (255 - lane) : 0;
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) best_node = max(best_node, __shfl_xor(best_node, m, 64));
+  const int best_node = wave_max_i32(accepted ? (__popcll(anc) << 8) | (255 - lane) : 0);
   const int depth = best_node >> 8;
   const int last = depth > 0 ? 255 - (best_node & 255) : -1;
-  const u64 path_bits = last >= 0 ? __shfl(anc, last, 64) : 0ull;
+  const u64 path_bits = last >= 0 ? readlane_u64(anc, last) : 0ull;
   // result = [m, bonus, path (root to leaf), -1 ...]: node j on the path goes
   // to position 2 + (number of path nodes below j); ancestors have lower
   // indices, so that is root-to-leaf order.
