@@ -285,7 +285,7 @@ def run_extras(ta, torch, cfg, dev, parent, P, K, timed):
     v_tok = vx["tokens"].to(dev)
     v_choice = torch.empty(n + 1, dtype=torch.int32, device=dev)
     v_result = torch.empty(n + 2, dtype=torch.int32, device=dev)
-    v_ws = torch.zeros(8192, dtype=torch.uint8, device=dev)
+    v_ws = torch.zeros(16384, dtype=torch.uint8, device=dev)
 
     def verify(i):
         ta.tree_verify(v_sets[i % vrot], v_tok, parent, choice=v_choice, result=v_result, workspace=v_ws)

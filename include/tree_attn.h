@@ -42,7 +42,7 @@ extern "C" {
 #endif
 
 #define TA_ABI_VERSION 1
-#define TA_MAX_TREE 64 /* nodes per call: one 64-bit ancestor word per node */
+#define TA_MAX_TREE 128 /* nodes per call: two 64-bit ancestor words per node */
 
 typedef enum {
   TA_OK = 0,
@@ -238,14 +238,19 @@ ta_status ta_tree_expand(const void* logits, int32_t dtype, int64_t vocab, int64
  * Host-only planning steps of ta_tree_attn and ta_kv_reroot (no device work; usable
  * without a GPU).
  *
- * ta_tree_ancestor_bits: bits_out[i] has bit j set iff node j is i itself or
- * an ancestor of i. Validates parent like ta_tree_attn.
+ * ta_tree_ancestor_bitset: words_out[2 i + w] has bit b set iff node 64 w + b
+ * is i itself or an ancestor of i (two words per node, 2 n_tree words).
+ * Validates parent like ta_tree_attn.
+ *
+ * ta_tree_ancestor_bits: the same for trees of at most 64 nodes, one word per
+ * node (bits_out[i]); TA_ERR_UNSUPPORTED for larger trees.
  *
  * ta_kv_reroot_plan: validates a re-root request exactly like ta_kv_reroot and
  * writes src_rows_out[k] = prefix_len + order[k] for k < n_accepted +
  * n_surviving (the source slot of destination slot prefix_len + k), plus
  * new_parent and new_prefix_len as ta_kv_reroot would.
  */
+ta_status ta_tree_ancestor_bitset(const int32_t* parent, int32_t n_tree, uint64_t* words_out);
 ta_status ta_tree_ancestor_bits(const int32_t* parent, int32_t n_tree, uint64_t* bits_out);
 ta_status ta_kv_reroot_plan(int32_t prefix_len, int32_t capacity, const int32_t* parent,
                             int32_t n_tree, const int32_t* accepted_path, int32_t n_accepted,

@@ -99,6 +99,37 @@ def test_frontier_rows_edge_cases():
     assert empty.shape[0] == 0
 
 
+def test_frontier_rows_past_64_nodes():
+    rng = np.random.default_rng(23)
+    cfg = dict(n_q_heads=8, n_kv_heads=2, head_dim=128, dtype="bf16", prefix=500, n_tree=128,
+               capacity=700, seed=0, value_scale=0.5, tree="random")
+    x = W.make_inputs(cfg, rng)
+    x["parent"] = deep_tree(rng, 128)
+    for qf in (0, 64, 100, 127):
+        say(f"[frontier] n=128 q_first={qf}")
+        sub = dict(x, q=x["q"][qf:], q_first=qf)
+        check_close(gpu_attn(sub), ref_attn(sub, cfg["n_kv_heads"]), "bf16", f"n=128 q_first {qf}")
+
+
+@pytest.mark.parametrize("head_dim", [64, 128])
+def test_mask_probe_past_64_nodes(head_dim):
+    """Each node's output spells its visible set over 128 tree nodes (the
+    second ancestor word included)."""
+    n = head_dim
+    cfg = W.config("llama3_8b_verify" if head_dim == 128 else "draft_loop_1b", n_tree=n, prefix=777,
+                   capacity=777 + n + 16)
+    parent = deep_tree(np.random.default_rng(head_dim), n)
+    say(f"[mask-probe] {n} nodes, head_dim {head_dim}")
+    x = W.mask_probe_inputs(cfg, parent)
+    got = gpu_attn(x)
+    check_close(got, ref_attn(x, cfg["n_kv_heads"]), cfg["dtype"], f"probe {n}")
+    for i in range(n):
+        vis = oracle.ancestors_inclusive(parent, i)
+        want = np.zeros(head_dim)
+        want[vis] = 1.0 / len(vis)
+        assert np.abs(got[i, :, :] - want).max() < 2e-2, i
+
+
 @pytest.mark.parametrize("name", ["tiny_fp32", "llama3_8b_verify", "llama3_70b_verify", "draft_loop_1b"])
 def test_mask_probe(name):
     """Outputs that spell the visible set of every node: 1/|A| on A, ~0 elsewhere."""
@@ -123,10 +154,26 @@ def test_peaked_softmax_unscaled_inputs():
     check_close(gpu_attn(x), ref_attn(x, cfg["n_kv_heads"]), "bf16", "peaked")
 
 
+def deep_tree(rng, n):
+    """A random tree whose root paths run past 64 nodes (each node's parent
+    is one of the three nodes just before it)."""
+    return [-1] + [max(-1, i - 1 - int(rng.integers(0, 3))) for i in range(1, n)]
+
+
 def edge_cases():
     rng = np.random.default_rng(5)
     rnd = lambda n: [-1] + [int(rng.integers(-1, i)) for i in range(1, n)]  # noqa: E731
     return {
+        # more than 64 nodes: two ancestor words per node
+        "chain128_ragged": (dict(n_q_heads=8, n_kv_heads=2, head_dim=64, dtype="bf16", prefix=37),
+                            [-1] + list(range(127))),
+        "forest128_no_prefix": (dict(n_q_heads=4, n_kv_heads=2, head_dim=128, dtype="bf16", prefix=0), [-1] * 128),
+        "random100_gqa3": (dict(n_q_heads=12, n_kv_heads=4, head_dim=128, dtype="bf16", prefix=1000), rnd(100)),
+        "deep128_gqa16": (dict(n_q_heads=16, n_kv_heads=1, head_dim=64, dtype="bf16", prefix=3000), deep_tree(rng, 128)),
+        "deep65_split": (dict(n_q_heads=8, n_kv_heads=8, head_dim=128, dtype="bf16", prefix=9000), deep_tree(rng, 65)),
+        "f32_random100": (dict(n_q_heads=2, n_kv_heads=1, head_dim=64, dtype="f32", prefix=300), rnd(100)),
+        "f32_d128_chain128": (dict(n_q_heads=4, n_kv_heads=2, head_dim=128, dtype="f32", prefix=50),
+                              [-1] + list(range(127))),
         "root_only": (dict(n_q_heads=8, n_kv_heads=2, head_dim=128, dtype="bf16", prefix=100), [-1]),
         "chain64_ragged": (dict(n_q_heads=8, n_kv_heads=2, head_dim=64, dtype="bf16", prefix=37),
                            [-1] + list(range(63))),
@@ -254,6 +301,18 @@ def test_reroot_all_80_layers_target_and_draft_side():
     path = W.draft_path(rng, parent)
     reroot_case(cfg, cfg["layers"], rng, path, [], parent)
     reroot_case(cfg, cfg["layers"], rng, path, W.descendants(parent, path[-1]), parent)
+
+
+def test_reroot_past_64_nodes():
+    """A 128-node tree whose accepted path is longer than 64 nodes."""
+    cfg = W.config("draft_loop_1b", prefix=300, capacity=300 + 128 + 8)
+    rng = np.random.default_rng(128)
+    parent = deep_tree(rng, 128)
+    deepest = max(range(128), key=lambda i: len(oracle.ancestors_inclusive(parent, i)))
+    chain = oracle.ancestors_inclusive(parent, deepest)
+    path = chain[:70]
+    reroot_case(cfg, 3, rng, path, W.descendants(parent, path[-1]), parent)
+    reroot_case(cfg, 3, rng, path, [], parent)
 
 
 def test_reroot_then_attend_equals_attend_on_gpu():

@@ -82,14 +82,21 @@ def test_ragged_vocab_sizes(dtype, vocab):
         check(x["logits"], x["tokens"], parent, f"vocab {vocab} strided", stride_pad=pad)
 
 
-@pytest.mark.parametrize("shape", ["root_only", "chain64", "forest64", "random64", "strided"])
+def _deep_parent(rng, n):
+    return [-1] + [max(-1, i - 1 - int(rng.integers(0, 3))) for i in range(1, n)]
+
+
+@pytest.mark.parametrize("shape", ["root_only", "chain64", "forest64", "random64", "strided", "chain128",
+                                   "forest128", "random128", "deep128", "deep100"])
 def test_tree_shapes(shape):
     rng = np.random.default_rng(zlib.crc32(shape.encode()))
     parent = {"root_only": [], "chain64": [-1] + list(range(63)), "forest64": [-1] * 64,
-              "random64": _rand_parent(rng, 64), "strided": _rand_parent(rng, 40)}[shape]
+              "random64": _rand_parent(rng, 64), "strided": _rand_parent(rng, 40),
+              "chain128": [-1] + list(range(127)), "forest128": [-1] * 128, "random128": _rand_parent(rng, 128),
+              "deep128": _deep_parent(rng, 128), "deep100": _deep_parent(rng, 100)}[shape]
     cfg = dict(seed=1, vocab=5000, dtype="bf16")
     say(f"[verify] shape {shape} n={len(parent)}")
-    for accept in (0.5, 1.0):
+    for accept in (0.5, 0.97, 1.0):
         x = W.make_verify_inputs(cfg, parent, rng, accept=accept)
         check(x["logits"], x["tokens"], parent, f"{shape} accept={accept}", stride_pad=24 if shape == "strided" else 0)
 
@@ -123,7 +130,7 @@ def test_ties_signed_zeros_and_infinities(dtype):
 def test_repeat_calls_reuse_the_workspace():
     """Calls of different shapes in a row on one workspace; each must match."""
     rng = np.random.default_rng(3)
-    ws = torch.zeros(8192, dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(16384, dtype=torch.uint8, device=DEV)
     for k, (n, vocab, dtype) in enumerate([(64, 128256, "bf16"), (3, 100, "f32"), (0, 80, "bf16"),
                                            (64, 152064, "bf16"), (17, 9000, "f32"), (64, 128256, "bf16")]):
         parent = _rand_parent(rng, n)

@@ -41,16 +41,29 @@ def test_status_strings():
 def test_ancestor_bits_match_oracle_walk():
     rng = np.random.default_rng(0)
     trees = [c["parent"] for c in pins.load_golden("mask_visible_sets.json")["cases"]]
-    trees += [[-1] + [int(rng.integers(-1, i)) for i in range(1, n)] for n in (1, 2, 17, 63, 64)]
+    trees += [[-1] + [int(rng.integers(-1, i)) for i in range(1, n)] for n in (1, 2, 17, 63, 64, 65, 100, 128)]
+    trees += [[-1] + list(range(127)), [-1] * 128]
     for parent in trees:
         bits = ta.tree_ancestor_bits(parent)
         for i, b in enumerate(bits):
-            assert [j for j in range(64) if (b >> j) & 1] == oracle.ancestors_inclusive(parent, i)
+            assert [j for j in range(128) if (b >> j) & 1] == oracle.ancestors_inclusive(parent, i)
+
+
+def test_one_word_ancestor_bits_match_the_two_word_sets_up_to_64_nodes():
+    rng = np.random.default_rng(1)
+    for n in (1, 9, 64):
+        parent = [-1] + [int(rng.integers(-1, i)) for i in range(1, n)]
+        par, _ = ta._i32(parent)
+        one = (ctypes.c_uint64 * n)()
+        assert ta.lib().ta_tree_ancestor_bits(par, n, one) == ta.TA_OK
+        assert list(one) == ta.tree_ancestor_bits(parent)
+    par, _ = ta._i32([-1] * 65)
+    assert ta.lib().ta_tree_ancestor_bits(par, 65, (ctypes.c_uint64 * 65)()) == ta.TA_ERR_UNSUPPORTED
 
 
 def test_ancestor_bits_reject_bad_trees():
     for bad, status in (([0], ta.TA_ERR_TREE), ([-1, 1], ta.TA_ERR_TREE), ([-1, 0, 5], ta.TA_ERR_TREE),
-                        ([-1] * 65, ta.TA_ERR_UNSUPPORTED)):
+                        ([-1] * 129, ta.TA_ERR_UNSUPPORTED)):
         with pytest.raises(ta.TreeAttnError) as e:
             ta.tree_ancestor_bits(bad)
         assert e.value.status == status
@@ -102,7 +115,7 @@ def _attn(desc, n_q_heads=64, prefix=8192, parent=None, q=FAKE, out=FAKE, ws=Non
     (dict(desc=_desc(dtype=7)), ta.TA_ERR_UNSUPPORTED),
     (dict(desc=_desc(), n_q_heads=60), ta.TA_ERR_UNSUPPORTED),
     (dict(desc=_desc(H=2), n_q_heads=64), ta.TA_ERR_UNSUPPORTED),   # 32 q heads per KV head
-    (dict(desc=_desc(), parent=[-1] * 65), ta.TA_ERR_UNSUPPORTED),
+    (dict(desc=_desc(), parent=[-1] * 129), ta.TA_ERR_UNSUPPORTED),
     (dict(desc=_desc(), prefix=8448 - 7), ta.TA_ERR_CAPACITY),
     (dict(desc=_desc(), prefix=-1), ta.TA_ERR_ARG),
     (dict(desc=_desc(), parent=[-1, 1]), ta.TA_ERR_TREE),
@@ -155,7 +168,7 @@ def test_workspace_and_split_plan():
 
 def test_kv_reroot_rejects_before_enqueueing():
     lib = ta.lib()
-    np_out = (ctypes.c_int32 * 64)()
+    np_out = (ctypes.c_int32 * 128)()
     npl = ctypes.c_int32(-7)
 
     def call(desc, P, parent, path, surv, new_parent=np_out, new_prefix=ctypes.byref(npl)):
@@ -194,7 +207,7 @@ def test_package_does_not_import_the_oracle():
 
 
 def _verify_call(logits=FAKE, dtype=ta.TA_BF16, vocab=1000, stride=1000, tokens=FAKE, parent=(-1, 0),
-                 choice=FAKE, result=FAKE, ws=FAKE, ws_len=8192):
+                 choice=FAKE, result=FAKE, ws=FAKE, ws_len=16384):
     par, n = ta._i32(parent)
     return ta.lib().ta_tree_verify(logits, dtype, vocab, stride, tokens, par, n, choice, result, ws, ws_len, None)
 
@@ -216,7 +229,7 @@ def _verify_call(logits=FAKE, dtype=ta.TA_BF16, vocab=1000, stride=1000, tokens=
     (dict(ws_len=16), ta.TA_ERR_ARG),
     (dict(ws=FAKE + 16), ta.TA_ERR_ARG),
     (dict(parent=(0,)), ta.TA_ERR_TREE),
-    (dict(parent=(-1,) * 65), ta.TA_ERR_UNSUPPORTED),
+    (dict(parent=(-1,) * 129), ta.TA_ERR_UNSUPPORTED),
 ])
 def test_tree_verify_rejects_before_enqueueing(kwargs, status):
     assert _verify_call(**kwargs) == status
@@ -225,9 +238,9 @@ def test_tree_verify_rejects_before_enqueueing(kwargs, status):
 
 def test_tree_verify_workspace_bytes():
     L = ta.lib()
-    sizes = {L.ta_tree_verify_workspace_bytes(n) for n in range(65)}
-    assert len(sizes) == 1 and 0 < sizes.pop() <= 8192
-    assert L.ta_tree_verify_workspace_bytes(65) == 0 and L.ta_tree_verify_workspace_bytes(-1) == 0
+    sizes = {L.ta_tree_verify_workspace_bytes(n) for n in range(129)}
+    assert len(sizes) == 1 and 0 < sizes.pop() <= 16384
+    assert L.ta_tree_verify_workspace_bytes(129) == 0 and L.ta_tree_verify_workspace_bytes(-1) == 0
 
 
 def _expand_call(logits=FAKE, dtype=ta.TA_BF16, vocab=1000, stride=1000, scores=FAKE, w=8, k=8,

@@ -29,7 +29,7 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "tree_attn.h")
 
 TA_OK, TA_ERR_ARG, TA_ERR_UNSUPPORTED, TA_ERR_CAPACITY, TA_ERR_TREE, TA_ERR_DEVICE = range(6)
 TA_F32, TA_BF16 = 0, 1
-MAX_TREE = 64
+MAX_TREE = 128
 
 
 class TreeAttnError(RuntimeError):
@@ -104,6 +104,8 @@ def lib():
             L.ta_set_split_wait_limit.argtypes = [ctypes.c_int32]
             L.ta_tree_ancestor_bits.restype = ctypes.c_int
             L.ta_tree_ancestor_bits.argtypes = [_I32P, ctypes.c_int32, _U64P]
+            L.ta_tree_ancestor_bitset.restype = ctypes.c_int
+            L.ta_tree_ancestor_bitset.argtypes = [_I32P, ctypes.c_int32, _U64P]
             L.ta_kv_reroot_plan.restype = ctypes.c_int
             L.ta_kv_reroot_plan.argtypes = [ctypes.c_int32, ctypes.c_int32, _I32P, ctypes.c_int32, _I32P,
                                             ctypes.c_int32, _I32P, ctypes.c_int32, _I32P, _I32P, _I32P]
@@ -174,7 +176,7 @@ def _workspace(device, nbytes, kind="attn"):
     with _ws_lock:
         ws = _workspaces.get(key)
         if ws is None or ws.numel() < nbytes:
-            ws = torch.zeros(max(nbytes, 1 << 20 if kind == "attn" else 8192), dtype=torch.uint8, device=device)
+            ws = torch.zeros(max(nbytes, 1 << 20 if kind == "attn" else 16384), dtype=torch.uint8, device=device)
             _workspaces[key] = ws
     return ws
 
@@ -328,11 +330,12 @@ def set_split_wait_limit(polls):
 
 
 def tree_ancestor_bits(parent):
-    """Host-only: bit j of entry i is set iff node j is i or an ancestor of i."""
+    """Host-only: bit j of entry i is set iff node j is i or an ancestor of i
+    (Python ints of up to 128 bits, from the two-word C bitsets)."""
     par, n = _i32(parent)
-    bits = (ctypes.c_uint64 * max(n, 1))()
-    _check(lib().ta_tree_ancestor_bits(par, n, bits))
-    return [bits[i] for i in range(n)]
+    words = (ctypes.c_uint64 * max(2 * n, 1))()
+    _check(lib().ta_tree_ancestor_bitset(par, n, words))
+    return [words[2 * i] | (words[2 * i + 1] << 64) for i in range(n)]
 
 
 def kv_reroot_plan(prefix_len, capacity, parent, accepted_path, surviving_nodes):

@@ -59,9 +59,25 @@ const char* ta_status_string(ta_status s) {
   return "unknown status";
 }
 
+static_assert(kMaxTree == TA_MAX_TREE, "tree size of the kernels and of the ABI");
+
+ta_status ta_tree_ancestor_bitset(const int32_t* parent, int32_t n_tree, uint64_t* words_out) {
+  clear_error();
+  if (n_tree > 0 && words_out == nullptr) return fail(TA_ERR_ARG, "words_out is null");
+  uint64_t lo[TA_MAX_TREE], hi[TA_MAX_TREE];
+  const ta_status st = ancestor_bits(parent, n_tree, lo, hi);
+  if (st != TA_OK) return st;
+  for (int32_t i = 0; i < n_tree; ++i) {
+    words_out[2 * i] = lo[i];
+    words_out[2 * i + 1] = hi[i];
+  }
+  return TA_OK;
+}
+
 ta_status ta_tree_ancestor_bits(const int32_t* parent, int32_t n_tree, uint64_t* bits_out) {
   clear_error();
-  return ancestor_bits(parent, n_tree, bits_out);
+  if (n_tree > 64) return fail(TA_ERR_UNSUPPORTED, "one word per node holds at most 64 nodes");
+  return ancestor_bits(parent, n_tree, bits_out, nullptr);
 }
 
 ta_status ta_kv_reroot_plan(int32_t prefix_len, int32_t capacity, const int32_t* parent,
@@ -120,7 +136,7 @@ ta_status ta_tree_attn_rows(const void* q, const ta_kv_cache* cache, int32_t lay
   if (layer < 0 || layer >= cache->n_layers) return fail(TA_ERR_ARG, "layer out of range");
   TreeAttnArgs a;
   std::memset(&a, 0, sizeof(a));
-  st = ancestor_bits(parent, n_tree, a.anc);
+  st = ancestor_bits(parent, n_tree, a.anc, a.anc_hi);
   if (st != TA_OK) return st;
   if (plan.rows_per_head == 0) return TA_OK;  // no query rows
   if (q == nullptr || out == nullptr) return fail(TA_ERR_ARG, "q or out is null");
@@ -184,7 +200,7 @@ ta_status ta_tree_verify(const void* logits, int32_t dtype, int64_t vocab, int64
   clear_error();
   VerifyArgs a;
   std::memset(&a, 0, sizeof(a));
-  ta_status st = ancestor_bits(parent, n_tree, a.anc);
+  ta_status st = ancestor_bits(parent, n_tree, a.anc, a.anc_hi);
   if (st != TA_OK) return st;
   const size_t es = dtype_bytes(dtype);
   if (es == 0) return fail(TA_ERR_UNSUPPORTED, "dtype must be TA_F32 or TA_BF16");

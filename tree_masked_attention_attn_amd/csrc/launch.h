@@ -8,6 +8,9 @@
 
 namespace ta {
 
+// Tree nodes per call (the C ABI's TA_MAX_TREE): two 64-bit ancestor words.
+constexpr int kMaxTree = 128;
+
 struct TreeAttnArgs {
   const void* q;            // [n_tree][n_q_heads][D]
   const void* k;            // layer base: [n_kv_heads][capacity][D]
@@ -39,7 +42,10 @@ struct TreeAttnArgs {
   // one stage more than split_stages when s < split_extra.
   int32_t split_stages;     // n_tiles / splits
   int32_t split_extra;      // n_tiles % splits
-  uint64_t anc[64];         // ancestor-or-self bitset per tree node
+  // Ancestor-or-self set of each tree node: anc[i] holds nodes 0..63,
+  // anc_hi[i] nodes 64..127 (zero for trees of up to 64 nodes).
+  uint64_t anc[kMaxTree];
+  uint64_t anc_hi[kMaxTree];
 };
 
 hipError_t launch_tree_attn(const TreeAttnArgs& a, int32_t dtype, int32_t head_dim,
@@ -54,13 +60,13 @@ struct RerootArgs {
   int32_t n_rows;           // rows to place: n_accepted + n_surviving
   int32_t dst0;             // first destination slot (= prefix_len)
   int32_t col_groups;       // column groups per plane (grid.y)
-  int32_t src[64];          // source slot of destination slot dst0 + k
+  int32_t src[kMaxTree];    // source slot of destination slot dst0 + k
 };
 
 hipError_t launch_kv_reroot(const RerootArgs& a, hipStream_t stream);
 
-// Rows of one verification: the virtual root and up to 64 tree nodes.
-constexpr int kMaxVerifyRows = 65;
+// Rows of one verification: the virtual root and up to kMaxTree nodes.
+constexpr int kMaxVerifyRows = kMaxTree + 1;
 // Bytes per row slot of the verification workspace (one slot per cache line
 // pair, so that the rows' atomics do not share lines).
 constexpr int kVerifySlot = 64;
@@ -77,8 +83,9 @@ struct VerifyArgs {
   char* ws;                 // workspace, zero between calls: the arrival count of
                             // rows at 0, then per row r at kVerifySlot * (1 + r)
                             // its 8-byte key and its 4-byte arrival count
-  uint64_t anc[64];         // ancestor-or-self bitset per tree node
-  int8_t parent[64];
+  uint64_t anc[kMaxTree];   // ancestor-or-self set per node: nodes 0..63
+  uint64_t anc_hi[kMaxTree];  // nodes 64..127
+  int8_t parent[kMaxTree];
 };
 
 hipError_t launch_tree_verify(const VerifyArgs& a, int32_t dtype, hipStream_t stream);

@@ -44,13 +44,17 @@ ta_status check_parent(const int32_t* parent, int32_t n) {
   return TA_OK;
 }
 
-ta_status ancestor_bits(const int32_t* parent, int32_t n, uint64_t* bits) {
+ta_status ancestor_bits(const int32_t* parent, int32_t n, uint64_t* lo, uint64_t* hi) {
   ta_status st = check_parent(parent, n);
   if (st != TA_OK) return st;
-  if (n > 0 && bits == nullptr) return fail(TA_ERR_ARG, "bits_out is null");
-  // parent[i] < i, so bits[parent[i]] is final when node i is reached.
-  for (int32_t i = 0; i < n; ++i)
-    bits[i] = (uint64_t{1} << i) | (parent[i] < 0 ? 0 : bits[parent[i]]);
+  if (n > 0 && lo == nullptr) return fail(TA_ERR_ARG, "bits_out is null");
+  if (n > 64 && hi == nullptr) return fail(TA_ERR_UNSUPPORTED, "more than 64 nodes need two words per node");
+  // parent[i] < i, so the sets of parent[i] are final when node i is reached.
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t p = parent[i];
+    lo[i] = (i < 64 ? uint64_t{1} << i : 0) | (p < 0 ? 0 : lo[p]);
+    if (hi != nullptr) hi[i] = (i >= 64 ? uint64_t{1} << (i - 64) : 0) | (p < 0 ? 0 : hi[p]);
+  }
   return TA_OK;
 }
 

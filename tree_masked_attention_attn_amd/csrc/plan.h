@@ -19,8 +19,9 @@ const char* last_error();
 // parent[i] in {-1} U [0, i) for every i < n.
 ta_status check_parent(const int32_t* parent, int32_t n);
 
-// bits[i] = bit i | bits[parent[i]] (root path of i, self included).
-ta_status ancestor_bits(const int32_t* parent, int32_t n, uint64_t* bits);
+// Root path of i, self included, as a 128-bit set split in two words:
+// lo[i] holds nodes 0..63, hi[i] nodes 64..127 (hi may be null when n <= 64).
+ta_status ancestor_bits(const int32_t* parent, int32_t n, uint64_t* lo, uint64_t* hi);
 
 // Validates a KV-cache descriptor (pointers may be null when `need_ptrs` is false).
 ta_status check_cache(const ta_kv_cache* c, bool need_ptrs);

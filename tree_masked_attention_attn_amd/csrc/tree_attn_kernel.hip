@@ -531,7 +531,8 @@ void tree_attn_kernel(const TreeAttnArgs a) {
   const bool row_ok = row < a.rows_per_head;
   const int node = row_ok ? div_small(row, a.group, a.group_rcp) : 0;  // query row (tree node q_first + node)
   const int head = g * a.group + (row_ok ? row - node * a.group : 0);
-  const uint64_t anc = row_ok ? a.anc[a.q_first + node] : 0;
+  const uint64_t anc = row_ok ? a.anc[a.q_first + node] : 0;        // tree nodes 0..63
+  const uint64_t anc_hi = row_ok ? a.anc_hi[a.q_first + node] : 0;  // tree nodes 64..127
 
   const T* kh = static_cast<const T*>(a.k) + (size_t)g * a.kv_head_stride;
   const T* vh = static_cast<const T*>(a.v) + (size_t)g * a.kv_head_stride;
@@ -571,7 +572,10 @@ void tree_attn_kernel(const TreeAttnArgs a) {
       for (int j = 0; j < 16 * kSub; ++j) {
         const int key = kb + kTile * (j >> 4) + 8 * ((j >> 2) & 3) + 4 * half + (j & 3);
         bool vis = key < a.prefix_len;
-        if (!vis && key < a.total_keys) vis = (anc >> (key - a.prefix_len)) & 1;
+        if (!vis && key < a.total_keys) {
+          const int t = key - a.prefix_len;
+          vis = ((t < 64 ? anc >> t : anc_hi >> (t - 64)) & 1) != 0;
+        }
         if (!vis) p[j] = kNegInf;
       }
     }
@@ -698,8 +702,8 @@ struct BfGeo {
   static constexpr int KOPS = CPR / 8;                // DMA instructions per wave per slot
   static constexpr int VRING = kRing * SLOT;          // the V ring follows the K ring
   static constexpr int QSTAGE0 = 3 * SLOT;            // Q rows 0-63 wait in K slot 3
-  static constexpr int ANC = 2 * kRing * SLOT;        // ancestor table (64 x u64) + DMA spill
-  static constexpr int QSTAGE1 = ANC + 1024;          // Q rows 64-127
+  static constexpr int ANC = 2 * kRing * SLOT;        // ancestor words: [2][kMaxTree] x u64
+  static constexpr int QSTAGE1 = ANC + 2048;          // Q rows 64-127
   static constexpr int LDS = QSTAGE1 + SLOT;
   static_assert(kBlockRows == 128 && CPR % 8 == 0, "layout");
   static_assert(LDS <= 160 * 1024, "LDS");
@@ -820,11 +824,14 @@ __device__ __forceinline__ void bf_dma_q_anc(unsigned lds, const TreeAttnArgs& a
       bf_dma16(r, lds + (h ? G::QSTAGE1 : G::QSTAGE0) + op * 1024, off);
     }
   if (wave == 0) {
-    // The arguments block sits at the start of the kernarg segment; its 512-byte
-    // ancestor table is read by lanes 0..31, lanes 32..63 fall out of range.
+    // The arguments block sits at the start of the kernarg segment; its two
+    // 1 KB ancestor tables (words of nodes 0..63, then of nodes 64..127) are
+    // adjacent and land in LDS as [2][kMaxTree] words.
+    static_assert(offsetof(TreeAttnArgs, anc_hi) == offsetof(TreeAttnArgs, anc) + kMaxTree * 8, "tables");
     const char* args = (const char*)__builtin_amdgcn_kernarg_segment_ptr();
-    const i32x4 ra = bf_rsrc(args + offsetof(TreeAttnArgs, anc), 64 * 8);
+    const i32x4 ra = bf_rsrc(args + offsetof(TreeAttnArgs, anc), 2 * kMaxTree * 8);
     bf_dma16(ra, lds + G::ANC, lane * 16);
+    bf_dma16(ra, lds + G::ANC + kMaxTree * 8, lane * 16 + kMaxTree * 8);
   }
 }
 
@@ -865,7 +872,7 @@ struct BfWave {
   float m_ref[NT], l_run[NT];
   float alpha[NT];        // rescale of O owed by the last softmax (applied before the next PV)
   bool pend;              // some row of the wave owes one
-  uint64_t anc[NT];
+  unsigned anc_at[NT];    // LDS address of the row's first ancestor word (the second is kMaxTree words on)
 };
 
 // Settle the rescale the last softmax owes O. Kept a real branch (the asm
@@ -951,13 +958,15 @@ __device__ __forceinline__ void bf_pv(BfWave<D, NT>& w, const bf16x8 (&vf)[2][D 
 }
 
 // Visibility of the 32 keys kb .. kb + 31 for a row whose ancestor-or-self
-// set is `anc`: bit i set iff key kb + i is a prefix key or one of the row's
-// tree nodes (anc has no bits past n_tree, so keys past the end are hidden).
-__device__ __forceinline__ uint32_t visible32(uint64_t anc, int kb, int prefix_len) {
+// set is (hi:lo), tree nodes 0..127: bit i set iff key kb + i is a prefix key
+// or one of the row's tree nodes (the set has no bits past n_tree, so keys
+// past the end are hidden).
+__device__ __forceinline__ uint32_t visible32(uint64_t lo, uint64_t hi, int kb, int prefix_len) {
   const int d = kb - prefix_len;  // key kb is tree node d when d >= 0
+  const unsigned __int128 set = (static_cast<unsigned __int128>(hi) << 64) | lo;
   uint32_t tree;
-  if (d >= 0) tree = d < 64 ? static_cast<uint32_t>(anc >> d) : 0u;
-  else tree = d > -32 ? static_cast<uint32_t>(anc << (-d)) : 0u;
+  if (d >= 0) tree = d < 2 * 64 ? static_cast<uint32_t>(set >> d) : 0u;
+  else tree = d > -32 ? static_cast<uint32_t>(lo << (-d)) : 0u;
   const uint32_t pre = d <= -32 ? ~0u : (d >= 0 ? 0u : ((1u << (-d)) - 1u));
   return pre | tree;
 }
@@ -972,7 +981,8 @@ __device__ __forceinline__ void bf_mask(const BfWave<D, NT>& w, float (&x)[NT][1
   if (kb + 32 > a.prefix_len) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const uint32_t vis = visible32(w.anc[nt], kb, a.prefix_len) >> (4 * half);  // then constant bit tests
+      const auto* set = (__attribute__((address_space(3))) const uint64_t*)(unsigned long)w.anc_at[nt];
+      const uint32_t vis = visible32(set[0], set[kMaxTree], kb, a.prefix_len) >> (4 * half);  // then constant bit tests
 #pragma unroll
       for (int j = 0; j < 16; ++j)
         if (!((vis >> (8 * (j >> 2) + (j & 3))) & 1u)) x[nt][j] = kNegInf;
@@ -1245,7 +1255,8 @@ void tree_attn_bf16_kernel(const TreeAttnArgs a) {
   for (int nt = 0; nt < NT; ++nt) {
     const int row = 32 * (NT * rg + nt) + l32;
     bf_read_k<D>(w.qf[nt], lds0 + (row < 64 ? G::QSTAGE0 : G::QSTAGE1), (row >> 5) & 1, lane);
-    w.anc[nt] = row_ok[nt] ? reinterpret_cast<const uint64_t*>(lds + G::ANC)[a.q_first + node[nt]] : 0;
+    // rows past the block's last row (never written out) read node 0's words
+    w.anc_at[nt] = lds0 + G::ANC + 8 * (row_ok[nt] ? a.q_first + node[nt] : 0);
   }
   f32x16 sc[NT];
   bf16x8 pp[NT][2];

@@ -65,11 +65,20 @@ __global__ __launch_bounds__(kThreads) void tree_verify_kernel(const VerifyArgs 
   const int64_t v0 = static_cast<int64_t>(blockIdx.x) * kThreads * kUnroll + tid;
   // Inputs of the path search, loaded early by every workgroup (only the
   // last one uses them) so that their latency hides under the logits': the
-  // drafted token, ancestor bitset and parent of node `lane`.
-  const bool live = wave == 0 && lane < a.n_tree;
-  const int tok = live ? a.tokens[lane] : 0;
-  const u64 anc = live ? a.anc[lane] : 0ull;
-  const int par = live ? a.parent[lane] : 0;
+  // drafted token, ancestor set (two words: nodes 0..63, 64..127) and parent
+  // of nodes `lane` (h = 0) and `lane + 64` (h = 1).
+  bool live[2];
+  int tok[2], par[2];
+  u64 anc_lo[2], anc_hi[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int i = lane + 64 * h;
+    live[h] = wave == 0 && i < a.n_tree;
+    tok[h] = live[h] ? a.tokens[i] : 0;
+    anc_lo[h] = live[h] ? a.anc[i] : 0ull;
+    anc_hi[h] = live[h] ? a.anc_hi[i] : 0ull;
+    par[h] = live[h] ? a.parent[i] : 0;
+  }
 
   // Each thread scans its elements in ascending index order and keeps the
   // first maximum; it starts from its first element's index with -inf, which
@@ -160,14 +169,28 @@ __global__ __launch_bounds__(kThreads) void tree_verify_kernel(const VerifyArgs 
   }
   __syncthreads();
   if (wave != 0) return;
-  const bool match = live && tok == s_choice[par + 1];
-  const u64 matched = __ballot(match);
-  const bool accepted = live && (anc & ~matched) == 0ull;
-  // deepest accepted node, lowest index among equally deep ones
-  const int best_node = wave_max_i32(accepted ? (__popcll(anc) << 8) | (255 - lane) : 0);
+  // matched[h]: ballot of the nodes 64 h + lane whose token is the target's
+  // choice at their parent
+  const u64 matched_lo = __ballot(live[0] && tok[0] == s_choice[par[0] + 1]);
+  const u64 matched_hi = __ballot(live[1] && tok[1] == s_choice[par[1] + 1]);
+  // deepest accepted node (all of its root path matched), lowest index
+  // among equally deep ones: the maximum of depth << 8 | (255 - node)
+  int node_key = 0;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const bool accepted = live[h] && (anc_lo[h] & ~matched_lo) == 0ull && (anc_hi[h] & ~matched_hi) == 0ull;
+    const int depth_h = __popcll(anc_lo[h]) + __popcll(anc_hi[h]);
+    if (accepted) node_key = max(node_key, (depth_h << 8) | (255 - (lane + 64 * h)));
+  }
+  const int best_node = wave_max_i32(node_key);
   const int depth = best_node >> 8;
   const int last = depth > 0 ? 255 - (best_node & 255) : -1;
-  const u64 path_bits = last >= 0 ? readlane_u64(anc, last) : 0ull;
+  u64 path_lo = 0, path_hi = 0;  // the last node's ancestor set
+  if (last >= 0) {
+    const int h = last >> 6, l = last & 63;
+    path_lo = readlane_u64(h ? anc_lo[1] : anc_lo[0], l);
+    path_hi = readlane_u64(h ? anc_hi[1] : anc_hi[0], l);
+  }
   // result = [m, bonus, path (root to leaf), -1 ...]: node j on the path goes
   // to position 2 + (number of path nodes below j); ancestors have lower
   // indices, so that is root-to-leaf order.
@@ -175,12 +198,17 @@ __global__ __launch_bounds__(kThreads) void tree_verify_kernel(const VerifyArgs 
     a.result[0] = depth;
     a.result[1] = s_choice[last + 1];
   }
-  if (live) {
-    const bool on_path = (path_bits >> lane) & 1ull;
-    const int below = __popcll(path_bits & ((1ull << lane) - 1ull));
-    if (on_path) a.result[2 + below] = lane;
-    // positions depth .. n-1 hold -1
-    if (lane >= depth) a.result[2 + lane] = -1;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    if (live[h]) {
+      const int j = lane + 64 * h;
+      const u64 below_mask = (1ull << lane) - 1ull;  // bits of this word below j
+      const bool on_path = ((h ? path_hi : path_lo) >> lane) & 1ull;
+      const int below = h ? __popcll(path_lo) + __popcll(path_hi & below_mask) : __popcll(path_lo & below_mask);
+      if (on_path) a.result[2 + below] = j;
+      // positions depth .. n-1 hold -1
+      if (j >= depth) a.result[2 + j] = -1;
+    }
   }
 }
 
