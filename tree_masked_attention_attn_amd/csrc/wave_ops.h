@@ -73,31 +73,34 @@ __device__ __forceinline__ float readlane_f32(float v, int lane) {
 
 // Maximum over the wave, returned to every lane (a uniform value): a
 // butterfly inside each row, then the row broadcasts carry the running
-// maximum on to lane 63.
-__device__ __forceinline__ u64 wave_max_u64(u64 k) {
-  u64 o;
-  o = dpp_u64<dpp::kXor1>(k);
-  k = o > k ? o : k;
-  o = dpp_u64<dpp::kXor2>(k);
-  k = o > k ? o : k;
-  o = dpp_u64<dpp::kRor4>(k);
-  k = o > k ? o : k;
-  o = dpp_u64<dpp::kRor8>(k);
-  k = o > k ? o : k;
-  o = dpp_u64<dpp::kBcast15, 0xA>(k);
-  k = o > k ? o : k;
-  o = dpp_u64<dpp::kBcast31, 0xC>(k);
-  k = o > k ? o : k;
-  return readlane_u64(k, 63);
+// maximum on to lane 63. Each step is one max with a DPP operand.
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ uint32_t dpp_max_u32(uint32_t k) {
+  // lanes of rows outside ROWS see 0, the identity of the max
+  return max(k, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(k), CTRL, ROWS, 0xF, false)));
 }
 
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t k) {
+  k = dpp_max_u32<dpp::kXor1>(k);
+  k = dpp_max_u32<dpp::kXor2>(k);
+  k = dpp_max_u32<dpp::kRor4>(k);
+  k = dpp_max_u32<dpp::kRor8>(k);
+  k = dpp_max_u32<dpp::kBcast15, 0xA>(k);
+  k = dpp_max_u32<dpp::kBcast31, 0xC>(k);
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(k), 63));
+}
+
+// 64-bit maximum as two 32-bit ones: the high words, then the low words of
+// the lanes that hold the highest high word.
+__device__ __forceinline__ u64 wave_max_u64(u64 k) {
+  const uint32_t hi = wave_max_u32(static_cast<uint32_t>(k >> 32));
+  const uint32_t lo = wave_max_u32(static_cast<uint32_t>(k >> 32) == hi ? static_cast<uint32_t>(k) : 0u);
+  return (static_cast<u64>(hi) << 32) | lo;
+}
+
+// Maximum of non-negative ints over the wave.
 __device__ __forceinline__ int wave_max_i32(int k) {
-  k = max(k, static_cast<int>(dpp_u32<dpp::kXor1>(static_cast<unsigned>(k))));
-  k = max(k, static_cast<int>(dpp_u32<dpp::kXor2>(static_cast<unsigned>(k))));
-  k = max(k, static_cast<int>(dpp_u32<dpp::kRor4>(static_cast<unsigned>(k))));
-  k = max(k, static_cast<int>(dpp_u32<dpp::kRor8>(static_cast<unsigned>(k))));
-  return max(max(__builtin_amdgcn_readlane(k, 0), __builtin_amdgcn_readlane(k, 16)),
-             max(__builtin_amdgcn_readlane(k, 32), __builtin_amdgcn_readlane(k, 48)));
+  return static_cast<int>(wave_max_u32(static_cast<uint32_t>(k)));
 }
 
 }  // namespace ta
