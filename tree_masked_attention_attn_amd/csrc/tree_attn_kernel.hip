@@ -1288,16 +1288,20 @@ void tree_attn_bf16_kernel(const TreeAttnArgs a) {
     // slots that nothing reads any more (K(j) and V(j-1) are consumed): every
     // steady iteration issues the same instructions, and no branch splits the
     // MFMAs.
+    // One buffer range per stream for the whole split, [its first key, the
+    // split's end): the stage's offset goes into the per-lane offset, so the
+    // range check still zeroes everything past the end, and no descriptor is
+    // rebuilt per iteration.
     const int end_keys = min(a.total_keys, t1 * 64);  // loads never reach the next split
+    const i32x4 rk = bf_rsrc(kh_ptr + (size_t)t0 * 64 * D, max(end_keys - t0 * 64, 0) * G::ROWB);
+    const i32x4 rv = bf_rsrc(vh_ptr + (size_t)t0 * 64 * D, max(end_keys - t0 * 64, 0) * G::ROWB);
     auto steady = [&](int j) {
-      const int k4 = (t0 + j + 4) * 64, v3 = (t0 + j + 3) * 64;
-      const i32x4 rk = bf_rsrc(kh_ptr + (size_t)k4 * D, max(end_keys - k4, 0) * G::ROWB);
-      const i32x4 rv = bf_rsrc(vh_ptr + (size_t)v3 * D, max(end_keys - v3, 0) * G::ROWB);
+      const int ko4 = koff + (j + 4) * G::SLOT, vo3 = voff + (j + 3) * G::SLOT;  // G::SLOT: bytes of 64 keys
       const unsigned ks4 = kslot(j + 4);
       const unsigned vs3 = vslot(j + 3);
       auto dma = [&](int i) {
-        if (i < G::KOPS) bf_dma16(rk, ks4 + (i * NW + wave) * 1024, koff, i * NW * 1024);
-        else bf_dma16(rv, vs3 + ((i - G::KOPS) * NW + wave) * 1024, voff, (i - G::KOPS) * NW * 1024);
+        if (i < G::KOPS) bf_dma16(rk, ks4 + (i * NW + wave) * 1024, ko4, i * NW * 1024);
+        else bf_dma16(rv, vs3 + ((i - G::KOPS) * NW + wave) * 1024, vo3, (i - G::KOPS) * NW * 1024);
       };
       bf_iter<MF, D, NT, true, true, true, 2 * G::KOPS>(w, sc, pp, vf, kslot(j + 1), vslot(j), kb_of(j), kh, lane,
                                                         a, dma);
