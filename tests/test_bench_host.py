@@ -1,0 +1,105 @@
+"""bench.py on the CPU: the one-GPU contract, the algorithmic work counts and
+the rocprofv3 summary tools (on synthetic profiler output). No GPU needed."""
+
+import csv
+import json
+import os
+import sqlite3
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused_before_touching_a_gpu():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "single MI355X" in r.stderr and r.stdout == ""
+
+
+@pytest.mark.parametrize("name", ["llama3_70b_verify", "llama3_70b_verify_bs8", "draft_expand_w8", "tiny_fp32"])
+def test_tree_attn_work_counts_visible_pairs_and_bytes(name):
+    cfg = W.config(name)
+    parent, _ = W.make_tree(cfg, np.random.default_rng(cfg["seed"]))
+    nbytes, flops, anc = bench.tree_attn_work(cfg, parent)
+    qf, n = cfg.get("q_first", 0), cfg["n_tree"]
+    want_anc = sum(len(oracle.ancestors_inclusive(parent, i)) for i in range(qf, n))
+    assert anc == want_anc
+    es = 4 if cfg["dtype"] == "f32" else 2
+    P, d, hq, hkv = cfg["prefix"], cfg["head_dim"], cfg["n_q_heads"], cfg["n_kv_heads"]
+    # every visible (row, key) pair: the whole prefix plus the root path, QK and PV
+    assert flops == 4 * d * hq * sum(P + len(oracle.ancestors_inclusive(parent, i)) for i in range(qf, n))
+    assert nbytes == 2 * hkv * d * es * (P + n) + 2 * (n - qf) * hq * d * es + 4 * n
+    if name == "llama3_70b_verify":
+        assert (nbytes, flops) == (35_913_984, 17_189_306_368)
+
+
+def test_reroot_verify_expand_byte_counts():
+    cfg = W.config("llama3_70b_verify")
+    # rows already in place move nothing
+    assert bench.reroot_bytes(cfg, [8192, 8193], 8192, n_layers=80) == 0
+    # one moved row: read + write, K and V, every KV head and layer
+    assert bench.reroot_bytes(cfg, [8195], 8192, n_layers=80) == 2 * 2 * 8 * 128 * 2 * 80
+    assert bench.verify_bytes(cfg, 64) == 65 * 128256 * 2 + 4 * 64 + 4 * 65 + 4 * 66
+    assert bench.expand_bytes(cfg, 8, 8) == 8 * 128256 * 2 + 4 * 8 + 12 * 8
+
+
+def _write_csv(path, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=list(rows[0]))
+        w.writeheader()
+        w.writerows(rows)
+
+
+def test_summary_of_kernel_stats_and_of_a_rocpd_database(tmp_path):
+    d = tmp_path / "stats"
+    d.mkdir()
+    _write_csv(d / "run_kernel_stats.csv", [
+        {"Name": "tree_attn_bf16_kernel<128, 1>", "Calls": 10, "TotalDurationNs": 300000, "AverageNs": 30000,
+         "MinNs": 29000, "MaxNs": 31000, "Percentage": 90.0}])
+    lines, _ = bench.summarize(str(d), "x.md", "cmd")
+    assert any("tree_attn_bf16_kernel" in l and "| 10 | 300.0 | 30.00 | 29.00 | 31.00 |" in l for l in lines)
+    db_dir = tmp_path / "db"
+    db_dir.mkdir()
+    con = sqlite3.connect(str(db_dir / "run_results.db"))
+    con.execute("create table kernels (name text, duration integer)")
+    con.executemany("insert into kernels values (?, ?)", [("tree_verify_kernel", 7000), ("tree_verify_kernel", 9000)])
+    con.commit()
+    con.close()
+    lines, _ = bench.summarize(str(db_dir), "y.md", "cmd")
+    assert any("tree_verify_kernel | 2 | 16.0 | 8.00 | 7.00 | 9.00 |" in l for l in lines)
+
+
+def test_traffic_record_scales_counters_by_the_copy_calibration(tmp_path, monkeypatch):
+    def counters(path, name, attn_kib, copy_kib):
+        path.mkdir()
+        rows = [{"Kernel_Name": "tree_attn_bf16_kernel", "Counter_Name": name, "Dispatch_Id": i,
+                 "Counter_Value": attn_kib} for i in range(3)]
+        rows += [{"Kernel_Name": "__amd_rocclr_copyBuffer", "Counter_Name": name, "Dispatch_Id": 10,
+                  "Counter_Value": copy_kib},
+                 {"Kernel_Name": "__amd_rocclr_copyBuffer", "Counter_Name": name, "Dispatch_Id": 11,
+                  "Counter_Value": 4.0}]  # a small upload: not the calibration copy
+        _write_csv(path / "run_counter_collection.csv", rows)
+
+    copy_kib = bench.COPY_BYTES / 1024
+    counters(tmp_path / "fetch", "FETCH_SIZE", 1000.0, copy_kib / 2)  # FETCH counts half the bytes
+    counters(tmp_path / "write", "WRITE_SIZE", 300.0, copy_kib)
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    args = type("A", (), {"traffic": (str(tmp_path / "fetch"), str(tmp_path / "write")),
+                          "config": "llama3_70b_verify", "command": "cmd"})()
+    bench.main_traffic(args)
+    text = open(bench.traffic_file(W.config("llama3_70b_verify"))).read()
+    rec = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
+    assert rec["copy_fetch_factor"] == 0.5 and rec["copy_write_factor"] == 1.0
+    assert rec["traffic_bytes"] == int((1000.0 / 0.5 + 300.0) * 1024)
+    assert rec["source_sha"] == bench.kernel_source_sha()
+    assert bench.load_traffic(W.config("llama3_70b_verify")) == rec["traffic_bytes"]

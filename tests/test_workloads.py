@@ -91,3 +91,29 @@ def test_mask_probe_layout():
     x = W.mask_probe_inputs(cfg, [-1, 0, 1])
     assert x["q"][..., 0].eq(16).all() and x["k"][0, :, :2048, 0].eq(-16).all()
     assert x["v"][0, 3, 2048 + 2, 2] == 1
+
+
+def test_verify_inputs_plant_one_maximum_per_row_and_follow_accept():
+    cfg = W.config("llama3_8b_verify", vocab=3000)
+    parent, _ = W.make_tree(cfg, np.random.default_rng(cfg["seed"]))
+    for accept, seed in ((1.0, 1), (0.0, 2)):
+        x = W.make_verify_inputs(cfg, parent, np.random.default_rng(seed), accept=accept)
+        logits = W.to_f64(x["logits"])
+        assert logits.shape == (len(parent) + 1, 3000) and x["tokens"].dtype == torch.int32
+        top = np.sort(logits, axis=1)
+        assert (top[:, -1] > top[:, -2]).all()  # a unique maximum, even after bf16 rounding
+        choice = logits.argmax(axis=1)
+        kids = W.children(parent)
+        for owner in [-1] + list(range(len(parent))):
+            c = [i for i in range(len(parent)) if parent[i] == owner] if owner < 0 else kids[owner]
+            hits = sum(int(x["tokens"][i]) == choice[owner + 1] for i in c)
+            assert hits == ((1 if c else 0) if accept == 1.0 else 0)
+
+
+def test_expand_inputs_are_seeded_and_shaped():
+    cfg = W.config("draft_expand_w8")
+    a = W.make_expand_inputs(cfg, 8, np.random.default_rng(3))
+    b = W.make_expand_inputs(cfg, 8, np.random.default_rng(3))
+    assert torch.equal(a["logits"], b["logits"]) and torch.equal(a["path_scores"], b["path_scores"])
+    assert a["logits"].shape == (8, 128256) and a["logits"].dtype == torch.bfloat16
+    assert a["path_scores"].dtype == torch.float32 and (a["path_scores"] < 0).all()
