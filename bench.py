@@ -100,6 +100,18 @@ def reroot_bytes(cfg, src_rows, prefix, n_layers=1):
     return 2 * moved * 2 * cfg["n_kv_heads"] * cfg["head_dim"] * es * n_layers
 
 
+def split_partial_bytes(cfg, splits):
+    """Bytes of split partials one tree_attn launch writes (and the merge
+    reads back once): per unit, 128 rows of (max, sum) fp32 pairs and O in
+    fp32 (fp32 caches) or row-normalised fp16 (bf16 caches). Overhead, not
+    algorithmic."""
+    if splits <= 1:
+        return 0
+    rows = cfg["n_q_heads"] // cfg["n_kv_heads"] * (cfg["n_tree"] - cfg.get("q_first", 0))
+    units = cfg["n_kv_heads"] * -(-rows // 128) * splits
+    return units * 128 * (8 + cfg["head_dim"] * (4 if cfg["dtype"] == "f32" else 2))
+
+
 def verify_bytes(cfg, n):
     """Algorithmic bytes of one tree_verify: every logits value once, the
     drafted tokens, the arg-max and result arrays."""
@@ -498,6 +510,7 @@ def main():
 
 
     nbytes, flops, anc = tree_attn_work(cfg, parent)
+    splits = ta.tree_attn_num_splits(sets[0]["k"], sets[0]["v"], cfg["n_q_heads"], P, cfg["n_tree"], qf)
     rr_bytes = reroot_bytes(cfg, src_rows, P)
     attn_mean = statistics.fmean(attn_us)
     rr_mean = statistics.fmean(reroot_us)
@@ -530,14 +543,14 @@ def main():
         "config": {"workload": cfg["name"], "n_q_heads": cfg["n_q_heads"], "n_kv_heads": cfg["n_kv_heads"],
                    "head_dim": cfg["head_dim"], "prefix_len": P, "n_tree": cfg["n_tree"], "q_first": qf,
                    "visible_tree_pairs": anc, "accepted_path": len(path), "survivors": len(surv),
-                   "rotated_sets": rotate, "splits": ta.tree_attn_num_splits(sets[0]["k"], sets[0]["v"],
-                                                                              cfg["n_q_heads"], P, cfg["n_tree"],
-                                                                              qf)},
+                   "rotated_sets": rotate, "splits": splits},
         "tree_attn": {"us_mean": round(attn_mean, 2), "us_p10": round(pct(attn_us, 10), 2),
                       "us_p50": round(pct(attn_us, 50), 2), "us_p90": round(pct(attn_us, 90), 2),
                       "us_launch_period_back_to_back": round(attn_b2b / K, 2),
                       "hot_cache_us_p50": round(hot_us, 2),
                       "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
+                      "split_partial_bytes_written": split_partial_bytes(cfg, splits),
+                      "split_partial_bytes_read": split_partial_bytes(cfg, splits),
                       "hbm_GBs": round(hbm_gbs, 1), "hbm_frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
                       "TFLOPs": round(tflops, 1), "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4)},
         "kv_reroot": {"us_mean": round(rr_mean, 2), "us_p50": round(pct(reroot_us, 50), 2),

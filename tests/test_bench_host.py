@@ -103,3 +103,12 @@ def test_traffic_record_scales_counters_by_the_copy_calibration(tmp_path, monkey
     assert rec["traffic_bytes"] == int((1000.0 / 0.5 + 300.0) * 1024)
     assert rec["source_sha"] == bench.kernel_source_sha()
     assert bench.load_traffic(W.config("llama3_70b_verify")) == rec["traffic_bytes"]
+
+
+def test_split_partial_bytes_match_the_traffic_excess_model():
+    cfg = W.config("llama3_70b_verify")
+    # 8 KV heads x 4 row blocks x 8 splits = 256 units of 128 rows, fp16 O + fp32 (max, sum)
+    assert bench.split_partial_bytes(cfg, 8) == 256 * 128 * (8 + 128 * 2)
+    assert bench.split_partial_bytes(cfg, 1) == 0
+    tiny = W.config("tiny_fp32")
+    assert bench.split_partial_bytes(tiny, 2) == 1 * 1 * 2 * 128 * (8 + 64 * 4)
