@@ -1212,13 +1212,13 @@ void tree_attn_bf16_kernel(const TreeAttnArgs a) {
   // areas, after Q has been read); iteration j >= 1 issues K(j+4), V(j+3).
   // Iteration j needs K(j+1) and V(j); each wait counts the DMA instructions
   // issued after the newest of those, which may stay in flight.
+  // The first burst carries only what the first two iterations read first
+  // (Q, the ancestors, K0, K1, V0); K2, V1 and V2 follow once Q and K0 have
+  // landed, so that those do not queue behind the whole chip's later stages.
   bf_dma_q_anc<D, NW>(lds0, a, g, rb, wave, lane);
-#pragma unroll
-  for (int j = 0; j < 3; ++j)
-    if (j < n) dma_k(j);
-#pragma unroll
-  for (int j = 0; j < 3; ++j)
-    if (j < n) dma_v(j);
+  dma_k(0);
+  if (n > 1) dma_k(1);
+  dma_v(0);
   // DMA instructions each wave issues per K (V) stage.
   constexpr int KO = G::KOPS, VO = G::KOPS;
   auto iter_ops = [&](int j) {  // DMA instructions iteration j < n - 1 issues
@@ -1243,8 +1243,13 @@ void tree_attn_bf16_kernel(const TreeAttnArgs a) {
   }
   w.pend = false;
 
-  // Q, the ancestors and K0 have landed: read Q and the ancestor bits, QK(0).
-  wait_vm_atmost(KO * ((n > 1) + (n > 2)) + VO * (1 + (n > 1) + (n > 2)));
+  // Q, the ancestors and K0 have landed (K1 and V0 may still be on the way):
+  // issue K2, V1, V2, then read Q and the ancestor bits, QK(0). Issue order:
+  // Q, K0, K1, V0, K2, V1, V2.
+  wait_vm_atmost(KO * (n > 1) + VO);
+  if (n > 2) dma_k(2);
+  if (n > 1) dma_v(1);
+  if (n > 2) dma_v(2);
   bf_barrier();
   // The first wave to get here on each SIMD issues its MFMAs before its
   // softmax in every iteration, the second one after (SIMD_ID: HW_ID bits 5:4).
@@ -1271,8 +1276,9 @@ void tree_attn_bf16_kernel(const TreeAttnArgs a) {
   // The pipeline, compiled once per order (each copy keeps its own registers).
   auto pipeline = [&](auto order) {
     constexpr bool MF = decltype(order)::value;
-    // Iteration 0: softmax(0), QK(1), read V(0); no PV yet. Needs K1 and V0.
-    wait_vm_atmost(VO * ((n > 1) + (n > 2)));
+    // Iteration 0: softmax(0), QK(1), read V(0); no PV yet. Needs K1 and V0
+    // (after V0 come K2, V1, V2).
+    wait_vm_atmost(KO * (n > 2) + VO * ((n > 1) + (n > 2)));
     bf_barrier();  // Q has been read by every wave: its staging slots are free
     if (3 < n) dma_k(3);
     if (4 < n) dma_k(4);
