@@ -260,7 +260,7 @@ ta_status ta_kv_reroot_plan(int32_t prefix_len, int32_t capacity, const int32_t*
 /*
  * How long a prefix split of ta_tree_attn waits for the other splits of its
  * row block before leaving its share of the merge to the last split to
- * arrive: `polls` polls of about 128 GPU cycles each (default 20000, about
+ * arrive: `polls` polls about 2048 GPU cycles apart (default 1000, about
  * 1 ms). Results do not depend on it: when every split of a row block runs at
  * once (the normal case on an otherwise idle GPU) each merges 1/splits of the
  * rows; a split that stops waiting leaves its rows to the last arrival, which

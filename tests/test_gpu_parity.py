@@ -346,7 +346,7 @@ def test_split_merge_when_splits_stop_waiting(polls):
         got = gpu_attn(x)
         again = gpu_attn(x)
     finally:
-        ta.set_split_wait_limit(20000)
+        ta.set_split_wait_limit(1000)  # the default
     ref = ref_attn(x, cfg["n_kv_heads"])
     check_close(got, ref, cfg["dtype"], f"give-up polls={polls}")
     check_close(again, ref, cfg["dtype"], f"give-up polls={polls}, second call")

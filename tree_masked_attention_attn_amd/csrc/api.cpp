@@ -18,9 +18,9 @@ using namespace ta;
 
 namespace {
 
-// Polls (of about 128 cycles each) a split waits for the other splits of its
-// row block before leaving its rows to the last arrival.
-std::atomic<int32_t> g_wait_polls{20000};
+// Polls (about 2048 cycles apart) a split waits for the other splits of its
+// row block before leaving its rows to the last arrival: about 1 ms.
+std::atomic<int32_t> g_wait_polls{1000};
 
 // floor(2^32 / d) + 1 (0 for d = 1): the kernels divide x < 2^17 by d < 2^15
 // as the high word of x times this (the product overshoots x / d by less
