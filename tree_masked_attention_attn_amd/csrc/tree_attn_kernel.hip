@@ -1259,7 +1259,10 @@ void tree_attn_bf16_kernel(const TreeAttnArgs a) {
   // softmax in every iteration, the second one after (SIMD_ID: HW_ID bits 5:4).
   int seen = 0;
   if (lane == 0) seen = atomicAdd(&s_pair[(__builtin_amdgcn_s_getreg(4 | (4 << 6) | (1 << 11))) & 3], 1);
-  const bool mfma_first = (__builtin_amdgcn_readfirstlane(seen) & 1) == 0;
+  // Which of the two takes the MFMA-first order: measured per head dim (the
+  // first to arrive for 128, the second for 64; the other way round costs
+  // 5% at 70B and 3% on the 64-wide draft shapes).
+  const bool mfma_first = (__builtin_amdgcn_readfirstlane(seen) & 1) == (D == 64 ? 1 : 0);
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int row = 32 * (NT * rg + nt) + l32;
