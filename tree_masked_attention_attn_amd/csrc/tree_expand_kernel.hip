@@ -75,8 +75,41 @@ __device__ __forceinline__ float to_float(T x) {
     return __uint_as_float(static_cast<uint32_t>(__builtin_bit_cast(uint16_t, x)) << 16);
 }
 
+// Keys inside one chunk. bf16 logits: the top 16 bits of the value's
+// orderable image (the low 16 are fixed by the sign) and the lower
+// in-chunk index (12 bits) fit one 32-bit word, so each selection round is
+// one 32-bit wave maximum; fp32 logits keep 64-bit (value, ~token) keys.
+template <typename T>
+using ChunkKey = std::conditional_t<std::is_same_v<T, float>, u64, uint32_t>;
+
+template <typename T>
+__device__ __forceinline__ ChunkKey<T> chunk_key(float f, uint32_t id, int local) {
+  if constexpr (std::is_same_v<T, float>)
+    return cand_key(f, id);
+  else
+    return (order_key(f) & 0xffff0000u) | static_cast<uint32_t>(kChunk - 1 - local);
+}
+
+// The 64-bit (value, ~token) key of a chunk key (zero stays zero).
+template <typename T>
+__device__ __forceinline__ u64 global_key(ChunkKey<T> k, int chunk) {
+  if constexpr (std::is_same_v<T, float>) {
+    return k;
+  } else {
+    if (k == 0) return 0ull;
+    const uint32_t hi = k & 0xffff0000u;
+    const uint32_t ok = hi | ((hi & 0x80000000u) ? 0u : 0xffffu);  // the orderable image's low half
+    const uint32_t id = static_cast<uint32_t>(chunk * kChunk + (kChunk - 1 - static_cast<int>(k & 0xfffu)));
+    return (static_cast<u64>(ok) << 32) | static_cast<u64>(~id);
+  }
+}
+
+__device__ __forceinline__ u64 wave_max_key(u64 k) { return wave_max_u64(k); }
+__device__ __forceinline__ uint32_t wave_max_key(uint32_t k) { return wave_max_u32(k); }
+
 template <typename T>
 __global__ __launch_bounds__(kThreads) void tree_expand_kernel(const ExpandArgs a) {
+  using CK = ChunkKey<T>;
   constexpr int EPV = 16 / sizeof(T);         // logits per 16-byte vector
   constexpr int NV = kPerThread / EPV;        // vectors per thread
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -97,7 +130,7 @@ __global__ __launch_bounds__(kThreads) void tree_expand_kernel(const ExpandArgs 
     if (vi < full_vecs) buf[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x) + vi);
   }
   float v[kPerThread];
-  u64 key[kPerThread];
+  CK key[kPerThread];
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     const int64_t vi = static_cast<int64_t>(chunk) * (kChunk / EPV) + j * kThreads + tid;
@@ -115,7 +148,9 @@ __global__ __launch_bounds__(kThreads) void tree_expand_kernel(const ExpandArgs 
         ok = true;
       }
       v[j * EPV + t] = f;
-      key[j * EPV + t] = ok ? cand_key(f, static_cast<uint32_t>(id)) : 0ull;
+      key[j * EPV + t] =
+          ok ? chunk_key<T>(f, static_cast<uint32_t>(id), static_cast<int>(id - static_cast<int64_t>(chunk) * kChunk))
+             : CK{0};
     }
   }
 
@@ -132,27 +167,27 @@ __global__ __launch_bounds__(kThreads) void tree_expand_kernel(const ExpandArgs 
 
   // The wave's K best keys: K rounds of a wave maximum over each lane's best
   // key below the last winner (keys are unique: they hold the token id).
-  auto best_below = [&](u64 lim) {
-    u64 b = 0;
+  auto best_below = [&](CK lim) {
+    CK b = 0;
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) b = (key[i] < lim && key[i] > b) ? key[i] : b;
     return b;
   };
-  __shared__ u64 s_key[4][kExpandMaxK];
+  __shared__ CK s_key[4][kExpandMaxK];
   __shared__ float s_m[4], s_s[4];
   // The lane's best and second-best keys: a winner moves on to its second
   // and only re-scans its keys when that one is taken too.
-  u64 cand = 0, alt = 0;
+  CK cand = 0, alt = 0;
 #pragma unroll
   for (int i = 0; i < kPerThread; ++i) {
-    const u64 q = key[i];
+    const CK q = key[i];
     alt = q > cand ? cand : (q > alt ? q : alt);
     cand = q > cand ? q : cand;
   }
 #pragma unroll
   for (int r = 0; r < kExpandMaxK; ++r) {
     if (r < K) {
-      const u64 w = wave_max_u64(cand);
+      const CK w = wave_max_key(cand);
       if (lane == 0) s_key[wave][r] = w;
       if (cand == w && w != 0) {
         cand = alt != 0 ? alt : best_below(w);
@@ -168,16 +203,17 @@ __global__ __launch_bounds__(kThreads) void tree_expand_kernel(const ExpandArgs 
   if (wave != 0) return;
 
   // Wave 0: the chunk's K best of the four waves' 4K, and its (max, sum).
-  u64 c4 = lane < 4 * K ? s_key[lane / K][lane % K] : 0ull;
-  u64 mine = 0;  // lane r keeps round r's winner
+  CK c4 = lane < 4 * K ? s_key[lane / K][lane % K] : CK{0};
+  CK mine_c = 0;  // lane r keeps round r's winner
 #pragma unroll
   for (int r = 0; r < kExpandMaxK; ++r) {
     if (r < K) {
-      const u64 w = wave_max_u64(c4);
-      if (lane == r) mine = w;
+      const CK w = wave_max_key(c4);
+      if (lane == r) mine_c = w;
       if (c4 == w) c4 = 0;
     }
   }
+  const u64 mine = global_key<T>(mine_c, chunk);
   float cm = s_m[0], cs = s_s[0];
 #pragma unroll
   for (int w = 1; w < 4; ++w) lse_merge(cm, cs, s_m[w], s_s[w]);
