@@ -668,6 +668,7 @@ void tree_attn_kernel(const TreeAttnArgs a) {
 //    prefix_len + n_tree fall outside the buffer range and arrive as zeros.
 // ============================================================================
 typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // NT: 32-row MFMA tiles per wave. A workgroup always covers 128 rows and both
@@ -844,7 +845,8 @@ __device__ __forceinline__ void bf_dma_q_anc(unsigned lds, const TreeAttnArgs& a
 // per input. Scores are finite or -inf.
 __device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
-__device__ __forceinline__ float max16(const float* p) {
+template <typename R>  // float[16] or f32x16
+__device__ __forceinline__ float max16(const R& p) {
   const float a = vmax(vmax(p[0], p[1]), p[2]);
   const float b = vmax(vmax(p[3], p[4]), p[5]);
   const float c = vmax(vmax(p[6], p[7]), p[8]);
@@ -853,7 +855,8 @@ __device__ __forceinline__ float max16(const float* p) {
   return vmax(vmax(vmax(a, b), c), vmax(vmax(d, e), p[15]));
 }
 
-__device__ __forceinline__ float sum16(const float* p) {  // fixed pairwise order
+template <typename R>  // float[16] or f32x16
+__device__ __forceinline__ float sum16(const R& p) {  // fixed pairwise order
   float a0 = (p[0] + p[1]) + (p[2] + p[3]);
   float a1 = (p[4] + p[5]) + (p[6] + p[7]);
   float a2 = (p[8] + p[9]) + (p[10] + p[11]);
@@ -975,13 +978,11 @@ __device__ __forceinline__ uint32_t visible32(uint64_t lo, uint64_t hi, int kb, 
   return pre | tree;
 }
 
-// Scores of one stage (keys kb .. kb + 31 of this half) copied out of the
-// accumulators, with tree keys that are not ancestors (and keys past the
-// end) set to -inf. The mask is a uniform branch taken only by stages that
-// reach the tree.
-template <int D, int NT>
-__device__ __forceinline__ void bf_mask(const BfWave<D, NT>& w, float (&x)[NT][16], int kb, int half,
-                                        const TreeAttnArgs& a) {
+// In the scores x of one stage (keys kb .. kb + 31 of this half), set tree
+// keys that are not ancestors of the row (and keys past the end) to -inf.
+// The mask is a uniform branch taken only by stages that reach the tree.
+template <int D, int NT, typename X>  // X: float[NT][16] or f32x16[NT]
+__device__ __forceinline__ void bf_mask(const BfWave<D, NT>& w, X& x, int kb, int half, const TreeAttnArgs& a) {
   if (kb + 32 > a.prefix_len) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -994,22 +995,20 @@ __device__ __forceinline__ void bf_mask(const BfWave<D, NT>& w, float (&x)[NT][1
   }
 }
 
-template <int D, int NT>
-__device__ __forceinline__ void bf_scores(const BfWave<D, NT>& w, const f32x16 (&sc)[NT], float (&x)[NT][16],
-                                          int kb, int half, const TreeAttnArgs& a) {
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) x[nt][j] = sc[nt][j];
-  bf_mask<D, NT>(w, x, kb, half, a);
-}
+// How softmax forms the row sum, measured per head dim (A/B on MI355X):
+// for 128, from the bf16 weights with v_dot2c, a serial chain left free to
+// overlap the MFMAs of the softmax-first wave (3% faster at 70B shapes);
+// for 64, whose MFMA block is half as long, as a pairwise fp32 tree of the
+// unrounded weights, finished before the MFMAs (the chain costs 2% there).
+template <int D>
+constexpr bool kBfDotSum = D == 128;
 
 // Online softmax of one stage: scores x (masked) -> bf16 weights pn. The
 // reference max is raised lazily (only when a score exceeds it by more than
 // 2^kSlack); the factors alpha that rescale O then wait in the wave state
 // until the next PV.
-template <int D, int NT>
-__device__ __forceinline__ void bf_softmax(BfWave<D, NT>& w, float (&x)[NT][16], bf16x8 (&pn)[NT][2], float c) {
+template <int D, int NT, typename X>  // X: float[NT][16] or f32x16[NT]
+__device__ __forceinline__ void bf_softmax(BfWave<D, NT>& w, X& x, bf16x8 (&pn)[NT][2], float c) {
   float mx[NT], nm[NT];
   // Row maxima over this lane's 16 keys, then over both lane halves.
 #pragma unroll
@@ -1040,11 +1039,27 @@ __device__ __forceinline__ void bf_softmax(BfWave<D, NT>& w, float (&x)[NT][16],
   for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) x[nt][j] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[nt][j], c, nm[nt]));
-    w.l_run[nt] = w.l_run[nt] * w.alpha[nt] + sum16(x[nt]);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int q = 0; q < 8; ++q) pn[nt][ks][q] = static_cast<__bf16>(x[nt][8 * ks + q]);
+    if constexpr (kBfDotSum<D>) {
+      // the bf16 weights that PV multiplies, two per instruction
+      // (v_dot2c_f32_bf16 against 1.0, fp32 accumulation)
+      float l = w.l_run[nt] * w.alpha[nt];
+      const bf16x2v one = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 v = pn[nt][ks];
+        l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one, l, false);
+        l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), one, l, false);
+        l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), one, l, false);
+        l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one, l, false);
+      }
+      w.l_run[nt] = l;
+    } else {
+      w.l_run[nt] = w.l_run[nt] * w.alpha[nt] + sum16(x[nt]);
+    }
   }
   w.pend = __ballot(bump_any) != 0;
 }
@@ -1059,8 +1074,10 @@ __device__ __forceinline__ void bf_mfma_block(BfWave<D, NT>& w, f32x16 (&sn)[NT]
   constexpr int NPV = PV ? 2 * (D / 32) * NT : 0;  // k-steps x head_dim tiles x row tiles
   constexpr int NQK = QK ? (D / 16) * NT : 0;      // k-steps x row tiles
   constexpr int NM = NPV + NQK;
+  if constexpr (QK) {
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) sn[nt] = f32x16{};
+    for (int nt = 0; nt < NT; ++nt) sn[nt] = f32x16{};
+  }
   static_assert(NOPS <= NM, "one DMA instruction per MFMA at most");
 #pragma unroll
   for (int i = 0; i < NM; ++i) {
@@ -1154,11 +1171,15 @@ __device__ __forceinline__ void bf_iter(BfWave<D, NT>& w, f32x16 (&sc)[NT], bf16
     }
   } else {
     bf16x8 pn[NT][2];
-    bf_scores<D, NT>(w, sc, x, kb, lane >> 5, a);
-    bf_softmax<D, NT>(w, x, pn, a.scale_log2);
+    // in place: the scores are dead once the weights exist, and QK below
+    // writes the next stage's into the same registers
+    bf_mask<D, NT>(w, sc, kb, lane >> 5, a);
+    bf_softmax<D, NT>(w, sc, pn, a.scale_log2);
     bf_pin_weights<NT>(pn);  // the softmax is done before the MFMAs
+    if constexpr (!kBfDotSum<D>) {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) bf_pin(w.l_run[nt]);
+      for (int nt = 0; nt < NT; ++nt) bf_pin(w.l_run[nt]);
+    }
     // K fragments only now (not live through the softmax); the PV MFMAs
     // cover their latency
     if constexpr (QK) bf_read_k<D>(kf, knext, kh, lane);
