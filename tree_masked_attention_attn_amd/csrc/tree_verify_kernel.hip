@@ -50,9 +50,10 @@ __device__ __forceinline__ float to_float(T x) {
 }
 
 // Vectors of 16 bytes per thread and chunk (kUnroll loads in flight per
-// thread): 16 KB chunks, 8 of a 128256-entry bf16 row, ~1000 workgroups for
-// 65 rows. Measured faster than 32, 64 or 256 KB chunks: the latency chain
-// after the loads is fixed, so the loads should finish as early as possible.
+// thread): 16 KB chunks, 16 of a 128256-entry bf16 row, 1040 workgroups for
+// 65 rows. Measured faster than 8, 32, 64 or 256 KB chunks and than 512- or
+// 1024-thread workgroups: the latency chain after the loads is fixed, so the
+// loads should finish as early as possible.
 constexpr int kUnroll = 4;
 
 template <typename T>
