@@ -283,6 +283,56 @@ def main_traffic(args):
     print(json.dumps(rec))
 
 
+def counter_summary(dirs, command, workload=""):
+    """Counter passes (rocprofv3 --pmc, CSV) over tree_attn: per-dispatch means
+    and rocprofv3's own derived utilisations. The CSV sums a counter's
+    instances, so GRBM_GUI_ACTIVE (one instance per XCD, where the derived
+    expressions take the maximum) is divided by the XCD count."""
+    means, info = {}, {}
+    for d in dirs:
+        _, agg = summarize(d, "", "")
+        for (k, c), v in agg.items():
+            if k == "tree_attn":
+                means.setdefault(c, []).append(v)
+        for r in _rows(d, "*agent_info.csv"):
+            if r.get("Name", "").startswith("gfx"):
+                info = r
+    m = {c: statistics.fmean(v) for c, v in means.items()}
+    xcc, cus, simds = int(info["Num_Xcc"]), int(info["Cu_Count"]), int(info["Simd_Count"])
+    gui = m["GRBM_GUI_ACTIVE"] / xcc
+    derived = []
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in m:
+        derived.append(("MfmaUtil (% of SIMD cycles, GPU-active basis)",
+                        100 * m["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * simds)))
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in m and "SQ_INSTS_MFMA" in m:
+        derived.append(("MFMA busy cycles per MFMA instruction", m["SQ_VALU_MFMA_BUSY_CYCLES"] / m["SQ_INSTS_MFMA"]))
+    if "SQ_VALU_MFMA_COEXEC_CYCLES" in m and "SQ_VALU_MFMA_BUSY_CYCLES" in m:
+        derived.append(("MFMA-busy cycles in which a VALU instruction also issued (%)",
+                        100 * m["SQ_VALU_MFMA_COEXEC_CYCLES"] / m["SQ_VALU_MFMA_BUSY_CYCLES"]))
+    if "SQ_LDS_IDX_ACTIVE" in m:
+        derived.append(("LDS indexed-access utilisation (% of CU cycles, GPU-active basis)", 100 * m["SQ_LDS_IDX_ACTIVE"] / (gui * cus)))
+    if "SQ_LDS_IDX_ACTIVE" in m and "SQ_LDS_BANK_CONFLICT" in m:
+        derived.append(("LDS bank-conflict cycles per conflict-free LDS cycle",
+                        m["SQ_LDS_BANK_CONFLICT"] / (m["SQ_LDS_IDX_ACTIVE"] - m["SQ_LDS_BANK_CONFLICT"])))
+    if "SQ_INSTS_VALU" in m and "SQ_INSTS_MFMA" in m:
+        derived.append(("VALU instructions per MFMA instruction", m["SQ_INSTS_VALU"] / m["SQ_INSTS_MFMA"]))
+    lines = ["# rocprofv3 counters: tree_attn" + (", " + workload if workload else ""), "", "Commands (from the repository root):", "", "```", command, "```",
+             "", f"Part: {info.get('Name', '?')}, {cus} CUs, {simds} SIMDs, {xcc} XCDs. Means per tree_attn dispatch "
+             "(all instances summed):", "", "| counter | value |", "|---|---|"]
+    lines += [f"| {c} | {v:.1f} |" for c, v in sorted(m.items())]
+    lines += ["", "Derived (rocprofv3's expressions; GRBM_GUI_ACTIVE per XCD):", "", "| metric | value |", "|---|---|"]
+    lines += [f"| {name} | {v:.3f} |" for name, v in derived]
+    return lines + [""], m, dict(derived)
+
+
+def main_counters(args):
+    out, dirs = args.counters[0], args.counters[1:]
+    lines, _, _ = counter_summary(dirs, args.command or "", args.config)
+    with open(out, "w") as f:
+        f.write("\n".join(lines))
+    print(f"wrote {out}")
+
+
 def run_extras(ta, torch, cfg, dev, parent, P, K, timed):
     """The labelled extras: verification, expansion, all-layer re-root."""
     # Verification of the same tree against the target's logits: rotated
@@ -397,6 +447,7 @@ def main():
     ap.add_argument("--no-extras", action="store_true", help="skip the labelled extras (verify, expand, all layers)")
     ap.add_argument("--summarize", nargs=2, metavar=("DIR", "OUT"))
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--counters", nargs="+", metavar="OUT DIR", help="summary file, then counter-pass directories")
     ap.add_argument("--command", default=None, help="command line recorded in a summary")
     args = ap.parse_args()
 
@@ -404,6 +455,8 @@ def main():
         return main_summarize(args)
     if args.traffic:
         return main_traffic(args)
+    if args.counters:
+        return main_counters(args)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the tree-attention path shards by KV head with no "

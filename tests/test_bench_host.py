@@ -112,3 +112,31 @@ def test_split_partial_bytes_match_the_traffic_excess_model():
     assert bench.split_partial_bytes(cfg, 1) == 0
     tiny = W.config("tiny_fp32")
     assert bench.split_partial_bytes(tiny, 2) == 1 * 1 * 2 * 128 * (8 + 64 * 4)
+
+
+def test_counter_summary_derives_rocprof_utilisations(tmp_path):
+    # two counter passes of 2 dispatches each; GRBM_GUI_ACTIVE comes once per XCD (summed by the CSV)
+    agent = [{"Name": "gfx950", "Num_Xcc": 8, "Cu_Count": 256, "Simd_Count": 1024}]
+
+    def counter_pass(name, values):
+        d = tmp_path / name
+        d.mkdir()
+        _write_csv(d / "run_agent_info.csv", agent)
+        rows = [{"Kernel_Name": "tree_attn_bf16_kernel<128, 1>", "Counter_Name": c, "Dispatch_Id": i,
+                 "Counter_Value": v} for i in range(2) for c, v in values.items()]
+        _write_csv(d / "run_counter_collection.csv", rows)
+        return str(d)
+
+    gui = 8 * 50_000.0  # 50k cycles per XCD
+    p1 = counter_pass("p1", {"GRBM_GUI_ACTIVE": gui, "SQ_VALU_MFMA_BUSY_CYCLES": 0.25 * 50_000 * 1024})
+    p2 = counter_pass("p2", {"GRBM_GUI_ACTIVE": gui, "SQ_INSTS_MFMA": 0.25 * 50_000 * 1024 / 32,
+                             "SQ_LDS_IDX_ACTIVE": 0.1 * 50_000 * 256, "SQ_LDS_BANK_CONFLICT": 0.0,
+                             "SQ_INSTS_VALU": 9 * 0.25 * 50_000 * 1024 / 32})
+    lines, means, derived = bench.counter_summary([p1, p2], "cmd", "llama3_70b_verify")
+    assert lines[0] == "# rocprofv3 counters: tree_attn, llama3_70b_verify"
+    assert means["GRBM_GUI_ACTIVE"] == gui
+    assert abs(derived["MfmaUtil (% of SIMD cycles, GPU-active basis)"] - 25.0) < 1e-9
+    assert derived["MFMA busy cycles per MFMA instruction"] == 32.0
+    assert abs(derived["LDS indexed-access utilisation (% of CU cycles, GPU-active basis)"] - 10.0) < 1e-9
+    assert derived["LDS bank-conflict cycles per conflict-free LDS cycle"] == 0.0
+    assert derived["VALU instructions per MFMA instruction"] == 9.0
