@@ -154,6 +154,27 @@ def test_peaked_softmax_unscaled_inputs():
     check_close(gpu_attn(x), ref_attn(x, cfg["n_kv_heads"]), "bf16", "peaked")
 
 
+@pytest.mark.parametrize("name", ["llama3_8b_verify", "draft_loop_1b"])
+def test_rising_scores_rescale_every_stage(name):
+    """Keys that grow along the cache: each 64-key stage raises every row's
+    maximum score by about 7, past the lazy maximum's slack (2^8, i.e. 5.5 in
+    score units), so the running output is rescaled on every stage (head_dim
+    128 and 64, whose row sums are formed differently)."""
+    cfg = W.config(name)
+    rng = np.random.default_rng(91)
+    x = W.make_inputs(cfg, rng)
+    d, T = cfg["head_dim"], x["prefix_len"] + cfg["n_tree"]
+    a = 7.0 / (64 * d / np.sqrt(d))  # score rise per key with q ~ 1
+    say(f"[rising] {name}: keys 0..{T - 1}, score slope {a * d / np.sqrt(d):.3f} per key")
+    t = torch.arange(T, dtype=torch.float32)[None, :, None]
+    k = x["k"].float()
+    k[0, :, :T, :] = a * t + 0.01 * torch.from_numpy(rng.standard_normal(size=(cfg["n_kv_heads"], T, d), dtype=np.float32))
+    x["k"] = k.to(x["k"].dtype)
+    q = 1.0 + 0.1 * torch.from_numpy(rng.standard_normal(size=tuple(x["q"].shape), dtype=np.float32))
+    x["q"] = q.to(x["q"].dtype)
+    check_close(gpu_attn(x), ref_attn(x, cfg["n_kv_heads"]), cfg["dtype"], "rising")
+
+
 def deep_tree(rng, n):
     """A random tree whose root paths run past 64 nodes (each node's parent
     is one of the three nodes just before it)."""
