@@ -1212,7 +1212,18 @@ void tree_attn_bf16_kernel(const TreeAttnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31;
   constexpr int NW = kBfWaves<NT>, RW = NW / 2;  // waves, row groups
-  const int rg = wave % RW, kh = wave / RW;      // row group, key half
+  // Row group and key half of the wave. Waves w and w + 4 share a SIMD. In a
+  // block of at most 64 query rows (half or more of it padding), each SIMD
+  // pairs a wave of real rows with a padding wave, and padding waves only
+  // load: every real wave then has its SIMD to itself. Otherwise a SIMD
+  // holds the two key halves of one row group.
+  const int block_rows = min(a.rows_per_head - rb * kBlockRows, kBlockRows);
+  const bool sparse = block_rows <= 64;
+  const int rg = sparse ? 2 * (wave >> 2) + ((wave & 3) >> 1) : wave % RW;
+  const int kh = sparse ? wave & 1 : wave / RW;
+  // no row of this wave's tiles is a query row: it issues its share of the
+  // loads and takes part in every barrier, nothing else
+  const bool idle = sparse && 32 * NT * rg >= block_rows;
   const __bf16* kh_ptr = static_cast<const __bf16*>(a.k) + (size_t)g * a.kv_head_stride;
   const __bf16* vh_ptr = static_cast<const __bf16*>(a.v) + (size_t)g * a.kv_head_stride;
   // LDS byte addresses (the space the DMA and the fragment reads take)
@@ -1294,7 +1305,7 @@ void tree_attn_bf16_kernel(const TreeAttnArgs a) {
   f32x16 sc[NT];
   bf16x8 pp[NT][2];
   bf16x8 vf[2][D / 32];
-  {
+  if (!idle) {
     bf16x8 kf[D / 16];
     bf_read_k<D>(kf, kslot(0), kh, lane);
     bf_qk<D, NT>(sc, kf, w);
@@ -1302,8 +1313,9 @@ void tree_attn_bf16_kernel(const TreeAttnArgs a) {
   auto kb_of = [&](int j) { return (t0 + j) * 64 + 32 * kh; };
 
   // The pipeline, compiled once per order (each copy keeps its own registers).
-  auto pipeline = [&](auto order) {
+  auto pipeline = [&](auto order, auto idle_tag) {
     constexpr bool MF = decltype(order)::value;
+    constexpr bool IDLE = decltype(idle_tag)::value;  // loads and barriers only
     // Iteration 0: softmax(0), QK(1), read V(0); no PV yet. Needs K1 and V0
     // (after V0 come K2, V1, V2).
     wait_vm_atmost(KO * (n > 2) + VO * ((n > 1) + (n > 2)));
@@ -1312,10 +1324,12 @@ void tree_attn_bf16_kernel(const TreeAttnArgs a) {
     if (4 < n) dma_k(4);
     if (3 < n) dma_v(3);
     auto no_dma = [](int) {};
-    if (n > 1)
-      bf_iter<MF, D, NT, true, false, true, 0>(w, sc, pp, vf, kslot(1), vslot(0), kb_of(0), kh, lane, a, no_dma);
-    else
-      bf_iter<MF, D, NT, false, false, true, 0>(w, sc, pp, vf, 0u, vslot(0), kb_of(0), kh, lane, a, no_dma);
+    if constexpr (!IDLE) {
+      if (n > 1)
+        bf_iter<MF, D, NT, true, false, true, 0>(w, sc, pp, vf, kslot(1), vslot(0), kb_of(0), kh, lane, a, no_dma);
+      else
+        bf_iter<MF, D, NT, false, false, true, 0>(w, sc, pp, vf, 0u, vslot(0), kb_of(0), kh, lane, a, no_dma);
+    }
     // Steady iteration j: needs K(j+1) and V(j), loads K(j+4) and V(j+3), one
     // DMA instruction after every few MFMAs. Past the split's last stage the
     // loads still run, with an empty range (zeros, no memory traffic), into
@@ -1337,8 +1351,13 @@ void tree_attn_bf16_kernel(const TreeAttnArgs a) {
         if (i < G::KOPS) bf_dma16(rk, ks4 + (i * NW + wave) * 1024, ko4, i * NW * 1024);
         else bf_dma16(rv, vs3 + ((i - G::KOPS) * NW + wave) * 1024, vo3, (i - G::KOPS) * NW * 1024);
       };
-      bf_iter<MF, D, NT, true, true, true, 2 * G::KOPS>(w, sc, pp, vf, kslot(j + 1), vslot(j), kb_of(j), kh, lane,
-                                                        a, dma);
+      if constexpr (IDLE) {
+#pragma unroll
+        for (int i = 0; i < 2 * G::KOPS; ++i) dma(i);
+      } else {
+        bf_iter<MF, D, NT, true, true, true, 2 * G::KOPS>(w, sc, pp, vf, kslot(j + 1), vslot(j), kb_of(j), kh, lane,
+                                                          a, dma);
+      }
     };
     for (int j = 1; j < n - 1; ++j) {
       // DMA instructions issued after the newest one needed: from j = 3 on,
@@ -1356,14 +1375,18 @@ void tree_attn_bf16_kernel(const TreeAttnArgs a) {
     if (n > 1) {
       TA_WAIT_VM(0);
       bf_barrier();
-      bf_iter<MF, D, NT, false, true, true, 0>(w, sc, pp, vf, 0u, vslot(n - 1), kb_of(n - 1), kh, lane, a,
-                                               no_dma);
+      if constexpr (!IDLE)
+        bf_iter<MF, D, NT, false, true, true, 0>(w, sc, pp, vf, 0u, vslot(n - 1), kb_of(n - 1), kh, lane, a,
+                                                 no_dma);
     }
-    bf_rescale<D, NT>(w);
-    bf_pv<D, NT>(w, vf, pp);
+    if constexpr (!IDLE) {
+      bf_rescale<D, NT>(w);
+      bf_pv<D, NT>(w, vf, pp);
+    }
   };
-  if (mfma_first) pipeline(std::true_type{});
-  else pipeline(std::false_type{});
+  if (idle) pipeline(std::true_type{}, std::true_type{});
+  else if (mfma_first) pipeline(std::true_type{}, std::false_type{});
+  else pipeline(std::false_type{}, std::false_type{});
   __syncthreads();  // every wave is done with the rings: reuse them below
 
   // Merge the two key halves: waves kh = 1 hand (m, l, O) to waves kh = 0
