@@ -1068,7 +1068,7 @@ __device__ __forceinline__ void bf_softmax(BfWave<D, NT>& w, X& x, bf16x8 (&pn)[
 // the previous iteration), then QK into sn, with the wave's NOPS DMA
 // instructions spread evenly between them: a stall on a busy load path then
 // costs nothing while the MFMA pipe is full.
-template <int D, int NT, bool QK, bool PV, int NOPS, typename Dma>
+template <int D, int NT, bool QK, bool PV, int NOPS, typename Dma, bool FENCE = true>
 __device__ __forceinline__ void bf_mfma_block(BfWave<D, NT>& w, f32x16 (&sn)[NT], const bf16x8 (&kf)[D / 16],
                                               const bf16x8 (&vf)[2][D / 32], const bf16x8 (&pp)[NT][2], Dma&& dma) {
   constexpr int NPV = PV ? 2 * (D / 32) * NT : 0;  // k-steps x head_dim tiles x row tiles
@@ -1090,9 +1090,9 @@ __device__ __forceinline__ void bf_mfma_block(BfWave<D, NT>& w, f32x16 (&sn)[NT]
     }
     if constexpr (NOPS > 0) {
       if ((i * NOPS) % NM == 0 && i * NOPS / NM < NOPS) {  // spread evenly, kept in place
-        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (FENCE) __builtin_amdgcn_sched_barrier(0);
         dma(i * NOPS / NM);
-        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (FENCE) __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
@@ -1145,14 +1145,31 @@ __device__ __forceinline__ void bf_pin_weights(bf16x8 (&p)[NT][2]) {
 // the workgroup barriers that start each iteration, the matrix core then
 // works for one wave while the vector ALU works for the other, instead of
 // both waves contending for the same unit at the same time.
-template <bool MFMA_FIRST, int D, int NT, bool QK, bool PV, bool VN, int NOPS, typename Dma>
+template <bool MFMA_FIRST, int D, int NT, bool QK, bool PV, bool VN, int NOPS, typename Dma, bool FREE = false>
 __device__ __forceinline__ void bf_iter(BfWave<D, NT>& w, f32x16 (&sc)[NT], bf16x8 (&pp)[NT][2],
                                         bf16x8 (&vf)[2][D / 32], unsigned knext, unsigned vcur, int kb,
                                         int kh, int lane, const TreeAttnArgs& a, Dma&& dma) {
   bf16x8 kf[D / 16];
   float x[NT][16];
   if constexpr (PV) bf_rescale<D, NT>(w);
-  if constexpr (MFMA_FIRST) {
+  if constexpr (FREE) {
+    // A wave alone on its SIMD: no partner to hand the units to, so the
+    // softmax is free to interleave with the MFMAs (mask first: its branch
+    // would split the block).
+    bf_mask<D, NT>(w, sc, kb, lane >> 5, a);
+    if constexpr (QK) bf_read_k<D>(kf, knext, kh, lane);
+    f32x16 sn[NT];
+    bf16x8 pn[NT][2];
+    bf_mfma_block<D, NT, QK, PV, NOPS, Dma, false>(w, sn, kf, vf, pp, dma);
+    bf_softmax<D, NT>(w, sc, pn, a.scale_log2);
+    if constexpr (VN) bf_read_v<D>(vf, vcur, kh, lane);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      pp[nt][0] = pn[nt][0];
+      pp[nt][1] = pn[nt][1];
+      if constexpr (QK) sc[nt] = sn[nt];
+    }
+  } else if constexpr (MFMA_FIRST) {
     // K fragments first: the PV MFMAs cover their latency
     if constexpr (QK) bf_read_k<D>(kf, knext, kh, lane);
     f32x16 sn[NT];
@@ -1193,7 +1210,7 @@ __device__ __forceinline__ void bf_iter(BfWave<D, NT>& w, f32x16 (&sc)[NT], bf16
   }
 }
 
-template <int D, int NT>
+template <int D, int NT, bool SPARSE>
 __global__ __launch_bounds__(kBfThreads<NT>)
 __attribute__((amdgpu_waves_per_eu(kBfWaves<NT> / 4, kBfWaves<NT> / 4)))  // waves per SIMD
 void tree_attn_bf16_kernel(const TreeAttnArgs a) {
@@ -1218,7 +1235,7 @@ void tree_attn_bf16_kernel(const TreeAttnArgs a) {
   // load: every real wave then has its SIMD to itself. Otherwise a SIMD
   // holds the two key halves of one row group.
   const int block_rows = min(a.rows_per_head - rb * kBlockRows, kBlockRows);
-  const bool sparse = block_rows <= 64;
+  const bool sparse = SPARSE || block_rows <= 64;
   const int rg = sparse ? 2 * (wave >> 2) + ((wave & 3) >> 1) : wave % RW;
   const int kh = sparse ? wave & 1 : wave / RW;
   // no row of this wave's tiles is a query row: it issues its share of the
@@ -1313,9 +1330,10 @@ void tree_attn_bf16_kernel(const TreeAttnArgs a) {
   auto kb_of = [&](int j) { return (t0 + j) * 64 + 32 * kh; };
 
   // The pipeline, compiled once per order (each copy keeps its own registers).
-  auto pipeline = [&](auto order, auto idle_tag) {
+  auto pipeline = [&](auto order, auto idle_tag, auto free_tag) {
     constexpr bool MF = decltype(order)::value;
     constexpr bool IDLE = decltype(idle_tag)::value;  // loads and barriers only
+    constexpr bool FR = decltype(free_tag)::value;    // see bf_iter
     // Iteration 0: softmax(0), QK(1), read V(0); no PV yet. Needs K1 and V0
     // (after V0 come K2, V1, V2).
     wait_vm_atmost(KO * (n > 2) + VO * ((n > 1) + (n > 2)));
@@ -1326,9 +1344,11 @@ void tree_attn_bf16_kernel(const TreeAttnArgs a) {
     auto no_dma = [](int) {};
     if constexpr (!IDLE) {
       if (n > 1)
-        bf_iter<MF, D, NT, true, false, true, 0>(w, sc, pp, vf, kslot(1), vslot(0), kb_of(0), kh, lane, a, no_dma);
+        bf_iter<MF, D, NT, true, false, true, 0, decltype(no_dma)&, FR>(w, sc, pp, vf, kslot(1), vslot(0), kb_of(0), kh, lane, a,
+                                                                     no_dma);
       else
-        bf_iter<MF, D, NT, false, false, true, 0>(w, sc, pp, vf, 0u, vslot(0), kb_of(0), kh, lane, a, no_dma);
+        bf_iter<MF, D, NT, false, false, true, 0, decltype(no_dma)&, FR>(w, sc, pp, vf, 0u, vslot(0), kb_of(0), kh, lane, a,
+                                                                      no_dma);
     }
     // Steady iteration j: needs K(j+1) and V(j), loads K(j+4) and V(j+3), one
     // DMA instruction after every few MFMAs. Past the split's last stage the
@@ -1355,8 +1375,8 @@ void tree_attn_bf16_kernel(const TreeAttnArgs a) {
 #pragma unroll
         for (int i = 0; i < 2 * G::KOPS; ++i) dma(i);
       } else {
-        bf_iter<MF, D, NT, true, true, true, 2 * G::KOPS>(w, sc, pp, vf, kslot(j + 1), vslot(j), kb_of(j), kh, lane,
-                                                          a, dma);
+        bf_iter<MF, D, NT, true, true, true, 2 * G::KOPS, decltype(dma)&, FR>(w, sc, pp, vf, kslot(j + 1), vslot(j),
+                                                                              kb_of(j), kh, lane, a, dma);
       }
     };
     for (int j = 1; j < n - 1; ++j) {
@@ -1376,17 +1396,24 @@ void tree_attn_bf16_kernel(const TreeAttnArgs a) {
       TA_WAIT_VM(0);
       bf_barrier();
       if constexpr (!IDLE)
-        bf_iter<MF, D, NT, false, true, true, 0>(w, sc, pp, vf, 0u, vslot(n - 1), kb_of(n - 1), kh, lane, a,
-                                                 no_dma);
+        bf_iter<MF, D, NT, false, true, true, 0, decltype(no_dma)&, FR>(w, sc, pp, vf, 0u, vslot(n - 1), kb_of(n - 1),
+                                                                        kh, lane, a, no_dma);
     }
     if constexpr (!IDLE) {
       bf_rescale<D, NT>(w);
       bf_pv<D, NT>(w, vf, pp);
     }
   };
-  if (idle) pipeline(std::true_type{}, std::true_type{});
-  else if (mfma_first) pipeline(std::true_type{}, std::false_type{});
-  else pipeline(std::false_type{}, std::false_type{});
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  if (idle) {
+    pipeline(T_{}, T_{}, F_{});
+  } else if constexpr (SPARSE) {
+    pipeline(T_{}, F_{}, T_{});  // every block sparse: a real wave is alone on its SIMD
+  } else {
+    if (mfma_first) pipeline(T_{}, F_{}, F_{});
+    else pipeline(F_{}, F_{}, F_{});
+  }
   __syncthreads();  // every wave is done with the rings: reuse them below
 
   // Merge the two key halves: waves kh = 1 hand (m, l, O) to waves kh = 0
@@ -1485,10 +1512,17 @@ hipError_t launch_tree_attn(const TreeAttnArgs& a, int32_t dtype, int32_t head_d
                             hipStream_t stream) {
   const dim3 grid(a.n_units), block(kThreads);
   if (dtype == 1) {
-    if (head_dim == 128)
-      hipLaunchKernelGGL((tree_attn_bf16_kernel<128, TA_BF16_NT>), grid, dim3(kBfThreads<TA_BF16_NT>), 0, stream, a);
-    else
-      hipLaunchKernelGGL((tree_attn_bf16_kernel<64, TA_BF16_NT>), grid, dim3(kBfThreads<TA_BF16_NT>), 0, stream, a);
+    // one row block of at most 64 query rows per KV head: the instance
+    // built for sparse blocks only
+    const bool sparse = a.rows_per_head <= 64;
+    const dim3 bf(kBfThreads<TA_BF16_NT>);
+    if (head_dim == 128) {
+      if (sparse) hipLaunchKernelGGL((tree_attn_bf16_kernel<128, TA_BF16_NT, true>), grid, bf, 0, stream, a);
+      else hipLaunchKernelGGL((tree_attn_bf16_kernel<128, TA_BF16_NT, false>), grid, bf, 0, stream, a);
+    } else {
+      if (sparse) hipLaunchKernelGGL((tree_attn_bf16_kernel<64, TA_BF16_NT, true>), grid, bf, 0, stream, a);
+      else hipLaunchKernelGGL((tree_attn_bf16_kernel<64, TA_BF16_NT, false>), grid, bf, 0, stream, a);
+    }
   } else {
     if (head_dim == 128)
       hipLaunchKernelGGL((tree_attn_kernel<float, 128>), grid, block, 0, stream, a);
