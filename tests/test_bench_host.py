@@ -107,8 +107,8 @@ def test_traffic_record_scales_counters_by_the_copy_calibration(tmp_path, monkey
 
 def test_split_partial_bytes_match_the_traffic_excess_model():
     cfg = W.config("llama3_70b_verify")
-    # 8 KV heads x 4 row blocks x 8 splits = 256 units of 128 rows, fp16 O + fp32 (max, sum)
-    assert bench.split_partial_bytes(cfg, 8) == 256 * 128 * (8 + 128 * 2)
+    # 8 KV heads x 4 row blocks x 8 splits = 256 units of 128 rows, fp32 O + fp32 (max, sum)
+    assert bench.split_partial_bytes(cfg, 8) == 256 * 128 * (8 + 128 * 4)
     assert bench.split_partial_bytes(cfg, 1) == 0
     tiny = W.config("tiny_fp32")
     assert bench.split_partial_bytes(tiny, 2) == 1 * 1 * 2 * 128 * (8 + 64 * 4)

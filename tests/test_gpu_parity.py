@@ -147,19 +147,53 @@ def test_mask_probe(name):
         assert np.abs(got[i, :, :] - want).max() < 2e-2, i
 
 
-def test_peaked_softmax_unscaled_inputs():
-    cfg = W.config("llama3_8b_verify")
-    say("[peaked] 8B shape with N(0,1) inputs")
+@pytest.mark.parametrize("name", ["llama3_8b_verify", "llama3_70b_verify_bs8", "draft_expand_w8"])
+def test_peaked_softmax_unscaled_inputs(name):
+    """N(0,1) inputs at head_dim 128 (or 64) give sharply peaked rows; the bs = 8
+    and draft-expansion shapes run the kernel instance built for blocks of at
+    most 64 query rows."""
+    cfg = W.config(name)
+    say(f"[peaked] {name} with N(0,1) inputs")
     x = W.make_inputs(cfg, np.random.default_rng(77), value_scale=1.0)
     check_close(gpu_attn(x), ref_attn(x, cfg["n_kv_heads"]), "bf16", "peaked")
 
 
 @pytest.mark.parametrize("name", ["llama3_8b_verify", "draft_loop_1b"])
+def test_split_partials_that_cancel(name):
+    """The split combine in fp32: with zero queries every visible key weighs
+    exactly 1, and the values are +c on the first half of the prefix and -c
+    on the second (plus N(0, 1/2) noise), so the splits' partial outputs are
+    large and of opposite sign while the true output is only the noise mean.
+    Partial rows rounded to 16 bits relative to their own magnitude would be
+    off by about 2^-11 c and miss the relative bound; fp32 partials meet it."""
+    cfg = W.config(name)
+    rng = np.random.default_rng(404)
+    x = W.make_inputs(cfg, rng)
+    P, d, T = x["prefix_len"], cfg["head_dim"], x["prefix_len"] + cfg["n_tree"]
+    c = 16.0
+    sign = torch.where(torch.arange(T) < P // 2, 1.0, -1.0)
+    sign[P:] = 0.0
+    v = x["v"].float()
+    noise = torch.from_numpy(rng.standard_normal(size=(cfg["n_kv_heads"], T, d), dtype=np.float32))
+    v[0, :, :T, :] = c * sign[None, :, None] + 0.5 * noise
+    x["v"] = v.to(x["v"].dtype)
+    x["q"] = torch.zeros_like(x["q"])
+    splits = ta.tree_attn_num_splits(x["k"], x["v"], cfg["n_q_heads"], P, cfg["n_tree"], x.get("q_first", 0))
+    say(f"[cancel] {name}: +/-{c} halves over {splits} splits")
+    assert splits > 1
+    ref = ref_attn(x, cfg["n_kv_heads"])
+    assert np.abs(ref).max() < 0.1 * c  # the halves cancel
+    check_close(gpu_attn(x), ref, cfg["dtype"], "cancelling splits")
+
+
+@pytest.mark.parametrize("name", ["llama3_8b_verify", "draft_loop_1b", "llama3_70b_verify_bs8", "draft_expand_w8"])
 def test_rising_scores_rescale_every_stage(name):
     """Keys that grow along the cache: each 64-key stage raises every row's
     maximum score by about 7, past the lazy maximum's slack (2^8, i.e. 5.5 in
     score units), so the running output is rescaled on every stage (head_dim
-    128 and 64, whose row sums are formed differently)."""
+    128 and 64, whose row sums are formed differently; the bs = 8 and
+    draft-expansion shapes run the sparse-block kernel instance, whose
+    softmax is free to move among its MFMAs)."""
     cfg = W.config(name)
     rng = np.random.default_rng(91)
     x = W.make_inputs(cfg, rng)

@@ -278,3 +278,42 @@ def test_tree_expand_workspace_bytes():
     assert L.ta_tree_expand_workspace_bytes(0) == 0 and L.ta_tree_expand_workspace_bytes(65) == 0
     sizes = [L.ta_tree_expand_workspace_bytes(w) for w in range(1, 65)]
     assert all(b > a for a, b in zip(sizes, sizes[1:])) and sizes[-1] <= 2 << 20
+
+
+def test_shapes_past_the_kernels_32_bit_ranges_are_refused():
+    """A KV head's [prefix | tree] bytes and one call's query bytes are
+    addressed through 32-bit buffer ranges, and work-unit ids are divided
+    exactly only below 2^17: such shapes fail validation before anything is
+    enqueued instead of being mis-addressed."""
+    lib = ta.lib()
+    par, n = ta._i32([-1] * 8)
+    keys_ok = (2 ** 31 - 1 - 2 ** 20) // 256 - 8  # bf16, head_dim 128: 256 bytes per key
+    big = _desc(H=1, C=keys_ok + 64)
+    assert lib.ta_tree_attn_rows(FAKE, ctypes.byref(big), 0, keys_ok + 1, par, n, 0, 4, FAKE, None, 0,
+                                 None) == ta.TA_ERR_UNSUPPORTED
+    assert b"32-bit" in lib.ta_last_error()
+    assert lib.ta_tree_attn_workspace_bytes(ctypes.byref(big), 4, keys_ok, n) > 0  # at the bound: planned
+    f32 = _desc(H=1, C=keys_ok + 64, dtype=ta.TA_F32)  # 512 bytes per key: half as many keys
+    assert lib.ta_tree_attn_workspace_bytes(ctypes.byref(f32), 4, keys_ok // 2 + 1, n) == 0
+    # 140000 KV heads of one query row each: one unit per head and no split
+    many = _desc(H=140000, C=64, D=64)
+    one, _ = ta._i32([-1])
+    assert lib.ta_tree_attn_rows(FAKE, ctypes.byref(many), 0, 8, one, 1, 0, 140000, FAKE, None, 0,
+                                 None) == ta.TA_ERR_UNSUPPORTED
+    assert b"work units" in lib.ta_last_error()
+    fewer = _desc(H=120000, C=64, D=64)
+    assert lib.ta_tree_attn_num_splits(ctypes.byref(fewer), 120000, 8, 1) == 1
+
+
+def test_default_workspaces_are_kept_per_stream():
+    """Two streams of one device must not share the split counters and
+    partial rows of one workspace; calls on one stream reuse theirs."""
+    a = ta._workspace("cpu", 4096, "attn", stream=11)
+    b = ta._workspace("cpu", 4096, "attn", stream=12)
+    assert a.data_ptr() != b.data_ptr()
+    assert ta._workspace("cpu", 4096, "attn", stream=11).data_ptr() == a.data_ptr()
+    assert ta._workspace("cpu", 4096, "verify", stream=11).data_ptr() != a.data_ptr()
+    grown = ta._workspace("cpu", 8 << 20, "attn", stream=11)
+    assert grown.numel() >= 8 << 20 and ta._workspace("cpu", 16, "attn", stream=11).data_ptr() == grown.data_ptr()
+    assert ta._workspace("cpu", 0, "attn", stream=11) is None
+

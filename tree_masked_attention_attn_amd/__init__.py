@@ -162,21 +162,28 @@ _workspaces = {}
 _ws_lock = threading.Lock()
 
 
-def _workspace(device, nbytes, kind="attn"):
-    """A zero-filled workspace per device and kind, grown on demand and kept
-    for reuse.
+def _workspace(device, nbytes, kind="attn", stream=None):
+    """A zero-filled workspace per (kind, device, stream), grown on demand and
+    kept for reuse.
 
     Every call leaves the counters ready for the next (arrival counts back at
-    zero), so reuse needs no clearing; it does assume calls on one device are
-    ordered (one stream). Attention and verification keep separate ones.
+    zero), so reuse needs no clearing. Calls on one stream are ordered, so they
+    may share one workspace; two streams of a device must not (their launches
+    may overlap and would share arrival counts and partial rows), hence the
+    stream in the key. ``stream`` is the HIP stream handle (an int); None
+    means torch's current stream of ``device``. Attention, verification and
+    expansion keep separate ones.
     """
     if nbytes == 0:
         return None
-    key = (kind, torch.device(device).index)
+    dev = torch.device(device)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    key = (kind, dev.type, dev.index, int(stream))
     with _ws_lock:
         ws = _workspaces.get(key)
         if ws is None or ws.numel() < nbytes:
-            ws = torch.zeros(max(nbytes, 1 << 20 if kind == "attn" else 16384), dtype=torch.uint8, device=device)
+            ws = torch.zeros(max(nbytes, 1 << 20 if kind == "attn" else 16384), dtype=torch.uint8, device=dev)
             _workspaces[key] = ws
     return ws
 
@@ -325,7 +332,7 @@ def kv_reroot(k_cache, v_cache, prefix_len, parent, accepted_path, surviving_nod
 
 
 def set_split_wait_limit(polls):
-    """Bound (in polls of ~128 GPU cycles) of the wait between prefix splits."""
+    """Bound (in polls about 2048 GPU cycles apart) of the wait between prefix splits."""
     lib().ta_set_split_wait_limit(int(polls))
 
 

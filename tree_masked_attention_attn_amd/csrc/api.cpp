@@ -128,6 +128,17 @@ ta_status ta_tree_attn_rows(const void* q, const ta_kv_cache* cache, int32_t lay
                             int32_t n_q_heads, void* out, void* workspace, size_t workspace_bytes,
                             void* stream) {
   clear_error();
+  return tree_attn_rows_impl(q, cache, layer, prefix_len, parent, n_tree, q_first, n_q_heads, out, workspace,
+                             workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace ta {
+
+ta_status tree_attn_rows_impl(const void* q, const ta_kv_cache* cache, int32_t layer, int32_t prefix_len,
+                              const int32_t* parent, int32_t n_tree, int32_t q_first, int32_t n_q_heads,
+                              void* out, void* workspace, size_t workspace_bytes, void* stream) {
   ta_status st = check_cache(cache, true);
   if (st != TA_OK) return st;
   AttnPlan plan;
@@ -183,6 +194,10 @@ ta_status ta_tree_attn_rows(const void* q, const ta_kv_cache* cache, int32_t lay
   if (e != hipSuccess) return device_error(e, "tree_attn launch");
   return TA_OK;
 }
+
+}  // namespace ta
+
+extern "C" {
 
 size_t ta_tree_verify_workspace_bytes(int32_t n_tree) {
   clear_error();

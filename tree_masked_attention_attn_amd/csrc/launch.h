@@ -6,6 +6,8 @@
 
 #include <cstdint>
 
+#include "tree_attn.h"
+
 namespace ta {
 
 // Tree nodes per call (the C ABI's TA_MAX_TREE): two 64-bit ancestor words.
@@ -50,6 +52,13 @@ struct TreeAttnArgs {
 
 hipError_t launch_tree_attn(const TreeAttnArgs& a, int32_t dtype, int32_t head_dim,
                             hipStream_t stream);
+
+// ta_tree_attn_rows without the error reset: validation, planning and the
+// launch, on a caller-owned workspace (api.cpp) or the library's static
+// scratch (noalloc.hip).
+ta_status tree_attn_rows_impl(const void* q, const ta_kv_cache* cache, int32_t layer, int32_t prefix_len,
+                              const int32_t* parent, int32_t n_tree, int32_t q_first, int32_t n_q_heads,
+                              void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 struct RerootArgs {
   char* k;                  // cache base (all layers)

@@ -91,6 +91,19 @@ ta_status plan_tree_attn(const ta_kv_cache* cache, int32_t n_q_heads, int32_t pr
     return fail(TA_ERR_CAPACITY, "prefix_len + n_tree = " +
                                      std::to_string(static_cast<int64_t>(prefix_len) + n_tree) +
                                      " exceeds capacity " + std::to_string(cache->capacity));
+  // The kernels address one KV head's [prefix | tree] rows, and the query
+  // rows of one call, through raw-buffer descriptors whose byte ranges and
+  // per-lane offsets are 32-bit (loads run up to four 64-key stages past a
+  // range's end, where the range check returns zeros); refuse shapes whose
+  // ranges could wrap instead of mis-addressing them.
+  const int64_t es = static_cast<int64_t>(dtype_bytes(cache->dtype));
+  const int64_t kMaxRange = INT32_MAX - (int64_t{1} << 20);
+  if ((static_cast<int64_t>(prefix_len) + n_tree) * cache->head_dim * es > kMaxRange)
+    return fail(TA_ERR_UNSUPPORTED, "prefix_len + n_tree = " +
+                                        std::to_string(static_cast<int64_t>(prefix_len) + n_tree) +
+                                        " keys of one KV head exceed the kernels' 32-bit byte range");
+  if (static_cast<int64_t>(n_tree - q_first) * n_q_heads * cache->head_dim * es > kMaxRange)
+    return fail(TA_ERR_UNSUPPORTED, "the query rows of one call exceed the kernels' 32-bit byte range");
   AttnPlan p;
   p.head_dim = cache->head_dim;
   p.group = group;
@@ -112,6 +125,12 @@ ta_status plan_tree_attn(const ta_kv_cache* cache, int32_t n_q_heads, int32_t pr
   int32_t cap = std::max(1, p.n_tiles / kMinTilesPerSplit);
   p.splits = std::max(1, std::min(std::min(want, cap), kMaxSplits));
   p.n_units = base_units * p.splits;
+  // The kernels split a workgroup id into (group, split) and a group into
+  // (KV head, row block) with a multiply-high division that is exact for
+  // dividends below 2^17.
+  if (p.n_units >= kMaxUnits)
+    return fail(TA_ERR_UNSUPPORTED, std::to_string(p.n_units) + " work units (KV heads x row blocks x splits) "
+                                    "exceed " + std::to_string(kMaxUnits - 1));
   if (p.splits > 1) {
     if (base_units > kMaxGroups)
       return fail(TA_ERR_UNSUPPORTED, "more than " + std::to_string(kMaxGroups) +
@@ -121,8 +140,8 @@ ta_status plan_tree_attn(const ta_kv_cache* cache, int32_t n_q_heads, int32_t pr
     p.ws_ml_offset = kCounterBytes;
     const size_t ml_bytes = units * kRowsPerBlock * 2 * sizeof(float);
     p.ws_o_offset = align_up(p.ws_ml_offset + ml_bytes, 256);
-    // partial rows: fp32 for fp32 caches, row-normalised fp16 for bf16 caches
-    const size_t o_bytes = units * kRowsPerBlock * p.head_dim * (cache->dtype == TA_BF16 ? 2 : 4);
+    // partial rows in fp32 for every cache dtype
+    const size_t o_bytes = units * kRowsPerBlock * p.head_dim * sizeof(float);
     p.ws_bytes = align_up(p.ws_o_offset + o_bytes, 256);
   }
   *plan = p;

@@ -43,15 +43,15 @@ struct AttnPlan {
   // earlier call where it expects a counter.
   size_t ws_cnt_offset = 0;    // int32 x4 per group: arrivals, pad, give-up bits, pad
   size_t ws_ml_offset = 0;     // fp32 (max, sum) pairs [units][kRowsPerBlock][2]
-  size_t ws_o_offset = 0;      // partial outputs [units][kRowsPerBlock][head_dim]: fp32, or fp16 for bf16
+  size_t ws_o_offset = 0;      // partial outputs [units][kRowsPerBlock][head_dim], fp32
   size_t ws_bytes = 0;
 };
 
 constexpr int32_t kKeyTile = 64;       // keys per LDS stage (two 32-key MFMA sub-tiles)
-constexpr int32_t kWaves = 4;          // waves per workgroup
-constexpr int32_t kRowsPerWave = 32;   // query rows per wave (one 32-wide MFMA N tile)
-constexpr int32_t kRowsPerBlock = kWaves * kRowsPerWave;
-constexpr int32_t kTargetUnits = 512;  // 2 workgroups per CU on a 256-CU part
+constexpr int32_t kTilesPerBlock = 4;  // 32-row MFMA tiles per row block (the fp32 kernel: one per wave)
+constexpr int32_t kRowsPerTile = 32;   // query rows per MFMA tile (one 32-wide MFMA N tile)
+constexpr int32_t kRowsPerBlock = kTilesPerBlock * kRowsPerTile;
+constexpr int32_t kTargetUnits = 512;  // 2 workgroups per CU on a 256-CU part (half that for one per CU)
 constexpr int32_t kMinTilesPerSplit = 2;
 // At most 16 splits per row block (the give-up word would have room for 32):
 // past 16, the hand-off and merge of the extra partials cost more than the
@@ -60,7 +60,8 @@ constexpr int32_t kMinTilesPerSplit = 2;
 // 10 to 25 percent).
 constexpr int32_t kMaxSplits = 16;
 constexpr int32_t kMaxGroups = 4096;   // (KV head, row block) groups with counters
-constexpr int32_t kGroupWords = 4;     // arrivals, departures, give-up bits, pad
+constexpr int32_t kMaxUnits = 1 << 17; // the kernels' index divisions are exact below this
+constexpr int32_t kGroupWords = 4;     // arrival count, unused, give-up bits, unused
 constexpr size_t kCounterBytes = kMaxGroups * kGroupWords * sizeof(int32_t);
 
 ta_status plan_tree_attn(const ta_kv_cache* cache, int32_t n_q_heads, int32_t prefix_len,

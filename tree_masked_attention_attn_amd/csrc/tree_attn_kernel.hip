@@ -6,29 +6,32 @@
 // holds the prefix contiguously with the tree tokens right after it. The
 // pages' kernel targets Hopper and hands partial results between thread
 // blocks without explicit barriers; here the same idea is a per-row-block
-// arrival counter (release/acquire at agent scope) and the last workgroup to
-// arrive merges the split results, so the whole call is one launch with no
-// grid barrier.
+// arrival count (device-scope atomics; the partial rows travel by
+// device-scope stores and loads), after which each split merges its own
+// slice of the block's rows, so the whole call is one launch with no grid
+// barrier.
 //
-// Work decomposition. One workgroup = 4 waves = 128 query rows of one KV head
-// (row r of a head is tree node r / G, query head g*G + r % G, so a GQA
-// group's rows share every K/V tile) times one contiguous range of 32-key
-// tiles (a "split" of [0, prefix_len + n_tree)). Splits exist to spread a few
-// KV heads over 256 CUs; their partial (max, sum, unnormalised output) rows go
-// to the workspace and are merged in split order, so results are
+// Work decomposition (both kernels). A work unit is one workgroup: one KV
+// head x one block of 128 of its query rows (row r of a head is frontier
+// node q_first + r / G, query head g*G + r % G, so a GQA group's rows share
+// every K/V tile) x one contiguous range of 64-key stages (a "split" of
+// [0, prefix_len + n_tree)). Splits spread the few KV heads over the 256 CUs;
+// their partial (reference max, sum, unnormalised output) rows go to the
+// workspace in fp32 and are merged in split order, so results are
 // deterministic for a given shape.
 //
-// Per tile: K (32 x D, row-major) and V (transposed to D x 32, keys permuted to
-// match the MFMA operand layout) are staged in LDS by all 256 threads; the
-// next tile's global loads are in flight while the current one is consumed.
-// Each wave computes S^T = K Q^T with MFMA (keys = M, its 32 rows = N,
-// head_dim = K), so after the product every lane holds 16 scores of ONE row:
-// the online softmax needs only a single cross-lane exchange (lane ^ 32) per
-// tile. Then O^T += V^T P^T with MFMA, whose accumulator again holds one row
-// per lane, so the running-max rescale is a per-lane scalar.
+// The fp32 kernel (the tiny fp32 shapes) stages K and V through registers
+// into LDS with 4 waves of 32 rows. The bf16 kernel (below, with its own
+// description) streams K and V by buffer-to-LDS DMA into rings of 64-key
+// slots and runs 8 waves, two per SIMD. Both compute S^T = K Q^T with MFMA
+// (keys = M, a wave's 32 rows = N, head_dim = K), so after the product every
+// lane holds 16 scores of ONE row and the online softmax needs a single
+// cross-lane exchange (lane ^ 32) per tile; O^T += V^T P^T keeps one row per
+// lane as well, so the running-max rescale is a per-lane scalar.
 //
-// Ancestor mask: one 64-bit word per row (bit j = tree node j visible), held
-// in a register; only tiles that reach past the prefix test it.
+// Ancestor mask: two 64-bit words per tree node (bit j = node j is the node
+// itself or one of its ancestors; nodes 0..63 and 64..127), passed in the
+// kernel arguments; only stages that reach past the prefix test them.
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
@@ -319,12 +322,11 @@ struct PartialSink {
   __amdgpu_buffer_rsrc_t o, ml;
 };
 
-// PT: element type of the partial rows (float, or _Float16 for the bf16 path).
-template <int D, typename PT>
+template <int D>
 __device__ __forceinline__ PartialSink partial_sink(const TreeAttnArgs& a, int u) {
   PartialSink k;
-  const char* o = reinterpret_cast<const char*>(a.ws_o) + (size_t)u * kBlockRows * D * sizeof(PT);
-  k.o = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(o), 0, kBlockRows * D * (int)sizeof(PT), 0x00020000);
+  const char* o = reinterpret_cast<const char*>(a.ws_o) + (size_t)u * kBlockRows * D * sizeof(float);
+  k.o = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(o), 0, kBlockRows * D * (int)sizeof(float), 0x00020000);
   k.ml = __builtin_amdgcn_make_buffer_rsrc(a.ws_ml + (size_t)u * kBlockRows, 0, kBlockRows * 8, 0x00020000);
   return k;
 }
@@ -334,30 +336,21 @@ __device__ __forceinline__ void put_partial(const PartialSink& k, int i, f32x4 v
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), k.o, i * 16, 0, kWriteThrough);
 }
 
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-
-// ... the same four values as fp16 (8 bytes)
-__device__ __forceinline__ void put_partial_h(const PartialSink& k, int i, f32x4 v) {
-  const f16x4 h = {static_cast<_Float16>(v[0]), static_cast<_Float16>(v[1]), static_cast<_Float16>(v[2]),
-                   static_cast<_Float16>(v[3])};
-  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, h), k.o, i * 8, 0, kWriteThrough);
-}
-
 // (reference max, sum) of block row r
 __device__ __forceinline__ void put_ml(const PartialSink& k, int r, float m, float l) {
   __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, make_float2(m, l)), k.ml, r * 8, 0, kWriteThrough);
 }
 
 // Merge rows [r0, r1) of row block `grp` from all splits and write them to
-// `out` (PT: element type of the partial rows). One memory round trip per
+// `out`. One memory round trip per
 // batch of splits: each thread loads, for its
 // (row, float4 of head_dim), every split's (max, sum) pair and partial in one
 // batch, then combines them online in split order (deterministic for a
 // given shape): M is the running max, acc and L are rescaled by 2^(M_old - M).
-template <typename T, typename PT, int D, int NTH>
+template <typename T, int D, int NTH>
 __device__ void merge_rows(const TreeAttnArgs& a, int grp, int g, int rb, int r0, int r1, int tid) {
   constexpr int C4 = D / 4;  // chunks of 4 values per row
-  using V4 = std::conditional_t<std::is_same_v<PT, float>, f32x4, f16x4>;
+  using V4 = f32x4;
   const int S = a.splits;
   const size_t u0 = (size_t)grp * S;
   // Device-scope loads (cache policy sc1), like the count that announced
@@ -396,12 +389,8 @@ __device__ void merge_rows(const TreeAttnArgs& a, int grp, int g, int rb, int r0
         const int sk = s0 + k;
         ml[k] = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(rm, (sk * kBlockRows + br) * 8, 0,
                                                                                 kWriteThrough));
-        if constexpr (std::is_same_v<PT, float>)
-          o[k] = __builtin_bit_cast(V4, __builtin_amdgcn_raw_buffer_load_b128(
-                                            rp, (sk * kBlockRows * C4 + pi) * 16, 0, kWriteThrough));
-        else
-          o[k] = __builtin_bit_cast(V4, __builtin_amdgcn_raw_buffer_load_b64(
-                                            rp, (sk * kBlockRows * C4 + pi) * 8, 0, kWriteThrough));
+        o[k] = __builtin_bit_cast(V4, __builtin_amdgcn_raw_buffer_load_b128(
+                                          rp, (sk * kBlockRows * C4 + pi) * 16, 0, kWriteThrough));
       }
 #pragma unroll
       for (int k = 0; k < MB; ++k) {
@@ -410,9 +399,7 @@ __device__ void merge_rows(const TreeAttnArgs& a, int grp, int g, int rb, int r0
         const float Mn = ok ? fmaxf(M, ml[k].x) : M;
         const float sa = M == kNegInf ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
         const float sb = ok ? __builtin_amdgcn_exp2f(ml[k].x - Mn) : 0.f;
-        const f32x4 x = {static_cast<float>(o[k][0]), static_cast<float>(o[k][1]), static_cast<float>(o[k][2]),
-                         static_cast<float>(o[k][3])};
-        acc = acc * sa + x * sb;
+        acc = acc * sa + o[k] * sb;
         L = L * sa + ml[k].y * sb;
         M = Mn;
       }
@@ -450,7 +437,7 @@ __device__ void merge_rows(const TreeAttnArgs& a, int grp, int g, int rb, int r0
 //    twice is written twice with the same bytes, and a bit left set for a
 //    later call only makes that call's last arrival merge a slice that is
 //    already complete.
-template <typename T, typename PT, int D, int NTH>
+template <typename T, int D, int NTH>
 __device__ void split_handoff(const TreeAttnArgs& a, int* s_flags, int* s_mask, int grp, int g, int rb,
                               int split, int tid) {
   // Every wave waits for its own partial stores to complete before the
@@ -493,7 +480,7 @@ __device__ void split_handoff(const TreeAttnArgs& a, int* s_flags, int* s_mask, 
   }
   __syncthreads();
   const int flag = *s_flags;
-  if (flag) merge_rows<T, PT, D, NTH>(a, grp, g, rb, div_small(split * kBlockRows, a.splits, a.splits_rcp),
+  if (flag) merge_rows<T, D, NTH>(a, grp, g, rb, div_small(split * kBlockRows, a.splits, a.splits_rcp),
                                       div_small((split + 1) * kBlockRows, a.splits, a.splits_rcp), tid);
   if (flag == 2) {
     if (tid == 0) *s_mask = static_cast<int>(others & ~(1u << split));
@@ -501,7 +488,7 @@ __device__ void split_handoff(const TreeAttnArgs& a, int* s_flags, int* s_mask, 
     const unsigned marked = static_cast<unsigned>(*s_mask);
     for (int j = 0; j < a.splits; ++j)
       if ((marked >> j) & 1u)
-        merge_rows<T, PT, D, NTH>(a, grp, g, rb, div_small(j * kBlockRows, a.splits, a.splits_rcp),
+        merge_rows<T, D, NTH>(a, grp, g, rb, div_small(j * kBlockRows, a.splits, a.splits_rcp),
                                   div_small((j + 1) * kBlockRows, a.splits, a.splits_rcp), tid);
   }
 }
@@ -632,7 +619,7 @@ void tree_attn_kernel(const TreeAttnArgs a) {
 
   // Publish this split's rows (reference max, sum, unnormalised output), then hand off.
   {
-    const PartialSink sink = partial_sink<D, float>(a, u);
+    const PartialSink sink = partial_sink<D>(a, u);
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -641,7 +628,7 @@ void tree_attn_kernel(const TreeAttnArgs a) {
                     f32x4{o[dt][4 * jq], o[dt][4 * jq + 1], o[dt][4 * jq + 2], o[dt][4 * jq + 3]});
     if (half == 0) put_ml(sink, rloc, m_ref, l_tot);
   }
-  split_handoff<T, float, D, kThreads>(a, &s_flags, &s_taken, grp, g, rb, split, tid);
+  split_handoff<T, D, kThreads>(a, &s_flags, &s_taken, grp, g, rb, split, tid);
 }
 
 // ============================================================================
@@ -1258,7 +1245,7 @@ void tree_attn_bf16_kernel(const TreeAttnArgs a) {
     bf_dma_slot<D, NW>(vslot(j), vh_ptr, (t0 + j) * 64, a.total_keys, voff, wave);
   };
 
-  if (tid < 4) s_pair[tid] = 0;
+  if (!SPARSE && tid < 4) s_pair[tid] = 0;
 
   // DMA issue order (j = stage index within the split): Q and ancestors, K0,
   // K1, K2, V0, V1, V2; iteration 0 issues K3, K4, V3 (over the Q staging
@@ -1306,8 +1293,10 @@ void tree_attn_bf16_kernel(const TreeAttnArgs a) {
   bf_barrier();
   // The first wave to get here on each SIMD issues its MFMAs before its
   // softmax in every iteration, the second one after (SIMD_ID: HW_ID bits 5:4).
+  // (The sparse-block instance runs one real wave per SIMD and has no order
+  // to choose.)
   int seen = 0;
-  if (lane == 0) seen = atomicAdd(&s_pair[(__builtin_amdgcn_s_getreg(4 | (4 << 6) | (1 << 11))) & 3], 1);
+  if (!SPARSE && lane == 0) seen = atomicAdd(&s_pair[(__builtin_amdgcn_s_getreg(4 | (4 << 6) | (1 << 11))) & 3], 1);
   // Which of the two takes the MFMA-first order: measured per head dim (the
   // first to arrive for 128, the second for 64; the other way round costs
   // 5% at 70B and 3% on the 64-wide draft shapes).
@@ -1473,37 +1462,26 @@ void tree_attn_bf16_kernel(const TreeAttnArgs a) {
           }
       }
     } else {
-      // Row-normalised fp16 partials: the stored values are O / g with g the
-      // row's largest |O|, in [-1, 1]; g moves into the (max, sum) pair
-      // (m + log2 g, l / g), so the merge formula is unchanged.
-      const PartialSink sink = partial_sink<D, _Float16>(a, u);
+      // fp32 partials (unnormalised O, reference max, row sum): the merge
+      // combines the splits in fp32, so partial outputs of opposite sign
+      // cancel without losing digits.
+      const PartialSink sink = partial_sink<D>(a, u);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const int t = NT * rg + nt;  // 32-row tile of the block
-        float gm = 0.f;
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) gm = vmax(gm, __builtin_fabsf(w.o[nt][dt][j]));
-        float g_lo = gm, g_hi = gm;
-        swap32(g_lo, g_hi);  // the row's values sit in lanes l32 and l32 + 32
-        gm = vmax(g_lo, g_hi);
-        const float f = gm > 0.f ? 1.f / gm : 1.f;
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
           for (int jq = 0; jq < 4; ++jq)
-            put_partial_h(sink, ((t * (D / 32) + dt) * 4 + jq) * 64 + lane,
-                          f32x4{w.o[nt][dt][4 * jq], w.o[nt][dt][4 * jq + 1], w.o[nt][dt][4 * jq + 2],
-                                w.o[nt][dt][4 * jq + 3]} * f);
-        if (half == 0)
-          put_ml(sink, 32 * t + l32, gm > 0.f ? w.m_ref[nt] + __builtin_amdgcn_logf(gm) : w.m_ref[nt],
-                 l_tot[nt] * f);
+            put_partial(sink, ((t * (D / 32) + dt) * 4 + jq) * 64 + lane,
+                        f32x4{w.o[nt][dt][4 * jq], w.o[nt][dt][4 * jq + 1], w.o[nt][dt][4 * jq + 2],
+                              w.o[nt][dt][4 * jq + 3]});
+        if (half == 0) put_ml(sink, 32 * t + l32, w.m_ref[nt], l_tot[nt]);
       }
     }
   }
   if (a.splits == 1) return;
-  split_handoff<__bf16, _Float16, D, kBfThreads<NT>>(a, &s_flags, &s_taken, grp, g, rb, split, tid);
+  split_handoff<__bf16, D, kBfThreads<NT>>(a, &s_flags, &s_taken, grp, g, rb, split, tid);
 }
 
 }  // namespace
