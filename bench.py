@@ -103,13 +103,12 @@ def reroot_bytes(cfg, src_rows, prefix, n_layers=1):
 def split_partial_bytes(cfg, splits):
     """Bytes of split partials one tree_attn launch writes (and the merge
     reads back once): per unit, 128 rows of (max, sum) fp32 pairs and O in
-    fp32 (fp32 caches) or row-normalised fp16 (bf16 caches). Overhead, not
-    algorithmic."""
+    fp32. Overhead, not algorithmic."""
     if splits <= 1:
         return 0
     rows = cfg["n_q_heads"] // cfg["n_kv_heads"] * (cfg["n_tree"] - cfg.get("q_first", 0))
     units = cfg["n_kv_heads"] * -(-rows // 128) * splits
-    return units * 128 * (8 + cfg["head_dim"] * (4 if cfg["dtype"] == "f32" else 2))
+    return units * 128 * (8 + cfg["head_dim"] * 4)
 
 
 def verify_bytes(cfg, n):
@@ -148,8 +147,10 @@ def load_traffic(cfg):
     return rec.get("traffic_bytes")
 
 
-def cpu_baseline(cfg, x, path, surv, budget_s):
-    """The oracle as it stands, on a bounded sample of the same workload."""
+def cpu_baseline(cfg, x, path, surv, budget_s, budget_1t=0.0):
+    """The oracle as it stands, on a bounded sample of the same workload: with
+    BLAS threads on every host core (the reported value), and again with one
+    thread (value_1thread) on a smaller sample."""
     from threadpoolctl import threadpool_limits
 
     import oracle
@@ -160,22 +161,31 @@ def cpu_baseline(cfg, x, path, surv, budget_s):
     P, parent, n = x["prefix_len"], x["parent"], cfg["n_tree"]
     qf = x.get("q_first", 0)
     rows = n - qf
-    with threadpool_limits(limits=cores):
-        t0 = time.perf_counter()
-        done = 0
-        # one query node at a time (its own ancestors only), until the time budget is spent
-        while done < rows and time.perf_counter() - t0 < budget_s:
-            _one_node(oracle, q, k, v, P, parent, qf, qf + done, cfg["n_kv_heads"])
-            done += 1
-        attn_s = (time.perf_counter() - t0) / done
-        kb, vb = W.raw_bits(x["k"]), W.raw_bits(x["v"])
-        t1 = time.perf_counter()
-        oracle.kv_reroot_ref(kb, vb, P, parent, path, surv)
-        reroot_s = time.perf_counter() - t1
-    step_us = (attn_s * rows + reroot_s) * 1e6
-    return {"value": round(step_us, 1), "unit": "us/step", "cores": cores, "kind": "oracle",
-            "sample": f"tree_attn_ref on {done} of {rows} query nodes (all heads, full prefix), scaled "
-                      f"x{rows / done:.2f} to all of them, plus one kv_reroot_ref of the same cache; numpy fp64"}
+    kb, vb = W.raw_bits(x["k"]), W.raw_bits(x["v"])
+
+    def sample(threads, budget):
+        with threadpool_limits(limits=threads):
+            t0 = time.perf_counter()
+            done = 0
+            # one query node at a time (its own ancestors only), until the time budget is spent
+            while done < rows and time.perf_counter() - t0 < budget:
+                _one_node(oracle, q, k, v, P, parent, qf, qf + done, cfg["n_kv_heads"])
+                done += 1
+            attn_s = (time.perf_counter() - t0) / done
+            t1 = time.perf_counter()
+            oracle.kv_reroot_ref(kb, vb, P, parent, path, surv)
+            reroot_s = time.perf_counter() - t1
+        return (attn_s * rows + reroot_s) * 1e6, done
+
+    step_us, done = sample(cores, budget_s)
+    res = {"value": round(step_us, 1), "unit": "us/step", "cores": cores, "kind": "oracle",
+           "sample": f"tree_attn_ref on {done} of {rows} query nodes (all heads, full prefix), scaled "
+                     f"x{rows / done:.2f} to all of them, plus one kv_reroot_ref of the same cache; numpy fp64"}
+    if budget_1t > 0:
+        one_us, done1 = sample(1, budget_1t)
+        res["value_1thread"] = round(one_us, 1)
+        res["sample_1thread"] = f"the same with one BLAS thread on {done1} of {rows} query nodes"
+    return res
 
 
 def _one_node(oracle, q, k, v, P, parent, qf, i, hkv):
@@ -432,6 +442,131 @@ def run_extras(ta, torch, cfg, dev, parent, P, K, timed):
 
 
 # --------------------------------------------------------------------------
+# The draft loop, run as a loop
+
+
+def main_loop(args, cfg):
+    """The draft-loop workload as a loop: from P = 4096, every iteration is
+    one tree_attn over the current 64-node tree (one layer) and one kv_reroot
+    of the cache for a random accepted path of length 1..8 and its surviving
+    subtree, then the refill of the tree back to 64 nodes (new rows written
+    into the cache). The refill rows, queries and plans come from the seeded
+    workload, precomputed on the host. A step is one iteration; K steps run
+    the iterations in order (wrapping to a fresh cache after the last).
+
+    Each iteration's two kernels sit between their own HIP events; between
+    iterations, outside those events, an untimed fill of 512 MB evicts the
+    caches (in a draft step the other layers and the weights pass through
+    L2 and the Infinity Cache between two uses of one layer) and the refill
+    rows are copied in. value = mean over the K iterations of (tree_attn +
+    kv_reroot) event time.
+    """
+    import torch
+
+    import tree_masked_attention_attn_amd as ta
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    loop = W.DraftLoop(cfg)
+    k0, v0 = loop.initial_cache()
+    iters = []
+    for _ in range(cfg["iterations"]):
+        q = loop.queries()
+        P, parent = loop.prefix_len, list(loop.parent)
+        path, surv = loop.choose()
+        src, new_par, new_p = ta.kv_reroot_plan(P, cfg["capacity"], parent, path, surv)
+        keep, kr, vr = loop.advance(surv, new_par, new_p)
+        c = dict(cfg, prefix=P)
+        nbytes, flops, _ = tree_attn_work(c, parent)
+        iters.append(dict(q=q.to(dev), P=P, parent=parent, path=path, surv=surv, new_p=new_p, keep=keep,
+                          kr=kr.to(dev), vr=vr.to(dev), bytes=nbytes, flops=flops,
+                          rr_bytes=reroot_bytes(cfg, src, P), splits=ta.tree_attn_num_splits(
+                              k0, v0, cfg["n_q_heads"], P, cfg["n_tree"])))
+    kinit, vinit = k0.to(dev), v0.to(dev)
+    kd, vd = kinit.clone(), vinit.clone()
+    out = torch.empty_like(iters[0]["q"])
+    ws = torch.zeros(max(ta.tree_attn_workspace_bytes(kd, vd, cfg["n_q_heads"], cfg["capacity"] - 256,
+                                                      cfg["n_tree"]), 1 << 20), dtype=torch.uint8, device=dev)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    n = cfg["n_tree"]
+
+    def run(count, timed_events):
+        ev = []
+        for j in range(count):
+            it = iters[j % len(iters)]
+            if j % len(iters) == 0:
+                kd.copy_(kinit)
+                vd.copy_(vinit)
+            flush.fill_(j & 255)
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)] if timed_events else None
+            if e:
+                e[0].record(stream)
+            ta.tree_attn(it["q"], kd, vd, it["P"], it["parent"], out=out, workspace=ws)
+            if e:
+                e[1].record(stream)
+            ta.kv_reroot(kd, vd, it["P"], it["parent"], it["path"], it["surv"])
+            if e:
+                e[2].record(stream)
+                ev.append(e)
+            lo, hi = it["new_p"] + it["keep"], it["new_p"] + n
+            kd[:, :, lo:hi] = it["kr"]
+            vd[:, :, lo:hi] = it["vr"]
+        return ev
+
+    run(args.warmup, False)
+    torch.cuda.synchronize()
+    K = args.steps
+    wall = time.perf_counter()
+    ev = run(K, True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall
+    attn_us = [e[0].elapsed_time(e[1]) * 1e3 for e in ev]
+    rr_us = [e[1].elapsed_time(e[2]) * 1e3 for e in ev]
+    sel = [iters[j % len(iters)] for j in range(K)]
+    a_bytes = sum(it["bytes"] for it in sel)
+    a_flops = sum(it["flops"] for it in sel)
+    r_bytes = sum(it["rr_bytes"] for it in sel)
+    a_sum, r_sum = sum(attn_us), sum(rr_us)
+    hbm_gbs = a_bytes / (a_sum * 1e-6) / 1e9
+    step_us = (a_sum + r_sum) / K
+    roof = {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(hbm_gbs / HBM_PEAK_GBS, 4), "traffic": None}
+    cpu = None
+    if not args.no_cpu_baseline:
+        it0 = iters[0]
+        x0 = dict(q=it0["q"].cpu(), k=k0, v=v0, prefix_len=it0["P"], parent=it0["parent"], q_first=0)
+        cpu = cpu_baseline(cfg, x0, it0["path"], it0["surv"], args.cpu_budget, args.cpu_budget_1t)
+        cpu["sample"] += " (the loop's first iteration, P = %d)" % it0["P"]
+    ps = [it["P"] for it in sel]
+    line = {
+        "metric": "tree-attn us/step + achieved HBM GB/s (frac of peak); kv_reroot GB/s",
+        "value": round(step_us, 2), "unit": "us/step", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(step_us / 1e3, 5), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": cfg["dtype"],
+        "data": "synthetic (seeded Gaussian q/k/v, width-8 max-likelihood tree, random accepted paths, refills)",
+        "config": {"workload": cfg["name"], "mode": "loop", "iterations": len(iters),
+                   "n_q_heads": cfg["n_q_heads"], "n_kv_heads": cfg["n_kv_heads"], "head_dim": cfg["head_dim"],
+                   "prefix_len_first": ps[0], "prefix_len_last": ps[-1], "n_tree": n,
+                   "accepted_path_mean": round(statistics.fmean(len(it["path"]) for it in sel), 2),
+                   "splits": sorted({it["splits"] for it in sel})},
+        "tree_attn": {"us_mean": round(a_sum / K, 2), "us_p10": round(pct(attn_us, 10), 2),
+                      "us_p50": round(pct(attn_us, 50), 2), "us_p90": round(pct(attn_us, 90), 2),
+                      "algorithmic_bytes_mean": round(a_bytes / K), "algorithmic_flops_mean": round(a_flops / K),
+                      "hbm_GBs": round(hbm_gbs, 1), "hbm_frac": round(hbm_gbs / HBM_PEAK_GBS, 4)},
+        "kv_reroot": {"us_mean": round(r_sum / K, 2), "us_p50": round(pct(rr_us, 50), 2),
+                      "algorithmic_bytes_mean": round(r_bytes / K),
+                      "GBs": round(r_bytes / (r_sum * 1e-6) / 1e9, 2)},
+        "iteration_us_p50": round(pct([a + r for a, r in zip(attn_us, rr_us)], 50), 2),
+        "wall_s_timed_region": round(wall, 4),
+        "kernel_source_sha": kernel_source_sha(),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+# --------------------------------------------------------------------------
 
 
 def main():
@@ -442,6 +577,8 @@ def main():
     ap.add_argument("--config", default="llama3_70b_verify")
     ap.add_argument("--rotate", type=int, default=0, help="input sets cycled (0 = enough to exceed 2x MALL)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--cpu-budget-1t", type=float, default=6.0,
+                    help="seconds of oracle work for cpu_baseline's one-thread figure")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib", action="store_true", help="also run one plain device copy (counter calibration)")
     ap.add_argument("--no-extras", action="store_true", help="skip the labelled extras (verify, expand, all layers)")
@@ -463,11 +600,14 @@ def main():
               "exchange, and this benchmark runs and reports on a single MI355X only.", file=sys.stderr)
         sys.exit(2)
 
+    cfg = W.config(args.config)
+    if cfg.get("iterations"):
+        return main_loop(args, cfg)
+
     import torch
 
     import tree_masked_attention_attn_amd as ta
 
-    cfg = W.config(args.config)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     base = W.make_inputs(cfg, poison=False)
@@ -579,7 +719,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, base, path, surv, args.cpu_budget)
+        cpu = cpu_baseline(cfg, base, path, surv, args.cpu_budget, args.cpu_budget_1t)
 
     step_us = total_us / K
     line = {

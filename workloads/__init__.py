@@ -42,6 +42,11 @@ CONFIGS = {
     "llama3_70b_verify_bs8": dict(n_q_heads=64, n_kv_heads=8, head_dim=128, dtype="bf16",
                                   prefix=8192, n_tree=8, capacity=8192 + 256, seed=5,
                                   value_scale=1.0 / math.sqrt(128), tree="top8_bs8", vocab=128256, layers=80),
+    # One tensor-parallel rank's share of the 70B verify step when the target
+    # runs attention on 4 GPUs split by KV head (16 query / 2 KV heads).
+    "llama3_70b_verify_tp4": dict(n_q_heads=16, n_kv_heads=2, head_dim=128, dtype="bf16",
+                                  prefix=8192, n_tree=64, capacity=8192 + 256, seed=7,
+                                  value_scale=1.0 / math.sqrt(128), tree="top8", vocab=128256, layers=80),
     # A draft-expansion step: only the w = 8 newest leaves of the 64-node tree
     # are queries, against the whole [prefix | tree].
     "draft_expand_w8": dict(n_q_heads=32, n_kv_heads=8, head_dim=64, dtype="bf16",
