@@ -22,7 +22,9 @@
  * Conventions shared by every entry point:
  *  - Plain C types only. No exception crosses this boundary.
  *  - Device buffers are owned by the caller. The library never allocates,
- *    frees or retains device memory, and never synchronises a stream.
+ *    frees or retains device memory (the one exception is the static scratch
+ *    of ta_tree_attn_rows_noalloc, a device array of the library's own code
+ *    object), and never synchronises a stream.
  *  - Host arrays are read only during the call.
  *  - Every argument is validated before anything is enqueued. On error the
  *    call enqueues nothing, leaves every output untouched, returns a status
@@ -136,6 +138,30 @@ size_t ta_tree_attn_rows_workspace_bytes(const ta_kv_cache* cache, int32_t n_q_h
                                          int32_t prefix_len, int32_t n_tree, int32_t q_first);
 int32_t ta_tree_attn_rows_num_splits(const ta_kv_cache* cache, int32_t n_q_heads,
                                      int32_t prefix_len, int32_t n_tree, int32_t q_first);
+
+/*
+ * For callers that cannot allocate device memory or pass a workspace (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): ta_tree_attn_rows with the split workspace taken from a static
+ * device array of this library, TA_NOALLOC_SCRATCH_BYTES per GPU, which each
+ * GPU the library runs on holds until the process ends. The call itself
+ * allocates nothing (no hipMalloc, no allocating library routine); on its
+ * first use on a device it looks up that device's copy of the array.
+ *
+ *  stream  must belong to the current device (TA_ERR_ARG otherwise).
+ * Every other argument, limit and error as ta_tree_attn_rows. A shape whose
+ * workspace (ta_tree_attn_rows_workspace_bytes) exceeds the scratch is
+ * TA_ERR_UNSUPPORTED, with nothing enqueued.
+ *
+ * All no-alloc calls on one GPU share that GPU's scratch, whose hand-off
+ * counters every completed call leaves at zero: calls that can overlap on
+ * one GPU (two streams, overlapping graph replays, two threads) race and
+ * must be ordered by the caller.
+ */
+#define TA_NOALLOC_SCRATCH_BYTES (20u << 20)
+ta_status ta_tree_attn_rows_noalloc(const void* q, const ta_kv_cache* cache, int32_t layer,
+                                    int32_t prefix_len, const int32_t* parent, int32_t n_tree,
+                                    int32_t q_first, int32_t n_q_heads, void* out, void* stream);
 
 /*
  * Re-root every layer of the cache after a verification step.

@@ -317,3 +317,17 @@ def test_default_workspaces_are_kept_per_stream():
     assert grown.numel() >= 8 << 20 and ta._workspace("cpu", 16, "attn", stream=11).data_ptr() == grown.data_ptr()
     assert ta._workspace("cpu", 0, "attn", stream=11) is None
 
+
+def test_noalloc_entry_refuses_shapes_beyond_its_scratch_before_any_device_call():
+    """255 KV heads of 64 query rows each at 2 splits: 510 units of fp32
+    partials (33 MB) exceed the 20 MiB static scratch."""
+    lib = ta.lib()
+    d = _desc(H=255, C=1200)
+    par, n = ta._i32([-1] * 64)
+    need = lib.ta_tree_attn_rows_workspace_bytes(ctypes.byref(d), 255, 1000, 64, 0)
+    assert need > 20 << 20
+    st = lib.ta_tree_attn_rows_noalloc(FAKE, ctypes.byref(d), 0, 1000, par, n, 0, 255, FAKE, None)
+    assert st == ta.TA_ERR_UNSUPPORTED and b"static scratch" in lib.ta_last_error()
+    bad, _ = ta._i32([-1, 5] + [0] * 62)
+    assert lib.ta_tree_attn_rows_noalloc(FAKE, ctypes.byref(_desc()), 0, 8192, bad, 64, 0, 64, FAKE,
+                                         None) == ta.TA_ERR_TREE

@@ -6,6 +6,7 @@ memory and for the current HIP stream. There is no CPU fallback: if the
 library has not been built, importing works but every call raises.
 
     tree_attn(q, k_cache, v_cache, prefix_len, parent, layer=0, out=None)
+    tree_attn_noalloc(q, k_cache, v_cache, prefix_len, parent, out)  (no workspace, no allocation)
     tree_verify(logits, tokens, parent) -> (choice, result) device tensors
     tree_expand(logits, path_scores, k) -> (leaf, token, score) device tensors
     kv_reroot(k_cache, v_cache, prefix_len, parent, accepted_path, surviving_nodes)
@@ -84,6 +85,10 @@ def lib():
             L.ta_tree_attn_rows_num_splits.restype = ctypes.c_int32
             L.ta_tree_attn_rows_num_splits.argtypes = [_CP, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                        ctypes.c_int32]
+            L.ta_tree_attn_rows_noalloc.restype = ctypes.c_int
+            L.ta_tree_attn_rows_noalloc.argtypes = [ctypes.c_void_p, _CP, ctypes.c_int32, ctypes.c_int32, _I32P,
+                                                    ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                                    ctypes.c_void_p]
             L.ta_kv_reroot.restype = ctypes.c_int
             L.ta_kv_reroot.argtypes = [_CP, ctypes.c_int32, _I32P, ctypes.c_int32, _I32P, ctypes.c_int32,
                                        _I32P, ctypes.c_int32, _I32P, _I32P, ctypes.c_void_p]
@@ -230,6 +235,26 @@ def tree_attn(q, k_cache, v_cache, prefix_len, parent, layer=0, out=None, worksp
     else:
         _check(lib().ta_tree_attn_rows(q.data_ptr(), ctypes.byref(desc), layer, prefix_len, par, n, q_first,
                                        q.shape[1], out.data_ptr(), ws_ptr, ws_len, _stream_ptr(q.device)))
+    return out
+
+
+def tree_attn_noalloc(q, k_cache, v_cache, prefix_len, parent, out, layer=0, q_first=0):
+    """``tree_attn`` through ``ta_tree_attn_rows_noalloc``: no workspace and no
+    allocation anywhere (``out`` must be given). The split workspace is the
+    library's static scratch of the current device, shared by every such
+    call there; calls that can overlap on one GPU must not be issued."""
+    if q.dim() != 3 or not q.is_contiguous() or not q.is_cuda:
+        raise ValueError("q must be a contiguous [n_rows, n_q_heads, head_dim] GPU tensor")
+    desc = _cache_desc(k_cache, v_cache)
+    if q.dtype != k_cache.dtype or q.device != k_cache.device:
+        raise ValueError("q must match the cache in dtype and device")
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() or out.device != q.device:
+        raise ValueError("out must be a contiguous tensor like q")
+    par, n = _i32(parent)
+    if q.shape[0] != n - q_first:
+        raise ValueError("q must have one row per tree node from q_first on")
+    _check(lib().ta_tree_attn_rows_noalloc(q.data_ptr(), ctypes.byref(desc), layer, prefix_len, par, n, q_first,
+                                           q.shape[1], out.data_ptr(), _stream_ptr(q.device)))
     return out
 
 

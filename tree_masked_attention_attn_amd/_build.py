@@ -27,7 +27,7 @@ DEVICE = ["-x", "hip", "--offload-arch=" + ARCH,
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 SOURCES = [("plan.cpp", False), ("api.cpp", False),
            ("tree_attn_kernel.hip", True), ("kv_reroot_kernel.hip", True),
-           ("tree_verify_kernel.hip", True), ("tree_expand_kernel.hip", True)]
+           ("tree_verify_kernel.hip", True), ("tree_expand_kernel.hip", True), ("noalloc.hip", True)]
 
 
 def _compile(src, device):
