@@ -342,70 +342,111 @@ __device__ __forceinline__ void put_ml(const PartialSink& k, int r, float m, flo
 }
 
 // Merge rows [r0, r1) of row block `grp` from all splits and write them to
-// `out`. One memory round trip per
-// batch of splits: each thread loads, for its
-// (row, float4 of head_dim), every split's (max, sum) pair and partial in one
-// batch, then combines them online in split order (deterministic for a
-// given shape): M is the running max, acc and L are rescaled by 2^(M_old - M).
+// `out`: M is the running max of the splits' reference maxima, acc and L are
+// rescaled by 2^(M_old - M), in split order (deterministic for a given shape).
+// Device-scope loads (cache policy sc1), like the count that announced the
+// partials: they do not return lines cached before the partials were
+// written. A split index past the last one falls outside the buffer ranges
+// and reads zeros without a memory access; it is ignored.
+//
+// One memory round trip per item: a thread loads every split's (max, sum)
+// pair and partial float4 of its item before combining them.
+//  * Up to 8 splits: an item is one (row, float4 column); consecutive threads
+//    take consecutive rows, which are consecutive in the lane-ordered
+//    partials (a wave's load touches a few cache lines, not one per lane
+//    pair).
+//  * 9 to 32 splits: an item is (row, column, group of 8 splits); the H = 2
+//    or 4 groups of one (row, column) sit in adjacent lanes and are combined
+//    with lane exchanges, so a slice of 128/S rows still takes one batch of
+//    8 loads per thread instead of S/8 batches in a row.
 template <typename T, int D, int NTH>
 __device__ void merge_rows(const TreeAttnArgs& a, int grp, int g, int rb, int r0, int r1, int tid) {
   constexpr int C4 = D / 4;  // chunks of 4 values per row
-  using V4 = f32x4;
+  constexpr int MB = 8;      // splits per load batch
   const int S = a.splits;
   const size_t u0 = (size_t)grp * S;
-  // Device-scope loads (cache policy sc1), like the count that announced
-  // the partials: they do not return lines cached before the partials were
-  // written.
   const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<V4*>(reinterpret_cast<const V4*>(a.ws_o) + u0 * kBlockRows * C4), 0,
-      S * kBlockRows * C4 * (int)sizeof(V4), 0x00020000);
+      const_cast<f32x4*>(reinterpret_cast<const f32x4*>(a.ws_o) + u0 * kBlockRows * C4), 0,
+      S * kBlockRows * C4 * (int)sizeof(f32x4), 0x00020000);
   const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<float2*>(a.ws_ml + u0 * kBlockRows), 0, S * kBlockRows * 8, 0x00020000);
-  // Thread tid takes float4 column c of rows r0 + tid % RPP, + RPP, ...:
-  // consecutive threads take consecutive rows, which are consecutive in the
-  // lane-ordered partials (a wave's load touches a few cache lines instead
-  // of one per lane pair).
-  constexpr int RPP = NTH / C4;  // rows per pass
-  static_assert(RPP * C4 == NTH && (RPP & (RPP - 1)) == 0, "threads per pass");
-  const int c = tid / RPP;
-  for (int br = r0 + tid % RPP; br < r1; br += RPP) {
-    const int hrow = rb * kBlockRows + br;
-    if (hrow >= a.rows_per_head) continue;
+  // Online combine of the splits s0 .. s0 + MB - 1 of (block row br, column c)
+  // into (M, L, acc), after loading all of them.
+  auto combine = [&](int br, int c, int s0, float& M, float& L, f32x4& acc) {
     const int pi = part_index<D>(br, c);
-    float M = kNegInf, L = 0.f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    // Batches of MB splits: all loads of a batch first, unconditionally (a
-    // split index past the last one falls outside the buffer ranges, reads
-    // zeros without a memory access and is ignored below), so that a batch
-    // costs one memory round trip. Eight per batch measured faster than one
-    // batch of 16 or 32 loads for 16 and 32 splits: the wider batches hold
-    // more registers while the loads are in flight.
-    constexpr int MB = 8;
-    for (int s0 = 0; s0 < S; s0 += MB) {
-      float2 ml[MB];
-      V4 o[MB];
+    float2 ml[MB];
+    f32x4 o[MB];
 #pragma unroll
-      for (int k = 0; k < MB; ++k) {
-        const int sk = s0 + k;
-        ml[k] = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(rm, (sk * kBlockRows + br) * 8, 0,
-                                                                                kWriteThrough));
-        o[k] = __builtin_bit_cast(V4, __builtin_amdgcn_raw_buffer_load_b128(
-                                          rp, (sk * kBlockRows * C4 + pi) * 16, 0, kWriteThrough));
-      }
-#pragma unroll
-      for (int k = 0; k < MB; ++k) {
-        // a split past the end, or one with no visible key for this row, adds nothing
-        const bool ok = s0 + k < S && ml[k].x != kNegInf;
-        const float Mn = ok ? fmaxf(M, ml[k].x) : M;
-        const float sa = M == kNegInf ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
-        const float sb = ok ? __builtin_amdgcn_exp2f(ml[k].x - Mn) : 0.f;
-        acc = acc * sa + o[k] * sb;
-        L = L * sa + ml[k].y * sb;
-        M = Mn;
-      }
+    for (int k = 0; k < MB; ++k) {
+      const int sk = s0 + k;
+      ml[k] = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(rm, (sk * kBlockRows + br) * 8, 0,
+                                                                              kWriteThrough));
+      o[k] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, (sk * kBlockRows * C4 + pi) * 16,
+                                                                            0, kWriteThrough));
     }
+#pragma unroll
+    for (int k = 0; k < MB; ++k) {
+      // a split past the end, or one with no visible key for this row, adds nothing
+      const bool ok = s0 + k < S && ml[k].x != kNegInf;
+      const float Mn = ok ? fmaxf(M, ml[k].x) : M;
+      const float sa = M == kNegInf ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
+      const float sb = ok ? __builtin_amdgcn_exp2f(ml[k].x - Mn) : 0.f;
+      acc = acc * sa + o[k] * sb;
+      L = L * sa + ml[k].y * sb;
+      M = Mn;
+    }
+  };
+  auto put = [&](int br, int c, float L, f32x4 acc) {
+    const int hrow = rb * kBlockRows + br;
     const int nd = div_small(hrow, a.group, a.group_rcp), hd = g * a.group + hrow - nd * a.group;
     store4<T>(static_cast<T*>(a.out) + ((size_t)nd * a.n_q_heads + hd) * D + 4 * c, acc * (1.f / L));
+  };
+  if (S <= MB) {
+    constexpr int RPP = NTH / C4;  // rows per pass
+    static_assert(RPP * C4 == NTH && (RPP & (RPP - 1)) == 0, "threads per pass");
+    const int c = tid / RPP;
+    for (int br = r0 + tid % RPP; br < r1; br += RPP) {
+      if (rb * kBlockRows + br >= a.rows_per_head) continue;
+      float M = kNegInf, L = 0.f;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      combine(br, c, 0, M, L, acc);
+      put(br, c, L, acc);
+    }
+    return;
+  }
+  // H groups of 8 splits per (row, column), in lanes h = lane % H.
+  const int H = S <= 2 * MB ? 2 : 4;
+  const int h = tid & (H - 1);
+  const int rows = r1 - r0;
+  const int pairs = rows * C4;
+  const int per_pass = NTH / H;
+  const int passes = (pairs + per_pass - 1) / per_pass;  // uniform: every lane runs every pass
+  for (int pass = 0; pass < passes; ++pass) {
+    // every lane of a wave takes part in the exchanges below; an item past the
+    // slice loads nothing
+    const int p = pass * per_pass + tid / H;
+    const bool live = p < pairs;
+    const int br = r0 + (live ? p % rows : 0), c = live ? p / rows : 0;
+    float M = kNegInf, L = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (live) combine(br, c, h * MB, M, L, acc);
+    // combine the H groups, the lower group's terms first in every lane
+#pragma unroll
+    for (int step = 1; step < 4; step <<= 1) {
+      if (step >= H) break;
+      const float M2 = __shfl_xor(M, step), L2 = __shfl_xor(L, step);
+      f32x4 a2;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a2[i] = __shfl_xor(acc[i], step);
+      const float Mn = fmaxf(M, M2);
+      const float sa = M == kNegInf ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
+      const float sb = M2 == kNegInf ? 0.f : __builtin_amdgcn_exp2f(M2 - Mn);
+      const bool lower = (h & step) == 0;
+      acc = lower ? acc * sa + a2 * sb : a2 * sb + acc * sa;
+      L = lower ? L * sa + L2 * sb : L2 * sb + L * sa;
+      M = Mn;
+    }
+    if (live && h == 0 && rb * kBlockRows + br < a.rows_per_head) put(br, c, L, acc);
   }
 }
 
@@ -1469,6 +1510,7 @@ void tree_attn_bf16_kernel(const TreeAttnArgs a) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const int t = NT * rg + nt;  // 32-row tile of the block
+        if (32 * t >= block_rows) continue;  // padding rows: never merged
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
