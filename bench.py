@@ -208,8 +208,9 @@ def _rows(d, pattern):
 
 
 def summarize(d, out_path, command):
-    lines = [f"# rocprofv3 summary: {os.path.basename(out_path)}", "", "Command (from the repository root):", "",
-             "```", command, "```", ""]
+    lines = [f"# rocprofv3 summary: {os.path.basename(out_path)}", "",
+             f"Attention kernel sources (sha256, first 16 hex digits of {', '.join(os.path.basename(k) for k in KERNEL_SOURCES)}): "
+             f"{kernel_source_sha()}", "", "Command (from the repository root):", "", "```", command, "```", ""]
     stats = _rows(d, "*kernel_stats.csv")
     if stats:
         lines += ["Kernel statistics (durations in microseconds):", "",
@@ -226,11 +227,28 @@ def summarize(d, out_path, command):
                   "| kernel | calls | total us | average us | min us | max us |", "|---|---|---|---|---|---|"]
         for db in dbs:
             con = sqlite3.connect(db)
-            for name, n, tot, avg, mn, mx in con.execute(
-                    "select name, count(*), sum(duration), avg(duration), min(duration), max(duration) "
-                    "from kernels group by name order by sum(duration) desc"):
+            rows = list(con.execute(
+                "select name, count(*), sum(duration), avg(duration), min(duration), max(duration) "
+                "from kernels group by name order by sum(duration) desc"))
+            for name, n, tot, avg, mn, mx in rows:
                 lines.append(f"| {name[:90]} | {n} | {tot / 1e3:.1f} | {avg / 1e3:.2f} | {mn / 1e3:.2f} | "
                              f"{mx / 1e3:.2f} |")
+            # where the longest dispatches of the library's kernels fall in the run
+            lines += ["", "Longest dispatches of the library's kernels (n-th dispatch of that kernel, "
+                      "microseconds after the run's first dispatch of any kernel):", "",
+                      "| kernel | dispatch | of | duration us | at us |", "|---|---|---|---|---|"]
+            cols = {r[1] for r in con.execute("pragma table_info(kernels)")}
+            order = "start" if "start" in cols else "rowid"
+            t_first = next(con.execute(f"select min({order}) from kernels"))[0]
+            for name, n, *_ in rows:
+                if not any(k in name for k in ("tree_attn", "kv_reroot", "tree_verify", "tree_expand")):
+                    continue
+                disp = list(con.execute(f"select duration, {order} from kernels where name = ? order by {order}",
+                                        (name,)))
+                top = sorted(range(len(disp)), key=lambda i: -disp[i][0])[:3]
+                for i in top:
+                    lines.append(f"| {name[:60]} | {i + 1} | {n} | {disp[i][0] / 1e3:.2f} | "
+                                 f"{(disp[i][1] - t_first) / 1e3:.1f} |")
             con.close()
         lines.append("")
     counters = _rows(d, "*counter_collection.csv")
@@ -326,7 +344,9 @@ def counter_summary(dirs, command, workload=""):
                         m["SQ_LDS_BANK_CONFLICT"] / (m["SQ_LDS_IDX_ACTIVE"] - m["SQ_LDS_BANK_CONFLICT"])))
     if "SQ_INSTS_VALU" in m and "SQ_INSTS_MFMA" in m:
         derived.append(("VALU instructions per MFMA instruction", m["SQ_INSTS_VALU"] / m["SQ_INSTS_MFMA"]))
-    lines = ["# rocprofv3 counters: tree_attn" + (", " + workload if workload else ""), "", "Commands (from the repository root):", "", "```", command, "```",
+    lines = ["# rocprofv3 counters: tree_attn" + (", " + workload if workload else ""), "",
+             f"Attention kernel sources (sha256, first 16 hex digits): {kernel_source_sha()}", "",
+             "Commands (from the repository root):", "", "```", command, "```",
              "", f"Part: {info.get('Name', '?')}, {cus} CUs, {simds} SIMDs, {xcc} XCDs. Means per tree_attn dispatch "
              "(all instances summed):", "", "| counter | value |", "|---|---|"]
     lines += [f"| {c} | {v:.1f} |" for c, v in sorted(m.items())]
@@ -490,6 +510,13 @@ def main_loop(args, cfg):
                                                       cfg["n_tree"]), 1 << 20), dtype=torch.uint8, device=dev)
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     n = cfg["n_tree"]
+    if args.copy_calib:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def run(count, timed_events):
         ev = []
