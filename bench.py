@@ -233,6 +233,17 @@ def summarize(d, out_path, command):
             for name, n, tot, avg, mn, mx in rows:
                 lines.append(f"| {name[:90]} | {n} | {tot / 1e3:.1f} | {avg / 1e3:.2f} | {mn / 1e3:.2f} | "
                              f"{mx / 1e3:.2f} |")
+            # the library's kernels split by launch size (a re-root of all
+            # layers and one of a single layer are the same kernel)
+            if "grid_x" in {r[1] for r in con.execute("pragma table_info(kernels)")}:
+                lines += ["", "The library's kernels by launch size (grid in threads, x by y):", "",
+                          "| kernel | grid | calls | average us | min us | max us |", "|---|---|---|---|---|---|"]
+                for name, gx, gy, n, avg, mn, mx in con.execute(
+                        "select name, grid_x, grid_y, count(*), avg(duration), min(duration), max(duration) "
+                        "from kernels group by name, grid_x, grid_y order by name, grid_x * grid_y"):
+                    if any(k in name for k in ("tree_attn", "kv_reroot", "tree_verify", "tree_expand")):
+                        lines.append(f"| {name[:60]} | {gx} x {gy} | {n} | {avg / 1e3:.2f} | {mn / 1e3:.2f} | "
+                                     f"{mx / 1e3:.2f} |")
             # where the longest dispatches of the library's kernels fall in the run
             lines += ["", "Longest dispatches of the library's kernels (n-th dispatch of that kernel, "
                       "microseconds after the run's first dispatch of any kernel):", "",
@@ -400,22 +411,32 @@ def run_extras(ta, torch, cfg, dev, parent, P, K, timed):
     big = (n_layers, cfg["n_kv_heads"], cfg["capacity"], cfg["head_dim"])
     k_all = torch.zeros(big, dtype=W.TORCH_DTYPE[cfg["dtype"]], device=dev)
     v_all = torch.zeros(big, dtype=W.TORCH_DTYPE[cfg["dtype"]], device=dev)
+    # A third case moves the most rows this tree allows: the first-level node
+    # with the largest subtree is accepted alone and its whole subtree moves
+    # up by the gap in front of it.
     all_layers = {}
     v_surv = W.descendants(parent, v_path[-1]) if v_path else list(range(n))
-    for side, s_surv in (("draft", v_surv), ("target", [])):
-        s_src, _, _ = ta.kv_reroot_plan(P, cfg["capacity"], parent, v_path, s_surv)
+    firsts = [i for i in range(n) if parent[i] == -1]
+    big_root = max(firsts, key=lambda a: len(W.descendants(parent, a)))
+    cases = (("draft", v_path, v_surv), ("target", v_path, []),
+             ("largest_subtree", [big_root], W.descendants(parent, big_root)))
+    for side, s_path, s_surv in cases:
+        s_src, _, _ = ta.kv_reroot_plan(P, cfg["capacity"], parent, s_path, s_surv)
         b = reroot_bytes(cfg, s_src, P, n_layers)
         rrot = max(1, min(P // n, math.ceil(2 * MALL_BYTES / max(b, 1)) + 1))
 
-        def reroot_all(i, s_surv=s_surv, rrot=rrot):
-            ta.kv_reroot(k_all, v_all, P - (i % rrot) * n, parent, v_path, s_surv)
+        def reroot_all(i, s_path=s_path, s_surv=s_surv, rrot=rrot):
+            ta.kv_reroot(k_all, v_all, P - (i % rrot) * n, parent, s_path, s_surv)
 
         for i in range(3):
             reroot_all(i)
         _, ra_us, _ = timed(reroot_all, K, each=True)
+        ra_b2b, _, _ = timed(reroot_all, K)
         ra_mean = statistics.fmean(ra_us)
-        all_layers[side] = {"survivors": len(s_surv), "us_mean": round(ra_mean, 2),
-                            "us_p50": round(pct(ra_us, 50), 2), "algorithmic_bytes": b,
+        all_layers[side] = {"accepted_path": len(s_path), "survivors": len(s_surv),
+                            "rows_moved": sum(1 for k, r in enumerate(s_src) if r != P + k),
+                            "us_mean": round(ra_mean, 2), "us_p50": round(pct(ra_us, 50), 2),
+                            "us_launch_period_back_to_back": round(ra_b2b / K, 2), "algorithmic_bytes": b,
                             "GBs": round(b / (ra_mean * 1e-6) / 1e9, 1),
                             "hbm_frac": round(b / (ra_mean * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                             "rotated_positions": rrot}
@@ -452,7 +473,7 @@ def run_extras(ta, torch, cfg, dev, parent, P, K, timed):
                         "GBs": round(v_bytes / (ver_mean * 1e-6) / 1e9, 1),
                         "hbm_frac": round(v_bytes / (ver_mean * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                         "hot_cache_us_p50": round(statistics.median(ver_hot), 2), "rotated_sets": vrot},
-        "kv_reroot_all_layers": dict(layers=n_layers, accepted_path=len(v_path), **all_layers),
+        "kv_reroot_all_layers": dict(layers=n_layers, **all_layers),
         "tree_expand": {"vocab": cfg["vocab"], "w": ex_w, "k": ex_k, "us_mean": round(ex_mean, 2),
                         "us_p50": round(pct(ex_us, 50), 2), "us_launch_period_back_to_back": round(ex_b2b / K, 2),
                         "hot_cache_us_p50": round(statistics.median(ex_hot), 2), "algorithmic_bytes": e_bytes,

@@ -334,10 +334,12 @@ ta_status ta_kv_reroot(const ta_kv_cache* cache, int32_t prefix_len, const int32
     a.n_planes = cache->n_layers * cache->n_kv_heads;
     a.n_rows = rows;
     a.dst0 = prefix_len;
-    // Columns per workgroup: enough that every thread has about one item.
+    // Every column of a plane in one workgroup while a thread's share stays
+    // within kRerootItemsPerThread: its loads are then all in flight at once,
+    // and a launch of many planes needs only one workgroup per plane.
     const int32_t cols = a.row_bytes / 16;
     int32_t gcols = cols;
-    while (gcols > 1 && rows * gcols > 256) gcols /= 2;
+    while (gcols > 1 && rows * gcols > kRerootItemsPerThread * kRerootThreads) gcols /= 2;
     a.col_groups = cols / gcols;
     hipError_t e = launch_kv_reroot(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return device_error(e, "kv_reroot launch");

@@ -15,6 +15,11 @@
 // of its (row, column) items into registers, the workgroup barrier orders
 // every load before any store, then the stores run. No scratch memory and no
 // cross-workgroup ordering are needed.
+//
+// The stores are nontemporal: the moved rows stream to HBM instead of
+// waiting as dirty L2 lines for the write-back at the kernel's end (an
+// 80-layer move of 47 rows, 30.8 MB, measured 15.5 us back to back with
+// plain stores and 8.9 us with these).
 #include <hip/hip_runtime.h>
 
 #include "launch.h"
@@ -22,8 +27,8 @@
 namespace ta {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kMaxItems = 8;  // (row, 16-B column) items per thread
+constexpr int kThreads = kRerootThreads;
+constexpr int kMaxItems = kRerootItemsPerThread;  // (row, 16-B column) items per thread
 
 __global__ __launch_bounds__(kThreads) void kv_reroot_kernel(const RerootArgs a) {
   const int plane = blockIdx.x;            // 0 .. 2*n_planes-1 (K planes, then V planes)
@@ -35,14 +40,15 @@ __global__ __launch_bounds__(kThreads) void kv_reroot_kernel(const RerootArgs a)
   const int c0 = cg * gcols;
   const int items = a.n_rows * gcols;
 
-  uint4 val[kMaxItems];
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 val[kMaxItems];
 #pragma unroll
   for (int i = 0; i < kMaxItems; ++i) {
     const int it = threadIdx.x + i * kThreads;
     if (it < items) {
       const int k = it / gcols, c = c0 + it % gcols;
       if (a.src[k] != a.dst0 + k)
-        val[i] = *reinterpret_cast<const uint4*>(base + (size_t)a.src[k] * a.row_bytes + c * 16);
+        val[i] = *reinterpret_cast<const u32x4*>(base + (size_t)a.src[k] * a.row_bytes + c * 16);
     }
   }
   __syncthreads();
@@ -52,7 +58,8 @@ __global__ __launch_bounds__(kThreads) void kv_reroot_kernel(const RerootArgs a)
     if (it < items) {
       const int k = it / gcols, c = c0 + it % gcols;
       if (a.src[k] != a.dst0 + k)
-        *reinterpret_cast<uint4*>(base + (size_t)(a.dst0 + k) * a.row_bytes + c * 16) = val[i];
+        __builtin_nontemporal_store(val[i],
+                                    reinterpret_cast<u32x4*>(base + (size_t)(a.dst0 + k) * a.row_bytes + c * 16));
     }
   }
 }

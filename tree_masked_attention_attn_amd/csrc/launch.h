@@ -72,6 +72,10 @@ struct RerootArgs {
   int32_t src[kMaxTree];    // source slot of destination slot dst0 + k
 };
 
+// Workgroup size and (row, 16-byte column) items per thread of the re-root kernel.
+constexpr int kRerootThreads = 256;
+constexpr int kRerootItemsPerThread = 8;
+
 hipError_t launch_kv_reroot(const RerootArgs& a, hipStream_t stream);
 
 // Rows of one verification: the virtual root and up to kMaxTree nodes.

@@ -52,7 +52,11 @@ constexpr int32_t kTilesPerBlock = 4;  // 32-row MFMA tiles per row block (the f
 constexpr int32_t kRowsPerTile = 32;   // query rows per MFMA tile (one 32-wide MFMA N tile)
 constexpr int32_t kRowsPerBlock = kTilesPerBlock * kRowsPerTile;
 constexpr int32_t kTargetUnits = 512;  // 2 workgroups per CU on a 256-CU part (half that for one per CU)
-constexpr int32_t kMinTilesPerSplit = 2;
+// At least 4 key stages per split: below that, the fixed cost of a unit
+// (first loads, hand-off, merge) and the partial rows it writes outweigh the
+// extra CUs (Llama-3-8B verify, 33 stages: 8 splits on 128 CUs beat 16 on 256
+// by 7 percent; 6, 10 and 12 splits were slower still).
+constexpr int32_t kMinTilesPerSplit = 4;
 // At most 16 splits per row block (the give-up word would have room for 32):
 // past 16, the hand-off and merge of the extra partials cost more than the
 // shorter key ranges save, also when that leaves CUs idle (measured on a

@@ -13,15 +13,24 @@
 //
 // Work split (HBM-bound: each logit is read once). The grid is (chunk of
 // 4096 logits, leaf). A workgroup computes its chunk's (max, sum of exp) and
-// its k best (logit, token) keys: each wave extracts k winners with shuffles
-// only, then one wave merges the four waves' 4k. It stores them in its slot
-// of the workspace (write-through, so that another XCD reads them from
-// memory) and counts in on its leaf. The leaf's last chunk (its wrapping
-// count) merges the chunks into the leaf's logsumexp and its k best tokens,
-// turns them into fp32 scores, publishes them and counts the leaf in; the
-// last leaf's last chunk selects the k best of all leaves and writes them.
-// Each count per address takes a leaf's chunks or the leaves, never the
-// whole grid.
+// its k best (logit, token) keys, stores them in its slot of the workspace
+// (write-through, so that another XCD reads them from memory) and counts in
+// on its leaf. The leaf's last chunk (its wrapping count) merges the chunks
+// into the leaf's logsumexp and its k best tokens, turns them into fp32
+// scores, publishes them and counts the leaf in; the last leaf's last chunk
+// selects the k best of all leaves and writes them. Each count per address
+// takes a leaf's chunks or the leaves, never the whole grid.
+//
+// Selection without serial rounds. Every k-best step works on lists of L
+// keys (L = 8 or 16, at least k), sorted largest first and held in
+// registers. A thread sorts its own keys with a bitonic network; two sorted
+// lists a and b combine into their L best in one step, since the pairwise
+// maxima max(a[i], b[L-1-i]) are exactly those L keys in bitonic order, which
+// a bitonic merge sorts. Taking b from another lane by a DPP move, six such
+// steps (row mirror, half-row mirror, two quad swaps, two row broadcasts)
+// merge all 64 lanes' lists into lane 63's. Keys are unique (they carry the
+// token, or leaf and slot), so the result is the same set in the same order
+// as k rounds of "take the largest" would give.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -104,20 +113,145 @@ __device__ __forceinline__ u64 global_key(ChunkKey<T> k, int chunk) {
   }
 }
 
-__device__ __forceinline__ u64 wave_max_key(u64 k) { return wave_max_u64(k); }
-__device__ __forceinline__ uint32_t wave_max_key(uint32_t k) { return wave_max_u32(k); }
+template <typename K>
+__device__ __forceinline__ K kmax(K a, K b) { return a > b ? a : b; }
+template <typename K>
+__device__ __forceinline__ K kmin(K a, K b) { return a > b ? b : a; }
 
-template <typename T>
+// a, b <- the larger, the smaller (32-bit keys: a max and a min; 64-bit
+// keys: one comparison selecting both halves of both)
+__device__ __forceinline__ void cas(uint32_t& a, uint32_t& b) {
+  const uint32_t hi = kmax(a, b), lo = kmin(a, b);
+  a = hi;
+  b = lo;
+}
+__device__ __forceinline__ void cas(u64& a, u64& b) {
+  const bool gt = a > b;
+  const u64 hi = gt ? a : b, lo = gt ? b : a;
+  a = hi;
+  b = lo;
+}
+
+// r[0..N), a bitonic sequence, into descending order (half-cleaners at
+// distances N/2, .., 1).
+template <int N, typename K, int M>
+__device__ __forceinline__ void bitonic_merge_desc(K (&r)[M]) {
+  static_assert(N <= M && (N & (N - 1)) == 0, "power of two");
+#pragma unroll
+  for (int d = N / 2; d >= 1; d /= 2)
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      if ((i & d) == 0) cas(r[i], r[i + d]);
+}
+
+// r[0..N) into descending order: bitonic sort, blocks of each size sorted
+// in alternating directions so that each pair of them forms a bitonic run.
+template <int N, int OFF, typename K, int M>
+__device__ __forceinline__ void bitonic_sort_desc(K (&r)[M]) {
+  static_assert(OFF + N <= M && (N & (N - 1)) == 0, "power of two");
+#pragma unroll
+  for (int size = 2; size <= N; size *= 2)
+#pragma unroll
+    for (int d = size / 2; d >= 1; d /= 2)
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const int j = i ^ d;
+        if (j > i) {
+          if ((i & size) == 0) cas(r[OFF + i], r[OFF + j]);
+          else cas(r[OFF + j], r[OFF + i]);
+        }
+      }
+}
+
+// A key of the lane that DPP control CTRL selects (lanes of rows outside
+// ROWS get their own).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_key(uint32_t x) {
+  return dpp_u32<CTRL, ROWS>(x);
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ u64 dpp_key(u64 x) {
+  return dpp_u64<CTRL, ROWS>(x);
+}
+
+// This lane's sorted list and the CTRL-selected lane's -> their L best, sorted.
+template <int CTRL, int ROWS, int L, typename K>
+__device__ __forceinline__ void merge_lanes(K (&r)[L]) {
+  K c[L];
+#pragma unroll
+  for (int i = 0; i < L; ++i) c[i] = kmax(r[i], dpp_key<CTRL, ROWS>(r[L - 1 - i]));
+  bitonic_merge_desc<L>(c);
+#pragma unroll
+  for (int i = 0; i < L; ++i) r[i] = c[i];
+}
+
+// The L best keys of the sorted lists of lanes 0 .. n-1 (the other lanes'
+// lists empty), sorted, in the lane returned. The half-row mirror and two
+// quad swaps leave in every lane of an 8-lane half the best of that half,
+// with the row mirror first of a 16-lane row (each step pairs lanes whose
+// sets are disjoint); the row broadcasts then fold row 0 into row 1, row 2
+// into row 3, and row 1 into row 3. n is the same in every lane.
+template <int L, typename K>
+__device__ __forceinline__ int wave_top(K (&r)[L], int n) {
+  if (n > 8) merge_lanes<dpp::kMirror, 0xF>(r);
+  merge_lanes<dpp::kHalfMirror, 0xF>(r);
+  merge_lanes<dpp::kXor2, 0xF>(r);
+  merge_lanes<dpp::kXor1, 0xF>(r);
+  if (n <= 16) return 0;
+  merge_lanes<dpp::kBcast15, 0xA>(r);
+  if (n <= 32) return 31;
+  merge_lanes<dpp::kBcast31, 0xC>(r);
+  return 63;
+}
+
+// Lane `src`'s key r[i], for every lane.
+__device__ __forceinline__ uint32_t readlane_key(uint32_t x, int src) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(x), src));
+}
+__device__ __forceinline__ u64 readlane_key(u64 x, int src) { return readlane_u64(x, src); }
+
+// Element i of lane `src`'s list, into lane i (i < n): a list spread over lanes.
+template <int L, typename K>
+__device__ __forceinline__ K spread_list(const K (&r)[L], int src, int lane, int n) {
+  K mine = 0;
+#pragma unroll
+  for (int i = 0; i < L; ++i) {
+    if (i < n) {
+      const K v = readlane_key(r[i], src);
+      if (lane == i) mine = v;
+    }
+  }
+  return mine;
+}
+
+// The L best of a thread's 16 keys, sorted: both halves sorted, then their
+// pairwise maxima (the 8 best, bitonic) merged; for L = 16 all of them.
+template <int L, typename K>
+__device__ __forceinline__ void thread_top(K (&key)[kPerThread], K (&top)[L]) {
+  static_assert(kPerThread == 16 && (L == 8 || L == 16), "list sizes");
+  if constexpr (L == 16) {
+    bitonic_sort_desc<16, 0>(key);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) top[i] = key[i];
+  } else {
+    bitonic_sort_desc<8, 0>(key);
+    bitonic_sort_desc<8, 8>(key);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) top[i] = kmax(key[i], key[15 - i]);
+    bitonic_merge_desc<8>(top);
+  }
+}
+
+template <typename T, int L>
 __global__ __launch_bounds__(kThreads) void tree_expand_kernel(const ExpandArgs a) {
   using CK = ChunkKey<T>;
   constexpr int EPV = 16 / sizeof(T);         // logits per 16-byte vector
   constexpr int NV = kPerThread / EPV;        // vectors per thread
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int chunk = blockIdx.x, row = blockIdx.y;
-  const int K = a.k;
+  const int K = a.k;  // <= L
   const T* x = static_cast<const T*>(a.logits) + static_cast<size_t>(row) * a.row_stride;
   const int64_t full_vecs = a.vocab / EPV;
-  const float s_leaf = a.path_scores[row];  // used by the leaf's last chunk
   const __amdgpu_buffer_rsrc_t ws = __builtin_amdgcn_make_buffer_rsrc(a.ws, 0, a.ws_bytes, 0x00020000);
 
   // Thread tid reads vectors tid, tid + 256, .. of the chunk: whole vectors
@@ -165,34 +299,15 @@ __global__ __launch_bounds__(kThreads) void tree_expand_kernel(const ExpandArgs 
   }
   lse_wave(m, s);
 
-  // The wave's K best keys: K rounds of a wave maximum over each lane's best
-  // key below the last winner (keys are unique: they hold the token id).
-  auto best_below = [&](CK lim) {
-    CK b = 0;
-#pragma unroll
-    for (int i = 0; i < kPerThread; ++i) b = (key[i] < lim && key[i] > b) ? key[i] : b;
-    return b;
-  };
-  __shared__ CK s_key[4][kExpandMaxK];
+  // The wave's L best keys, then the workgroup's (wave 0, lane 0).
+  __shared__ CK s_key[4][L];
   __shared__ float s_m[4], s_s[4];
-  // The lane's best and second-best keys: a winner moves on to its second
-  // and only re-scans its keys when that one is taken too.
-  CK cand = 0, alt = 0;
+  {
+    CK top[L];
+    thread_top<L>(key, top);
+    if (lane == wave_top<L>(top, 64)) {
 #pragma unroll
-  for (int i = 0; i < kPerThread; ++i) {
-    const CK q = key[i];
-    alt = q > cand ? cand : (q > alt ? q : alt);
-    cand = q > cand ? q : cand;
-  }
-#pragma unroll
-  for (int r = 0; r < kExpandMaxK; ++r) {
-    if (r < K) {
-      const CK w = wave_max_key(cand);
-      if (lane == 0) s_key[wave][r] = w;
-      if (cand == w && w != 0) {
-        cand = alt != 0 ? alt : best_below(w);
-        alt = 0;
-      }
+      for (int i = 0; i < L; ++i) s_key[wave][i] = top[i];
     }
   }
   if (lane == 0) {
@@ -202,18 +317,12 @@ __global__ __launch_bounds__(kThreads) void tree_expand_kernel(const ExpandArgs 
   __syncthreads();
   if (wave != 0) return;
 
-  // Wave 0: the chunk's K best of the four waves' 4K, and its (max, sum).
-  CK c4 = lane < 4 * K ? s_key[lane / K][lane % K] : CK{0};
-  CK mine_c = 0;  // lane r keeps round r's winner
+  CK c4[L];
 #pragma unroll
-  for (int r = 0; r < kExpandMaxK; ++r) {
-    if (r < K) {
-      const CK w = wave_max_key(c4);
-      if (lane == r) mine_c = w;
-      if (c4 == w) c4 = 0;
-    }
-  }
-  const u64 mine = global_key<T>(mine_c, chunk);
+  for (int i = 0; i < L; ++i) c4[i] = lane < 4 ? s_key[lane][i] : CK{0};
+  merge_lanes<dpp::kXor1, 0xF>(c4);
+  merge_lanes<dpp::kXor2, 0xF>(c4);  // lane 0: the chunk's L best
+  const u64 mine = global_key<T>(spread_list<L>(c4, 0, lane, K), chunk);
   float cm = s_m[0], cs = s_s[0];
 #pragma unroll
   for (int w = 1; w < 4; ++w) lse_merge(cm, cs, s_m[w], s_s[w]);
@@ -235,37 +344,25 @@ __global__ __launch_bounds__(kThreads) void tree_expand_kernel(const ExpandArgs 
   if (!__builtin_amdgcn_readfirstlane(last)) return;
 
   // The leaf's last chunk: lane c reads chunk c's (max, sum) and its K keys
-  // (device-scope loads: they see memory as the count did).
+  // (device-scope loads: they see memory as the count did), a sorted list.
+  const float s_leaf = a.path_scores[row];
   float lm = kNegInf, ls = 0.f;
-  u64 kk[kExpandMaxK];
+  u64 kk[L];
 #pragma unroll
-  for (int r = 0; r < kExpandMaxK; ++r) kk[r] = 0;
+  for (int r = 0; r < L; ++r) kk[r] = 0;
   if (lane < a.chunks) {
     const int sl = kExpandChunkBase + (row * kExpandMaxChunks + lane) * kExpandChunkSlot;
     const float2 ms = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(ws, sl, 0, kWriteThrough));
     lm = ms.x;
     ls = ms.y;
 #pragma unroll
-    for (int r = 0; r < kExpandMaxK; ++r)
+    for (int r = 0; r < L; ++r)
       if (r < K) kk[r] = __builtin_bit_cast(u64, __builtin_amdgcn_raw_buffer_load_b64(ws, sl + 8 + 8 * r, 0, kWriteThrough));
   }
   lse_wave(lm, ls);
   const float log_sum = __logf(ls);  // logsumexp = lm + log_sum
-  // K rounds over the chunks' sorted lists: the lane holding the winner
-  // drops its head.
-  u64 rk = 0;
-#pragma unroll
-  for (int r = 0; r < kExpandMaxK; ++r) {
-    if (r < K) {
-      const u64 w = wave_max_u64(kk[0]);
-      if (lane == r) rk = w;
-      if (kk[0] == w && w != 0) {
-#pragma unroll
-        for (int i = 0; i + 1 < kExpandMaxK; ++i) kk[i] = kk[i + 1];
-        kk[kExpandMaxK - 1] = 0;
-      }
-    }
-  }
+  const int at2 = wave_top<L>(kk, a.chunks);  // lane at2: the leaf's L best
+  const u64 rk = spread_list<L>(kk, at2, lane, K);
   const int rslot = kExpandRowBase + row * kExpandRowSlot;
   if (lane < K) {
     // slot `lane` of this leaf: (score, token), or token -1 when the leaf
@@ -283,59 +380,39 @@ __global__ __launch_bounds__(kThreads) void tree_expand_kernel(const ExpandArgs 
                                          "agent") == static_cast<unsigned>(a.w - 1);
   if (!__builtin_amdgcn_readfirstlane(last)) return;
 
-  // The last leaf: lane l holds leaf l's K (score, token) in slot order; K
-  // rounds pick the best head (score, then the lower leaf, then the lower
-  // slot), whose lane drops it.
-  float sc[kExpandMaxK];
-  int tk[kExpandMaxK];
+  // The last leaf: lane l holds leaf l's K (score, token) in slot order, as
+  // keys (score, then the lower leaf, then the lower slot): a sorted list.
+  __shared__ float s_sc[kExpandMaxRows][L];
+  __shared__ int s_tk[kExpandMaxRows][L];
+  u64 hk[L];
 #pragma unroll
-  for (int r = 0; r < kExpandMaxK; ++r) {
-    sc[r] = kNegInf;
-    tk[r] = -1;
-  }
+  for (int r = 0; r < L; ++r) hk[r] = 0;
   if (lane < a.w) {
 #pragma unroll
-    for (int r = 0; r < kExpandMaxK; ++r) {
+    for (int r = 0; r < L; ++r) {
       if (r < K) {
         const u32x2 p = __builtin_bit_cast(
             u32x2, __builtin_amdgcn_raw_buffer_load_b64(ws, kExpandRowBase + lane * kExpandRowSlot + 8 * r, 0,
                                                         kWriteThrough));
-        sc[r] = __uint_as_float(p.x);
-        tk[r] = static_cast<int>(p.y);
+        const float sc = __uint_as_float(p.x);
+        const int tk = static_cast<int>(p.y);
+        s_sc[lane][r] = sc;
+        s_tk[lane][r] = tk;
+        hk[r] = tk >= 0 ? (static_cast<u64>(order_key(sc)) << 32) |
+                              static_cast<u64>(~static_cast<uint32_t>((lane << 8) | r))
+                        : 0ull;
       }
     }
   }
-  int head = 0;  // slots of this leaf taken so far
+  const int at3 = wave_top<L>(hk, a.w);  // lane at3: the K best of all leaves
+  const uint32_t who = ~static_cast<uint32_t>(spread_list<L>(hk, at3, lane, K));  // (leaf << 8) | slot
   int out_leaf = 0, out_slot = 0, out_tok = 0;
   float out_score = 0.f;
-#pragma unroll
-  for (int r = 0; r < kExpandMaxK; ++r) {
-    if (r < K) {
-      const u64 hk = tk[0] >= 0 ? (static_cast<u64>(order_key(sc[0])) << 32) |
-                                      static_cast<u64>(~static_cast<uint32_t>((lane << 8) | head))
-                                : 0ull;
-      const u64 w = wave_max_u64(hk);
-      const uint32_t who = ~static_cast<uint32_t>(w);  // (leaf << 8) | slot
-      const int src = static_cast<int>(who >> 8);
-      const int win_tok = __builtin_amdgcn_readlane(tk[0], src);
-      const float win_score = readlane_f32(sc[0], src);
-      if (lane == r) {
-        out_leaf = src;
-        out_slot = static_cast<int>(who & 255u);
-        out_tok = win_tok;
-        out_score = win_score;
-      }
-      if (hk == w && w != 0) {
-#pragma unroll
-        for (int i = 0; i + 1 < kExpandMaxK; ++i) {
-          sc[i] = sc[i + 1];
-          tk[i] = tk[i + 1];
-        }
-        sc[kExpandMaxK - 1] = kNegInf;
-        tk[kExpandMaxK - 1] = -1;
-        ++head;
-      }
-    }
+  if (lane < K) {
+    out_leaf = static_cast<int>(who >> 8);
+    out_slot = static_cast<int>(who & 255u);
+    out_tok = s_tk[out_leaf][out_slot];
+    out_score = s_sc[out_leaf][out_slot];
   }
   // List the K new nodes by (leaf, slot).
   const int mykey = (out_leaf << 8) | out_slot;
@@ -358,12 +435,17 @@ hipError_t launch_tree_expand(const ExpandArgs& a, int32_t dtype, hipStream_t st
       a.chunks > kExpandMaxChunks || static_cast<int64_t>(a.chunks) * kChunk < a.vocab)
     return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(a.chunks), static_cast<unsigned>(a.w));
-  if (dtype == TA_F32)
-    hipLaunchKernelGGL(tree_expand_kernel<float>, grid, dim3(kThreads), 0, stream, a);
-  else if (dtype == TA_BF16)
-    hipLaunchKernelGGL(tree_expand_kernel<__bf16>, grid, dim3(kThreads), 0, stream, a);
-  else
+  // lists of 8 keys for k <= 8, of 16 above
+  const bool small = a.k <= 8;
+  if (dtype == TA_F32) {
+    if (small) hipLaunchKernelGGL((tree_expand_kernel<float, 8>), grid, dim3(kThreads), 0, stream, a);
+    else hipLaunchKernelGGL((tree_expand_kernel<float, 16>), grid, dim3(kThreads), 0, stream, a);
+  } else if (dtype == TA_BF16) {
+    if (small) hipLaunchKernelGGL((tree_expand_kernel<__bf16, 8>), grid, dim3(kThreads), 0, stream, a);
+    else hipLaunchKernelGGL((tree_expand_kernel<__bf16, 16>), grid, dim3(kThreads), 0, stream, a);
+  } else {
     return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

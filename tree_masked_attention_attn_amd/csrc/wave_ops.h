@@ -39,6 +39,8 @@ constexpr int kXor1 = 0xB1;     // quad_perm [1, 0, 3, 2]
 constexpr int kXor2 = 0x4E;     // quad_perm [2, 3, 0, 1]
 constexpr int kRor4 = 0x124;    // row_ror:4
 constexpr int kRor8 = 0x128;    // row_ror:8
+constexpr int kMirror = 0x140;      // row_mirror: lane i of a row reads lane 15 - i
+constexpr int kHalfMirror = 0x141;  // row_half_mirror: lane i of an 8-lane half reads lane 7 - i
 constexpr int kBcast15 = 0x142; // row_bcast:15 (lane 15 of a row to the next row)
 constexpr int kBcast31 = 0x143; // row_bcast:31 (lane 31 to rows 2 and 3)
 }  // namespace dpp
