@@ -1405,8 +1405,19 @@ void tree_attn_bf16_kernel(const TreeAttnArgs a) {
 #pragma unroll
         for (int i = 0; i < 2 * G::KOPS; ++i) dma(i);
       } else {
-        bf_iter<MF, D, NT, true, true, true, 2 * G::KOPS, decltype(dma)&, FR>(w, sc, pp, vf, kslot(j + 1), vslot(j),
-                                                                              kb_of(j), kh, lane, a, dma);
+        if constexpr (FR) {
+          // A wave alone on its SIMD issues the stage's loads after its
+          // iteration (their slots are free all through it): bs = 8 verify
+          // 3% faster than with the loads among the MFMAs, which the paired
+          // waves of dense blocks keep (70B 2-4% slower the other way).
+          bf_iter<MF, D, NT, true, true, true, 0, decltype(no_dma)&, FR>(w, sc, pp, vf, kslot(j + 1), vslot(j),
+                                                                        kb_of(j), kh, lane, a, no_dma);
+#pragma unroll
+          for (int i = 0; i < 2 * G::KOPS; ++i) dma(i);
+        } else {
+          bf_iter<MF, D, NT, true, true, true, 2 * G::KOPS, decltype(dma)&, FR>(w, sc, pp, vf, kslot(j + 1), vslot(j),
+                                                                                kb_of(j), kh, lane, a, dma);
+        }
       }
     };
     for (int j = 1; j < n - 1; ++j) {
