@@ -29,6 +29,7 @@ namespace {
 
 constexpr int kThreads = kRerootThreads;
 constexpr int kMaxItems = kRerootItemsPerThread;  // (row, 16-B column) items per thread
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(kThreads) void kv_reroot_kernel(const RerootArgs a) {
   const int plane = blockIdx.x;            // 0 .. 2*n_planes-1 (K planes, then V planes)
@@ -40,15 +41,14 @@ __global__ __launch_bounds__(kThreads) void kv_reroot_kernel(const RerootArgs a)
   const int c0 = cg * gcols;
   const int items = a.n_rows * gcols;
 
-  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-  u32x4 val[kMaxItems];
+  uint4 val[kMaxItems];
 #pragma unroll
   for (int i = 0; i < kMaxItems; ++i) {
     const int it = threadIdx.x + i * kThreads;
     if (it < items) {
       const int k = it / gcols, c = c0 + it % gcols;
       if (a.src[k] != a.dst0 + k)
-        val[i] = *reinterpret_cast<const u32x4*>(base + (size_t)a.src[k] * a.row_bytes + c * 16);
+        val[i] = *reinterpret_cast<const uint4*>(base + (size_t)a.src[k] * a.row_bytes + c * 16);
     }
   }
   __syncthreads();
@@ -57,9 +57,12 @@ __global__ __launch_bounds__(kThreads) void kv_reroot_kernel(const RerootArgs a)
     const int it = threadIdx.x + i * kThreads;
     if (it < items) {
       const int k = it / gcols, c = c0 + it % gcols;
-      if (a.src[k] != a.dst0 + k)
-        __builtin_nontemporal_store(val[i],
-                                    reinterpret_cast<u32x4*>(base + (size_t)(a.dst0 + k) * a.row_bytes + c * 16));
+      if (a.src[k] != a.dst0 + k) {
+        // the builtin takes a vector type; the items stay uint4 (an array of
+        // vector-typed items compiled to a register copy per use)
+        const u32x4 v = {val[i].x, val[i].y, val[i].z, val[i].w};
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(base + (size_t)(a.dst0 + k) * a.row_bytes + c * 16));
+      }
     }
   }
 }
