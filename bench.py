@@ -102,13 +102,18 @@ def reroot_bytes(cfg, src_rows, prefix, n_layers=1):
 
 def split_partial_bytes(cfg, splits):
     """Bytes of split partials one tree_attn launch writes (and the merge
-    reads back once): per unit, 128 rows of (max, sum) fp32 pairs and O in
-    fp32. Overhead, not algorithmic."""
+    reads back once): per unit and written row, a (max, sum) fp32 pair and O
+    in fp32. A unit writes its block's 128 rows; the bf16 kernel skips the
+    32-row tiles that lie wholly past the head's last query row. Overhead,
+    not algorithmic."""
     if splits <= 1:
         return 0
     rows = cfg["n_q_heads"] // cfg["n_kv_heads"] * (cfg["n_tree"] - cfg.get("q_first", 0))
-    units = cfg["n_kv_heads"] * -(-rows // 128) * splits
-    return units * 128 * (8 + cfg["head_dim"] * 4)
+    written = 0
+    for rb in range(-(-rows // 128)):
+        block = min(128, rows - 128 * rb)
+        written += 128 if cfg["dtype"] == "f32" else 32 * -(-block // 32)
+    return cfg["n_kv_heads"] * splits * written * (8 + cfg["head_dim"] * 4)
 
 
 def verify_bytes(cfg, n):

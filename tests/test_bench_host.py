@@ -112,6 +112,9 @@ def test_split_partial_bytes_match_the_traffic_excess_model():
     assert bench.split_partial_bytes(cfg, 1) == 0
     tiny = W.config("tiny_fp32")
     assert bench.split_partial_bytes(tiny, 2) == 1 * 1 * 2 * 128 * (8 + 64 * 4)
+    # bs = 8 verify: 64 query rows per KV head, so each unit writes two of its four tiles
+    bs8 = W.config("llama3_70b_verify_bs8")
+    assert bench.split_partial_bytes(bs8, 16) == 8 * 16 * 64 * (8 + 128 * 4)
 
 
 def test_counter_summary_derives_rocprof_utilisations(tmp_path):
