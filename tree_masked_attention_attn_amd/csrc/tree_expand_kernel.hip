@@ -255,13 +255,28 @@ __global__ __launch_bounds__(kThreads) void tree_expand_kernel(const ExpandArgs 
   const __amdgpu_buffer_rsrc_t ws = __builtin_amdgcn_make_buffer_rsrc(a.ws, 0, a.ws_bytes, 0x00020000);
 
   // Thread tid reads vectors tid, tid + 256, .. of the chunk: whole vectors
-  // with 16-byte loads, a ragged tail element by element (a vector that
-  // would run past the vocabulary is never loaded).
+  // with 16-byte loads; a vector that would run past the vocabulary (only
+  // in the last chunk) is never loaded whole but filled element by element,
+  // -inf past the end. The per-logit work below is then free of branches
+  // (one branch per logit measured 1.3 us per call).
   u32x4 buf[NV];
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     const int64_t vi = static_cast<int64_t>(chunk) * (kChunk / EPV) + j * kThreads + tid;
     if (vi < full_vecs) buf[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x) + vi);
+  }
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int64_t vi = static_cast<int64_t>(chunk) * (kChunk / EPV) + j * kThreads + tid;
+    if (vi >= full_vecs) {
+      T tail[EPV];
+#pragma unroll
+      for (int t = 0; t < EPV; ++t) {
+        const int64_t id = vi * EPV + t;
+        tail[t] = id < a.vocab ? x[id] : static_cast<T>(kNegInf);
+      }
+      buf[j] = __builtin_bit_cast(u32x4, tail);
+    }
   }
   float v[kPerThread];
   CK key[kPerThread];
@@ -272,19 +287,11 @@ __global__ __launch_bounds__(kThreads) void tree_expand_kernel(const ExpandArgs 
 #pragma unroll
     for (int t = 0; t < EPV; ++t) {
       const int64_t id = vi * EPV + t;
-      float f = kNegInf;
-      bool ok = false;
-      if (vi < full_vecs) {
-        f = to_float(e[t]);
-        ok = true;
-      } else if (id < a.vocab) {
-        f = to_float(x[id]);
-        ok = true;
-      }
+      const float f = to_float(e[t]);
       v[j * EPV + t] = f;
-      key[j * EPV + t] =
-          ok ? chunk_key<T>(f, static_cast<uint32_t>(id), static_cast<int>(id - static_cast<int64_t>(chunk) * kChunk))
-             : CK{0};
+      key[j * EPV + t] = id < a.vocab ? chunk_key<T>(f, static_cast<uint32_t>(id),
+                                                     static_cast<int>(id - static_cast<int64_t>(chunk) * kChunk))
+                                      : CK{0};
     }
   }
 
