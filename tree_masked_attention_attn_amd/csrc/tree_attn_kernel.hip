@@ -1457,46 +1457,56 @@ void tree_attn_bf16_kernel(const TreeAttnArgs a) {
   }
   __syncthreads();  // every wave is done with the rings: reuse them below
 
-  // Merge the two key halves: waves kh = 1 hand (m, l, O) to waves kh = 0
-  // through LDS in lane order (conflict-free). 32-row tile t = 2 rg + nt of
-  // the block goes to [t * 32 D floats], its (m, l) pairs after the 4 tiles.
-  constexpr int TILE_F4 = 32 * D / 4;
+  // Merge the two key halves. The waves of a row group (kh = 0 and 1) each
+  // finish half of the head_dim columns: each hands the partner, through
+  // LDS in lane order (conflict-free), the other half of its O and its
+  // (m, l), then combines and writes out its own half, so all 8 waves share
+  // the combine and the stores. Both sides combine in one order, kh = 0's
+  // terms first, as one wave combining every column would.
+  constexpr int DT = D / 32, HD = DT / 2;  // 32-column blocks of O, half of them per wave
+  constexpr int SLOT_F4 = HD * 4 * 64;     // f32x4 of one (tile, key half)'s handed-over columns
   f32x4* xo = reinterpret_cast<f32x4*>(lds);
-  float2* xml = reinterpret_cast<float2*>(lds + 4 * TILE_F4 * 16);
+  float2* xml = reinterpret_cast<float2*>(lds + 8 * SLOT_F4 * 16);
   float l_tot[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) l_tot[nt] = w.l_run[nt] + __shfl_xor(w.l_run[nt], 32);
-  if (kh == 1) {
+  auto merge_halves = [&](auto kh_tag) {
+    constexpr int KH = decltype(kh_tag)::value;
+    constexpr int MINE = KH * HD, THEIRS = (1 - KH) * HD;  // first column block of each half
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const int t = NT * rg + nt;
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
+      for (int i = 0; i < HD; ++i)
 #pragma unroll
         for (int jq = 0; jq < 4; ++jq)
-          xo[t * TILE_F4 + (dt * 4 + jq) * 64 + lane] =
-              f32x4{w.o[nt][dt][4 * jq], w.o[nt][dt][4 * jq + 1], w.o[nt][dt][4 * jq + 2], w.o[nt][dt][4 * jq + 3]};
-      if (half == 0) xml[t * 32 + l32] = make_float2(w.m_ref[nt], l_tot[nt]);
+          xo[(t * 2 + KH) * SLOT_F4 + (i * 4 + jq) * 64 + lane] =
+              f32x4{w.o[nt][THEIRS + i][4 * jq], w.o[nt][THEIRS + i][4 * jq + 1], w.o[nt][THEIRS + i][4 * jq + 2],
+                    w.o[nt][THEIRS + i][4 * jq + 3]};
+      if (half == 0) xml[(t * 2 + KH) * 32 + l32] = make_float2(w.m_ref[nt], l_tot[nt]);
     }
-  }
-  __syncthreads();
-  if (kh == 0) {
+    __syncthreads();
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const int t = NT * rg + nt;
-      const float2 other = xml[t * 32 + l32];
+      const float2 other = xml[(t * 2 + 1 - KH) * 32 + l32];
       const float M = fmaxf(w.m_ref[nt], other.x);
-      const float w0 = w.m_ref[nt] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(w.m_ref[nt] - M);
-      const float w1 = other.x == kNegInf ? 0.f : __builtin_amdgcn_exp2f(other.x - M);
+      const float wm = w.m_ref[nt] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(w.m_ref[nt] - M);
+      const float wo = other.x == kNegInf ? 0.f : __builtin_amdgcn_exp2f(other.x - M);
+      // (weight, values) of key half 0 first
+      const float w0 = KH == 0 ? wm : wo, w1 = KH == 0 ? wo : wm;
       w.m_ref[nt] = M;
-      l_tot[nt] = w0 * l_tot[nt] + w1 * other.y;
+      l_tot[nt] = KH == 0 ? w0 * l_tot[nt] + w1 * other.y : w0 * other.y + w1 * l_tot[nt];
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
+      for (int i = 0; i < HD; ++i)
 #pragma unroll
         for (int jq = 0; jq < 4; ++jq) {
-          const f32x4 y = xo[t * TILE_F4 + (dt * 4 + jq) * 64 + lane];
+          const f32x4 y = xo[(t * 2 + 1 - KH) * SLOT_F4 + (i * 4 + jq) * 64 + lane];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) w.o[nt][dt][4 * jq + i] = w0 * w.o[nt][dt][4 * jq + i] + w1 * y[i];
+          for (int e = 0; e < 4; ++e) {
+            const float o = w.o[nt][MINE + i][4 * jq + e];
+            w.o[nt][MINE + i][4 * jq + e] = KH == 0 ? w0 * o + w1 * y[e] : w0 * y[e] + w1 * o;
+          }
         }
     }
     if (a.splits == 1) {
@@ -1506,9 +1516,10 @@ void tree_attn_bf16_kernel(const TreeAttnArgs a) {
         __bf16* orow = static_cast<__bf16*>(a.out) + ((size_t)node[nt] * a.n_q_heads + head[nt]) * D;
         const float inv = 1.f / l_tot[nt];
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
+        for (int i = 0; i < HD; ++i)
 #pragma unroll
           for (int jq = 0; jq < 4; ++jq) {
+            const int dt = MINE + i;
             f32x4 x = {w.o[nt][dt][4 * jq], w.o[nt][dt][4 * jq + 1], w.o[nt][dt][4 * jq + 2], w.o[nt][dt][4 * jq + 3]};
             store4<__bf16>(orow + 32 * dt + 8 * jq + 4 * half, x * inv);
           }
@@ -1523,16 +1534,20 @@ void tree_attn_bf16_kernel(const TreeAttnArgs a) {
         const int t = NT * rg + nt;  // 32-row tile of the block
         if (32 * t >= block_rows) continue;  // padding rows: never merged
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
+        for (int i = 0; i < HD; ++i)
 #pragma unroll
-          for (int jq = 0; jq < 4; ++jq)
-            put_partial(sink, ((t * (D / 32) + dt) * 4 + jq) * 64 + lane,
+          for (int jq = 0; jq < 4; ++jq) {
+            const int dt = MINE + i;
+            put_partial(sink, ((t * DT + dt) * 4 + jq) * 64 + lane,
                         f32x4{w.o[nt][dt][4 * jq], w.o[nt][dt][4 * jq + 1], w.o[nt][dt][4 * jq + 2],
                               w.o[nt][dt][4 * jq + 3]});
-        if (half == 0) put_ml(sink, 32 * t + l32, w.m_ref[nt], l_tot[nt]);
+          }
+        if (KH == 0 && half == 0) put_ml(sink, 32 * t + l32, w.m_ref[nt], l_tot[nt]);
       }
     }
-  }
+  };
+  if (kh == 0) merge_halves(std::integral_constant<int, 0>{});
+  else merge_halves(std::integral_constant<int, 1>{});
   if (a.splits == 1) return;
   split_handoff<__bf16, D, kBfThreads<NT>>(a, &s_flags, &s_taken, grp, g, rb, split, tid);
 }
