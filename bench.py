@@ -18,8 +18,10 @@ Timing: inputs are resident in HBM before the timed region. ``--rotate`` input
 sets are cycled so that the working set exceeds twice the 256 MB Infinity
 Cache (each set is one layer's K/V, as in a real step where the other layers
 have evicted it). A short device sleep is queued first so the host runs ahead
-and the kernels execute back to back. HIP events on the launch stream bracket
-the timed region of K whole steps (-> ms_per_step), then K launches of each
+and the kernels execute back to back. HIP events on the launch stream
+(created without the system-scope fence, so that recording them writes back
+no caches) bracket the timed region of K whole steps (-> ms_per_step), then K
+launches of each
 kernel alone, each between its own events (-> its mean launch duration, which
 the roofline uses, and the spread), then the same launches back to back
 (-> the launch period, dispatch gaps included). Prints ONE JSON line.
@@ -34,6 +36,7 @@ Counter support (the traffic figure of the roofline):
 """
 
 import argparse
+import ctypes
 import csv
 import glob
 import hashlib
@@ -61,6 +64,66 @@ KERNEL_SOURCES = ["tree_masked_attention_attn_amd/csrc/tree_attn_kernel.hip",
                   "tree_masked_attention_attn_amd/csrc/plan.h",
                   "tree_masked_attention_attn_amd/csrc/api.cpp"]
 PROFILES = os.path.join(ROOT, "profiles")
+
+
+# --------------------------------------------------------------------------
+# Timing events: HIP events created with hipEventDisableSystemFence, recorded
+# on the launch stream. The default events of torch add a system-scope cache
+# write-back and invalidation at every record, which lengthens the measured
+# interval of short kernels by 1-3 us and slows the work after it; these
+# record a timestamp only (the HIP runtime documents the flag for timing).
+
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
+_HIP = None
+
+
+def _hip():
+    """The HIP runtime the process already uses (torch's), for its events."""
+    global _HIP
+    if _HIP is None:
+        import torch
+        torch.cuda.init()
+        path = None
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64.so" in line:
+                    path = line.split()[-1]
+                    break
+        if path is None:
+            raise RuntimeError("the HIP runtime is not loaded in this process")
+        L = ctypes.CDLL(path)
+        L.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        L.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        _HIP = L
+    return _HIP
+
+
+class Ev:
+    """A timing event on a torch stream (record, then elapsed_time in ms)."""
+
+    def __init__(self):
+        self.h = ctypes.c_void_p()
+        rc = _hip().hipEventCreateWithFlags(ctypes.byref(self.h), HIP_EVENT_DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+
+    def record(self, stream):
+        rc = _hip().hipEventRecord(self.h, ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_time(self, end):
+        ms = ctypes.c_float()
+        rc = _hip().hipEventElapsedTime(ctypes.byref(ms), self.h, end.h)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def __del__(self):
+        if self.h and _HIP is not None:
+            _HIP.hipEventDestroy(self.h)
 
 
 def kernel_source_sha():
@@ -552,7 +615,7 @@ def main_loop(args, cfg):
                 kd.copy_(kinit)
                 vd.copy_(vinit)
             flush.fill_(j & 255)
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)] if timed_events else None
+            e = [Ev() for _ in range(3)] if timed_events else None
             if e:
                 e[0].record(stream)
             ta.tree_attn(it["q"], kd, vd, it["P"], it["parent"], out=out, workspace=ws)
@@ -711,9 +774,9 @@ def main():
     def timed(fn, count, each=False):
         """Run fn(0..count-1) on the stream between two HIP events; with
         each=True also bracket every call with its own pair."""
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        evs = [(Ev(), Ev())
                for _ in range(count if each else 0)]
-        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0, t1 = Ev(), Ev()
         torch.cuda.synchronize()
         queue_ahead(20 * max(1, count / 200))
         wall = time.perf_counter()
