@@ -30,7 +30,11 @@
 // steps (row mirror, half-row mirror, two quad swaps, two row broadcasts)
 // merge all 64 lanes' lists into lane 63's. Keys are unique (they carry the
 // token, or leaf and slot), so the result is the same set in the same order
-// as k rounds of "take the largest" would give.
+// as k rounds of "take the largest" would give. For bf16 logits the leaf
+// merge works on 32-bit keys (value, chunk, slot in the chunk's list), the
+// token read back from that list. The final choice among w * k <= 64
+// candidates is by rank: each lane holds one and counts the keys above its
+// own, with no dependent chain of merges.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -99,19 +103,27 @@ __device__ __forceinline__ ChunkKey<T> chunk_key(float f, uint32_t id, int local
     return (order_key(f) & 0xffff0000u) | static_cast<uint32_t>(kChunk - 1 - local);
 }
 
-// The 64-bit (value, ~token) key of a chunk key (zero stays zero).
-template <typename T>
-__device__ __forceinline__ u64 global_key(ChunkKey<T> k, int chunk) {
-  if constexpr (std::is_same_v<T, float>) {
-    return k;
-  } else {
-    if (k == 0) return 0ull;
-    const uint32_t hi = k & 0xffff0000u;
-    const uint32_t ok = hi | ((hi & 0x80000000u) ? 0u : 0xffffu);  // the orderable image's low half
-    const uint32_t id = static_cast<uint32_t>(chunk * kChunk + (kChunk - 1 - static_cast<int>(k & 0xfffu)));
-    return (static_cast<u64>(ok) << 32) | static_cast<u64>(~id);
-  }
+// A bf16 chunk key's logit and token (chunk `chunk`): the value's orderable
+// image is its top half, the low half being all ones for a negative value
+// and zero otherwise.
+__device__ __forceinline__ float chunk_key_value(uint32_t k) {
+  const uint32_t hi = k & 0xffff0000u;
+  return key_value(hi | ((hi & 0x80000000u) ? 0u : 0xffffu));
 }
+__device__ __forceinline__ int chunk_key_token(uint32_t k, int chunk) {
+  return chunk * kChunk + (kChunk - 1 - static_cast<int>(k & 0xfffu));
+}
+
+// Leaf-level key of slot r of chunk c's list (bf16): the value's 16-bit
+// image, then the lower chunk, then the lower slot. Chunks cover ascending
+// token ranges and a chunk's list is in (value, lower token) order, so this
+// 32-bit key orders candidates exactly as (value, lower token) does; the
+// token is read back from the chunk's list. Zero stays zero (an empty slot);
+// a real key is never zero since 64 - c >= 1.
+__device__ __forceinline__ uint32_t leaf_key(uint32_t ck, int c, int r) {
+  return ck == 0 ? 0u : (ck & 0xffff0000u) | (static_cast<uint32_t>(64 - c) << 4) | static_cast<uint32_t>(15 - r);
+}
+static_assert(kExpandMaxChunks <= 64 && kExpandMaxK <= 16, "leaf key fields");
 
 template <typename K>
 __device__ __forceinline__ K kmax(K a, K b) { return a > b ? a : b; }
@@ -329,15 +341,19 @@ __global__ __launch_bounds__(kThreads) void tree_expand_kernel(const ExpandArgs 
   for (int i = 0; i < L; ++i) c4[i] = lane < 4 ? s_key[lane][i] : CK{0};
   merge_lanes<dpp::kXor1, 0xF>(c4);
   merge_lanes<dpp::kXor2, 0xF>(c4);  // lane 0: the chunk's L best
-  const u64 mine = global_key<T>(spread_list<L>(c4, 0, lane, K), chunk);
+  const CK mine = spread_list<L>(c4, 0, lane, K);  // lane i < K: the chunk's key i
   float cm = s_m[0], cs = s_s[0];
 #pragma unroll
   for (int w = 1; w < 4; ++w) lse_merge(cm, cs, s_m[w], s_s[w]);
 
   const int cslot = kExpandChunkBase + (row * kExpandMaxChunks + chunk) * kExpandChunkSlot;
-  if (lane < K)
-    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, mine), ws, cslot + 8 + 8 * lane, 0,
-                                          kWriteThrough);
+  if (lane < K) {
+    if constexpr (std::is_same_v<T, float>)
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, mine), ws, cslot + 8 + 8 * lane, 0,
+                                            kWriteThrough);
+    else
+      __builtin_amdgcn_raw_buffer_store_b32(mine, ws, cslot + 8 + 4 * lane, 0, kWriteThrough);
+  }
   if (lane == 0)
     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, make_float2(cm, cs)), ws, cslot, 0,
                                           kWriteThrough);
@@ -354,29 +370,68 @@ __global__ __launch_bounds__(kThreads) void tree_expand_kernel(const ExpandArgs 
   // (device-scope loads: they see memory as the count did), a sorted list.
   const float s_leaf = a.path_scores[row];
   float lm = kNegInf, ls = 0.f;
-  u64 kk[L];
+  float score = 0.f;
+  int tok = -1;
+  if constexpr (std::is_same_v<T, float>) {
+    u64 kk[L];
 #pragma unroll
-  for (int r = 0; r < L; ++r) kk[r] = 0;
-  if (lane < a.chunks) {
-    const int sl = kExpandChunkBase + (row * kExpandMaxChunks + lane) * kExpandChunkSlot;
-    const float2 ms = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(ws, sl, 0, kWriteThrough));
-    lm = ms.x;
-    ls = ms.y;
+    for (int r = 0; r < L; ++r) kk[r] = 0;
+    if (lane < a.chunks) {
+      const int sl = kExpandChunkBase + (row * kExpandMaxChunks + lane) * kExpandChunkSlot;
+      const float2 ms = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(ws, sl, 0, kWriteThrough));
+      lm = ms.x;
+      ls = ms.y;
 #pragma unroll
-    for (int r = 0; r < L; ++r)
-      if (r < K) kk[r] = __builtin_bit_cast(u64, __builtin_amdgcn_raw_buffer_load_b64(ws, sl + 8 + 8 * r, 0, kWriteThrough));
+      for (int r = 0; r < L; ++r)
+        if (r < K)
+          kk[r] = __builtin_bit_cast(u64, __builtin_amdgcn_raw_buffer_load_b64(ws, sl + 8 + 8 * r, 0, kWriteThrough));
+    }
+    lse_wave(lm, ls);
+    const int at2 = wave_top<L>(kk, a.chunks);  // lane at2: the leaf's L best
+    const u64 rk = spread_list<L>(kk, at2, lane, K);
+    score = key_value(static_cast<uint32_t>(rk >> 32));
+    tok = rk != 0 ? static_cast<int>(~static_cast<uint32_t>(rk)) : -1;
+  } else {
+    // 32-bit leaf keys (value, chunk, slot); the chunks' lists stay in LDS
+    // for the token look-up.
+    __shared__ uint32_t s_ck[kExpandMaxChunks][L];
+    uint32_t lk[L];
+#pragma unroll
+    for (int r = 0; r < L; ++r) lk[r] = 0;
+    if (lane < a.chunks) {
+      const int sl = kExpandChunkBase + (row * kExpandMaxChunks + lane) * kExpandChunkSlot;
+      const float2 ms = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(ws, sl, 0, kWriteThrough));
+      lm = ms.x;
+      ls = ms.y;
+#pragma unroll
+      for (int r = 0; r < L; ++r) {
+        if (r < K) {
+          const uint32_t ck = __builtin_amdgcn_raw_buffer_load_b32(ws, sl + 8 + 4 * r, 0, kWriteThrough);
+          s_ck[lane][r] = ck;
+          lk[r] = leaf_key(ck, lane, r);
+        }
+      }
+    }
+    lse_wave(lm, ls);
+    const int at2 = wave_top<L>(lk, a.chunks);  // lane at2: the leaf's L best
+    const uint32_t rk = spread_list<L>(lk, at2, lane, K);
+    // the LDS writes above come before these reads in every lane's program
+    // order; LDS serves one wave's accesses in issue order
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    if (rk != 0) {
+      const int c = 64 - static_cast<int>((rk >> 4) & 127u), r = 15 - static_cast<int>(rk & 15u);
+      const uint32_t ck = s_ck[c][r];
+      score = chunk_key_value(ck);
+      tok = chunk_key_token(ck, c);
+    }
   }
-  lse_wave(lm, ls);
   const float log_sum = __logf(ls);  // logsumexp = lm + log_sum
-  const int at2 = wave_top<L>(kk, a.chunks);  // lane at2: the leaf's L best
-  const u64 rk = spread_list<L>(kk, at2, lane, K);
   const int rslot = kExpandRowBase + row * kExpandRowSlot;
   if (lane < K) {
     // slot `lane` of this leaf: (score, token), or token -1 when the leaf
     // has fewer than K tokens
-    const float score = s_leaf + ((key_value(static_cast<uint32_t>(rk >> 32)) - lm) - log_sum);
-    const int tok = rk != 0 ? static_cast<int>(~static_cast<uint32_t>(rk)) : -1;
-    __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(score), static_cast<unsigned>(tok)}, ws,
+    const float sc = s_leaf + ((score - lm) - log_sum);
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(sc), static_cast<unsigned>(tok)}, ws,
                                           rslot + 8 * lane, 0, kWriteThrough);
   }
   asm volatile("" ::: "memory");
@@ -387,8 +442,49 @@ __global__ __launch_bounds__(kThreads) void tree_expand_kernel(const ExpandArgs 
                                          "agent") == static_cast<unsigned>(a.w - 1);
   if (!__builtin_amdgcn_readfirstlane(last)) return;
 
-  // The last leaf: lane l holds leaf l's K (score, token) in slot order, as
-  // keys (score, then the lower leaf, then the lower slot): a sorted list.
+  // The last leaf. Candidate (leaf i, slot r) has the key (score, then the
+  // lower leaf, then the lower slot); zero for an empty slot, below every
+  // real key. At least K candidates are real (k <= w * vocab), and real keys
+  // are unique.
+  const int n = a.w * K;
+  if (n <= 64) {
+    // One candidate per lane, lane = leaf * K + slot: a candidate is chosen
+    // iff fewer than K keys exceed its own, and the chosen lanes, in lane
+    // order, are already in (leaf, slot) order.
+    __shared__ u64 s_hk[64];
+    int leaf = 0, slot = 0, ctok = -1;
+    float csc = 0.f;
+    u64 hk = 0;
+    if (lane < n) {
+      leaf = lane / K;
+      slot = lane - leaf * K;
+      const u32x2 p = __builtin_bit_cast(
+          u32x2, __builtin_amdgcn_raw_buffer_load_b64(ws, kExpandRowBase + leaf * kExpandRowSlot + 8 * slot, 0,
+                                                      kWriteThrough));
+      csc = __uint_as_float(p.x);
+      ctok = static_cast<int>(p.y);
+      hk = ctok >= 0 ? (static_cast<u64>(order_key(csc)) << 32) |
+                           static_cast<u64>(~static_cast<uint32_t>((leaf << 8) | slot))
+                     : 0ull;
+    }
+    s_hk[lane] = hk;
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    int above = 0;
+#pragma unroll
+    for (int j = 0; j < 64; ++j) above += s_hk[j] > hk ? 1 : 0;
+    const bool chosen = lane < n && hk != 0 && above < K;
+    const u64 sel = __ballot(chosen);
+    if (chosen) {
+      const int pos = __popcll(sel & ((1ull << lane) - 1ull));
+      a.leaf_out[pos] = leaf;
+      a.token_out[pos] = ctok;
+      a.score_out[pos] = csc;
+    }
+    return;
+  }
+
+  // More candidates than lanes: lane l holds leaf l's K (score, token) in
+  // slot order, a sorted list, and the lists are merged.
   __shared__ float s_sc[kExpandMaxRows][L];
   __shared__ int s_tk[kExpandMaxRows][L];
   u64 hk[L];
