@@ -51,6 +51,8 @@ constexpr int kThreads = 256;
 constexpr int kPerThread = 16;                 // logits per thread
 constexpr int kChunk = kThreads * kPerThread;  // logits per workgroup
 constexpr int kWriteThrough = 16;              // cache policy of workspace traffic (sc1)
+constexpr int kKeysAt = 16;                    // a chunk slot: (max, sum), pad, then k keys (16-byte loads)
+static_assert(kKeysAt + 8 * kExpandMaxK <= kExpandChunkSlot, "chunk slot size");
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_huge_valf();
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
@@ -66,26 +68,30 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2
   s = a + b;
 }
 
-// (max, sum) of the whole wave, returned to every lane.
-__device__ __forceinline__ void lse_wave(float& m, float& s) {
-  lse_merge(m, s, dpp_f32<dpp::kXor1>(m), dpp_f32<dpp::kXor1>(s));
-  lse_merge(m, s, dpp_f32<dpp::kXor2>(m), dpp_f32<dpp::kXor2>(s));
-  lse_merge(m, s, dpp_f32<dpp::kRor4>(m), dpp_f32<dpp::kRor4>(s));
-  lse_merge(m, s, dpp_f32<dpp::kRor8>(m), dpp_f32<dpp::kRor8>(s));
-  float m0 = readlane_f32(m, 0), s0 = readlane_f32(s, 0);
-  lse_merge(m0, s0, readlane_f32(m, 16), readlane_f32(s, 16));
-  lse_merge(m0, s0, readlane_f32(m, 32), readlane_f32(s, 32));
-  lse_merge(m0, s0, readlane_f32(m, 48), readlane_f32(s, 48));
-  m = m0;
-  s = s0;
+// Maximum and sum over the wave, returned to every lane: DPP steps inside
+// each 16-lane row, then the four rows' results. A logsumexp takes the
+// wave's maximum first and sums exp(x - max) after it, so no exponential
+// sits on the reduction's dependent chain.
+__device__ __forceinline__ float wave_max_f32(float x) {
+  x = fmaxf(x, dpp_f32<dpp::kXor1>(x));
+  x = fmaxf(x, dpp_f32<dpp::kXor2>(x));
+  x = fmaxf(x, dpp_f32<dpp::kRor4>(x));
+  x = fmaxf(x, dpp_f32<dpp::kRor8>(x));
+  return fmaxf(fmaxf(readlane_f32(x, 0), readlane_f32(x, 16)), fmaxf(readlane_f32(x, 32), readlane_f32(x, 48)));
+}
+__device__ __forceinline__ float wave_sum_f32(float x) {
+  x += dpp_f32<dpp::kXor1>(x);
+  x += dpp_f32<dpp::kXor2>(x);
+  x += dpp_f32<dpp::kRor4>(x);
+  x += dpp_f32<dpp::kRor8>(x);
+  return (readlane_f32(x, 0) + readlane_f32(x, 16)) + (readlane_f32(x, 32) + readlane_f32(x, 48));
 }
 
-template <typename T>
-__device__ __forceinline__ float to_float(T x) {
-  if constexpr (std::is_same_v<T, float>)
-    return x;
-  else
-    return __uint_as_float(static_cast<uint32_t>(__builtin_bit_cast(uint16_t, x)) << 16);
+// (max, sum of exp(x - max)) over the wave from every lane's own pair.
+__device__ __forceinline__ void lse_wave(float& m, float& s) {
+  const float M = wave_max_f32(m);
+  s = wave_sum_f32(m == kNegInf ? 0.f : s * __builtin_amdgcn_exp2f((m - M) * kLog2e));
+  m = M;
 }
 
 // Keys inside one chunk. bf16 logits: the top 16 bits of the value's
@@ -101,6 +107,20 @@ __device__ __forceinline__ ChunkKey<T> chunk_key(float f, uint32_t id, int local
     return cand_key(f, id);
   else
     return (order_key(f) & 0xffff0000u) | static_cast<uint32_t>(kChunk - 1 - local);
+}
+
+// The 16-bit orderable images of the two bf16 values in x (low half, high
+// half), as chunk_key takes them: a negative value's bits inverted, a
+// non-negative one's sign bit set, -0.0 taken as +0.0. Packed 16-bit integer
+// operations handle both halves at once.
+typedef short i16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16_pair_images(uint32_t x) {
+  const uint32_t mag = x & 0x7fff7fffu;
+  const i16x2 neg = __builtin_bit_cast(i16x2, x) >> 15;  // all ones where the sign bit is set
+  const i16x2 nz = __builtin_bit_cast(i16x2, __builtin_bit_cast(u16x2, mag) + u16x2{0x7fff, 0x7fff}) >>
+                   15;  // all ones where the magnitude is not zero
+  return (mag | 0x80008000u) ^ __builtin_bit_cast(uint32_t, neg & nz);
 }
 
 // A bf16 chunk key's logit and token (chunk `chunk`): the value's orderable
@@ -265,6 +285,9 @@ __global__ __launch_bounds__(kThreads) void tree_expand_kernel(const ExpandArgs 
   const T* x = static_cast<const T*>(a.logits) + static_cast<size_t>(row) * a.row_stride;
   const int64_t full_vecs = a.vocab / EPV;
   const __amdgpu_buffer_rsrc_t ws = __builtin_amdgcn_make_buffer_rsrc(a.ws, 0, a.ws_bytes, 0x00020000);
+  // loaded by every workgroup with the logits, its latency hidden there,
+  // though only the leaf's last chunk uses it
+  const float s_leaf = a.path_scores[row];
 
   // Thread tid reads vectors tid, tid + 256, .. of the chunk: whole vectors
   // with 16-byte loads; a vector that would run past the vocabulary (only
@@ -295,28 +318,50 @@ __global__ __launch_bounds__(kThreads) void tree_expand_kernel(const ExpandArgs 
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     const int64_t vi = static_cast<int64_t>(chunk) * (kChunk / EPV) + j * kThreads + tid;
-    const T* e = reinterpret_cast<const T*>(&buf[j]);
+    if constexpr (std::is_same_v<T, float>) {
+      const T* e = reinterpret_cast<const T*>(&buf[j]);
 #pragma unroll
-    for (int t = 0; t < EPV; ++t) {
-      const int64_t id = vi * EPV + t;
-      const float f = to_float(e[t]);
-      v[j * EPV + t] = f;
-      key[j * EPV + t] = id < a.vocab ? chunk_key<T>(f, static_cast<uint32_t>(id),
-                                                     static_cast<int>(id - static_cast<int64_t>(chunk) * kChunk))
-                                      : CK{0};
+      for (int t = 0; t < EPV; ++t) {
+        const int64_t id = vi * EPV + t;
+        const float f = e[t];
+        v[j * EPV + t] = f;
+        key[j * EPV + t] = id < a.vocab ? chunk_key<T>(f, static_cast<uint32_t>(id),
+                                                       static_cast<int>(id - static_cast<int64_t>(chunk) * kChunk))
+                                        : CK{0};
+      }
+    } else {
+      // two logits per 32-bit word: both keys' value images at once, then
+      // each with its in-chunk index; slots past the vocabulary (only in a
+      // vector that runs past it) are emptied afterwards
+      const int local = (j * kThreads + tid) * EPV;  // in-chunk index of the vector's first logit
+#pragma unroll
+      for (int q = 0; q < EPV / 2; ++q) {
+        const uint32_t x = buf[j][q];
+        const uint32_t k2 = bf16_pair_images(x);
+        v[j * EPV + 2 * q] = __uint_as_float(x << 16);
+        v[j * EPV + 2 * q + 1] = __uint_as_float(x & 0xffff0000u);
+        key[j * EPV + 2 * q] = (k2 << 16) | static_cast<uint32_t>(kChunk - 1 - local - 2 * q);
+        key[j * EPV + 2 * q + 1] = (k2 & 0xffff0000u) | static_cast<uint32_t>(kChunk - 2 - local - 2 * q);
+      }
+      if (vi >= full_vecs) {
+#pragma unroll
+        for (int t = 0; t < EPV; ++t)
+          if (vi * EPV + t >= a.vocab) key[j * EPV + t] = 0;
+      }
     }
   }
 
-  // This thread's (max, sum of exp).
+  // The wave's (max, sum of exp): the maximum first.
   float m = kNegInf;
 #pragma unroll
   for (int i = 0; i < kPerThread; ++i) m = fmaxf(m, v[i]);
+  m = wave_max_f32(m);
   float s = 0.f;
   if (m != kNegInf) {
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) s += __builtin_amdgcn_exp2f((v[i] - m) * kLog2e);
   }
-  lse_wave(m, s);
+  s = wave_sum_f32(s);
 
   // The wave's L best keys, then the workgroup's (wave 0, lane 0).
   __shared__ CK s_key[4][L];
@@ -349,10 +394,10 @@ __global__ __launch_bounds__(kThreads) void tree_expand_kernel(const ExpandArgs 
   const int cslot = kExpandChunkBase + (row * kExpandMaxChunks + chunk) * kExpandChunkSlot;
   if (lane < K) {
     if constexpr (std::is_same_v<T, float>)
-      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, mine), ws, cslot + 8 + 8 * lane, 0,
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, mine), ws, cslot + kKeysAt + 8 * lane, 0,
                                             kWriteThrough);
     else
-      __builtin_amdgcn_raw_buffer_store_b32(mine, ws, cslot + 8 + 4 * lane, 0, kWriteThrough);
+      __builtin_amdgcn_raw_buffer_store_b32(mine, ws, cslot + kKeysAt + 4 * lane, 0, kWriteThrough);
   }
   if (lane == 0)
     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, make_float2(cm, cs)), ws, cslot, 0,
@@ -368,7 +413,6 @@ __global__ __launch_bounds__(kThreads) void tree_expand_kernel(const ExpandArgs 
 
   // The leaf's last chunk: lane c reads chunk c's (max, sum) and its K keys
   // (device-scope loads: they see memory as the count did), a sorted list.
-  const float s_leaf = a.path_scores[row];
   float lm = kNegInf, ls = 0.f;
   float score = 0.f;
   int tok = -1;
@@ -382,9 +426,13 @@ __global__ __launch_bounds__(kThreads) void tree_expand_kernel(const ExpandArgs 
       lm = ms.x;
       ls = ms.y;
 #pragma unroll
-      for (int r = 0; r < L; ++r)
-        if (r < K)
-          kk[r] = __builtin_bit_cast(u64, __builtin_amdgcn_raw_buffer_load_b64(ws, sl + 8 + 8 * r, 0, kWriteThrough));
+      for (int q = 0; q < L / 2; ++q) {
+        if (2 * q < K) {
+          const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(ws, sl + kKeysAt + 16 * q, 0, kWriteThrough);
+          kk[2 * q] = (static_cast<u64>(v.y) << 32) | v.x;
+          if (2 * q + 1 < K) kk[2 * q + 1] = (static_cast<u64>(v.w) << 32) | v.z;
+        }
+      }
     }
     lse_wave(lm, ls);
     const int at2 = wave_top<L>(kk, a.chunks);  // lane at2: the leaf's L best
@@ -404,11 +452,17 @@ __global__ __launch_bounds__(kThreads) void tree_expand_kernel(const ExpandArgs 
       lm = ms.x;
       ls = ms.y;
 #pragma unroll
-      for (int r = 0; r < L; ++r) {
-        if (r < K) {
-          const uint32_t ck = __builtin_amdgcn_raw_buffer_load_b32(ws, sl + 8 + 4 * r, 0, kWriteThrough);
-          s_ck[lane][r] = ck;
-          lk[r] = leaf_key(ck, lane, r);
+      for (int q = 0; q < L / 4; ++q) {
+        if (4 * q < K) {
+          const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(ws, sl + kKeysAt + 16 * q, 0, kWriteThrough);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * q + e;
+            if (r < K) {
+              s_ck[lane][r] = v[e];
+              lk[r] = leaf_key(v[e], lane, r);
+            }
+          }
         }
       }
     }
