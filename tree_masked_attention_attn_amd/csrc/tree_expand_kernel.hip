@@ -68,25 +68,9 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2
   s = a + b;
 }
 
-// Maximum and sum over the wave, returned to every lane: DPP steps inside
-// each 16-lane row, then the four rows' results. A logsumexp takes the
-// wave's maximum first and sums exp(x - max) after it, so no exponential
-// sits on the reduction's dependent chain.
-__device__ __forceinline__ float wave_max_f32(float x) {
-  x = fmaxf(x, dpp_f32<dpp::kXor1>(x));
-  x = fmaxf(x, dpp_f32<dpp::kXor2>(x));
-  x = fmaxf(x, dpp_f32<dpp::kRor4>(x));
-  x = fmaxf(x, dpp_f32<dpp::kRor8>(x));
-  return fmaxf(fmaxf(readlane_f32(x, 0), readlane_f32(x, 16)), fmaxf(readlane_f32(x, 32), readlane_f32(x, 48)));
-}
-__device__ __forceinline__ float wave_sum_f32(float x) {
-  x += dpp_f32<dpp::kXor1>(x);
-  x += dpp_f32<dpp::kXor2>(x);
-  x += dpp_f32<dpp::kRor4>(x);
-  x += dpp_f32<dpp::kRor8>(x);
-  return (readlane_f32(x, 0) + readlane_f32(x, 16)) + (readlane_f32(x, 32) + readlane_f32(x, 48));
-}
-
+// A logsumexp over a wave takes the wave's maximum first and sums
+// exp(x - max) after it (wave_max_f32, wave_sum_f32), so no exponential sits
+// on the reduction's dependent chain.
 // (max, sum of exp(x - max)) over the wave from every lane's own pair.
 __device__ __forceinline__ void lse_wave(float& m, float& s) {
   const float M = wave_max_f32(m);

@@ -100,6 +100,24 @@ __device__ __forceinline__ u64 wave_max_u64(u64 k) {
   return (static_cast<u64>(hi) << 32) | lo;
 }
 
+// Float maximum and sum over the wave, returned to every lane: DPP steps
+// inside each 16-lane row, then the four rows' results (a fixed order, so
+// the sum is the same on every call).
+__device__ __forceinline__ float wave_max_f32(float x) {
+  x = fmaxf(x, dpp_f32<dpp::kXor1>(x));
+  x = fmaxf(x, dpp_f32<dpp::kXor2>(x));
+  x = fmaxf(x, dpp_f32<dpp::kRor4>(x));
+  x = fmaxf(x, dpp_f32<dpp::kRor8>(x));
+  return fmaxf(fmaxf(readlane_f32(x, 0), readlane_f32(x, 16)), fmaxf(readlane_f32(x, 32), readlane_f32(x, 48)));
+}
+__device__ __forceinline__ float wave_sum_f32(float x) {
+  x += dpp_f32<dpp::kXor1>(x);
+  x += dpp_f32<dpp::kXor2>(x);
+  x += dpp_f32<dpp::kRor4>(x);
+  x += dpp_f32<dpp::kRor8>(x);
+  return (readlane_f32(x, 0) + readlane_f32(x, 16)) + (readlane_f32(x, 32) + readlane_f32(x, 48));
+}
+
 // Maximum of non-negative ints over the wave.
 __device__ __forceinline__ int wave_max_i32(int k) {
   return static_cast<int>(wave_max_u32(static_cast<uint32_t>(k)));
