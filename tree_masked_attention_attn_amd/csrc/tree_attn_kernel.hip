@@ -675,16 +675,23 @@ void tree_attn_kernel(const TreeAttnArgs a) {
 // ============================================================================
 // bf16 kernel. Same maths and hand-off as above, built for CDNA4's balance of
 // MFMA, VALU and LDS:
-//  * 4 waves, one per SIMD, = 2 row groups x 2 key halves. Wave (rg, kh) owns
-//    block rows 64 rg .. 64 rg + 63 (two 32-row MFMA N tiles) and, of every
-//    64-key stage, the 32-key half kh. Each K or V fragment read from LDS
-//    feeds two MFMAs (both row tiles), which halves the LDS traffic per MFMA
-//    against one tile per wave; the two key halves are merged through LDS at
-//    the end.
-//  * Software pipeline inside the wave: iteration s issues the QK MFMAs of
-//    stage s + 1 and the PV MFMAs of stage s - 1 while the VALU computes the
-//    softmax of stage s, so the matrix cores and the VALU work side by side
-//    (a single wave keeps both busy when their instructions interleave).
+//  * 8 waves, two per SIMD: 4 row groups (one 32-row MFMA N tile each) x 2
+//    key halves. Wave w takes row group w % 4 and, of every 64-key stage,
+//    the 32-key half w / 4; waves w and w + 4 share a SIMD. The two halves'
+//    partial rows are merged through LDS at the end, each wave of the pair
+//    combining and storing half of the head_dim columns.
+//  * The two waves of a SIMD run each iteration in opposite orders: one
+//    issues its MFMAs (PV of stage s - 1, QK of stage s + 1) and then the
+//    softmax of stage s, the other the softmax first. Between the workgroup
+//    barriers that start each iteration the matrix core works for one wave
+//    while the VALU works for the other.
+//  * A block of at most 64 query rows (the sparse instance) pairs each wave
+//    of real rows with a padding wave that only loads, so every real wave
+//    has its SIMD to itself; its softmax is then free to interleave with its
+//    MFMAs.
+//  * The template parameter NT = 2 (one wave per SIMD holding two row
+//    tiles, each K or V fragment feeding two MFMAs) builds and gives the
+//    same outputs, but runs slower than NT = 1, the default build.
 //  * K and V reach LDS by buffer-to-LDS DMA (no staging registers, no VALU)
 //    into two rings of four 64-key slots; each slot is refilled three
 //    iterations before it is read. Q and the ancestor table are staged the
