@@ -689,9 +689,11 @@ void tree_attn_kernel(const TreeAttnArgs a) {
 //    of real rows with a padding wave that only loads, so every real wave
 //    has its SIMD to itself; its softmax is then free to interleave with its
 //    MFMAs.
-//  * The template parameter NT = 2 (one wave per SIMD holding two row
-//    tiles, each K or V fragment feeding two MFMAs) builds and gives the
-//    same outputs, but runs slower than NT = 1, the default build.
+//  * NT (32-row tiles per wave) is 1. NT = 2, one wave per SIMD holding two
+//    row tiles so that each K or V fragment feeds two MFMAs, was measured as
+//    a variant of this kernel (its DMA split over four waves): same outputs,
+//    slower. The register state and the iteration keep the parameter; the
+//    DMA code here assumes eight waves.
 //  * K and V reach LDS by buffer-to-LDS DMA (no staging registers, no VALU)
 //    into two rings of four 64-key slots; each slot is refilled three
 //    iterations before it is read. Q and the ancestor table are staged the
