@@ -341,6 +341,7 @@ ta_status ta_kv_reroot(const ta_kv_cache* cache, int32_t prefix_len, const int32
     int32_t gcols = cols;
     while (gcols > 1 && rows * gcols > kRerootItemsPerThread * kRerootThreads) gcols /= 2;
     a.col_groups = cols / gcols;
+    a.gcols_rcp = div_rcp(gcols);
     hipError_t e = launch_kv_reroot(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return device_error(e, "kv_reroot launch");
   }

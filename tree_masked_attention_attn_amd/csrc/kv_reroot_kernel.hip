@@ -29,6 +29,7 @@ namespace {
 
 constexpr int kThreads = kRerootThreads;
 constexpr int kMaxItems = kRerootItemsPerThread;  // (row, 16-B column) items per thread
+static_assert(kMaxItems * kThreads < (1 << 17), "item numbers within the reciprocal division's range");
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(kThreads) void kv_reroot_kernel(const RerootArgs a) {
@@ -41,12 +42,18 @@ __global__ __launch_bounds__(kThreads) void kv_reroot_kernel(const RerootArgs a)
   const int c0 = cg * gcols;
   const int items = a.n_rows * gcols;
 
+  // item it is (row it / gcols, column it % gcols): the quotient by a
+  // multiply with the host's rounded-up reciprocal (exact for it < 2^17 and
+  // gcols < 2^15, as here) instead of a division sequence per item
+  auto row_of = [&](int it) {
+    return gcols == 1 ? it : static_cast<int>(__umulhi(static_cast<uint32_t>(it), a.gcols_rcp));
+  };
   uint4 val[kMaxItems];
 #pragma unroll
   for (int i = 0; i < kMaxItems; ++i) {
     const int it = threadIdx.x + i * kThreads;
     if (it < items) {
-      const int k = it / gcols, c = c0 + it % gcols;
+      const int k = row_of(it), c = c0 + it - k * gcols;
       if (a.src[k] != a.dst0 + k)
         val[i] = *reinterpret_cast<const uint4*>(base + (size_t)a.src[k] * a.row_bytes + c * 16);
     }
@@ -56,7 +63,7 @@ __global__ __launch_bounds__(kThreads) void kv_reroot_kernel(const RerootArgs a)
   for (int i = 0; i < kMaxItems; ++i) {
     const int it = threadIdx.x + i * kThreads;
     if (it < items) {
-      const int k = it / gcols, c = c0 + it % gcols;
+      const int k = row_of(it), c = c0 + it - k * gcols;
       if (a.src[k] != a.dst0 + k) {
         // the builtin takes a vector type; the items stay uint4 (an array of
         // vector-typed items compiled to a register copy per use)

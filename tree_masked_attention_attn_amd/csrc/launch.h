@@ -69,6 +69,7 @@ struct RerootArgs {
   int32_t n_rows;           // rows to place: n_accepted + n_surviving
   int32_t dst0;             // first destination slot (= prefix_len)
   int32_t col_groups;       // column groups per plane (grid.y)
+  uint32_t gcols_rcp;       // 2^32 / (columns per group) + 1, 0 for one column: item -> (row, column)
   int32_t src[kMaxTree];    // source slot of destination slot dst0 + k
 };
 
