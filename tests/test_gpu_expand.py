@@ -76,8 +76,10 @@ def check(logits, scores, k, what, stride_pad=0):
 
 
 @pytest.mark.parametrize("name", ["draft_expand_w8", "qwen2_72b_32k_verify", "llama3_70b_verify"])
-@pytest.mark.parametrize("w,k", [(8, 8), (1, 8), (8, 1), (64, 16), (3, 16)])
+@pytest.mark.parametrize("w,k", [(8, 8), (1, 8), (8, 1), (64, 16), (3, 16), (16, 4), (13, 5)])
 def test_expand_parity(name, w, k):
+    # w * k = 64 is the largest final choice made by rank (one candidate per
+    # lane); 65 and above merge the leaves' lists
     cfg = W.config(name)
     rng = np.random.default_rng(cfg["seed"] * 100 + w * 17 + k)
     x = W.make_expand_inputs(cfg, w, rng)
