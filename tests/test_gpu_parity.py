@@ -242,6 +242,11 @@ def edge_cases():
         "f32_split": (dict(n_q_heads=8, n_kv_heads=1, head_dim=64, dtype="f32", prefix=5000), rnd(50)),
         "f32_no_prefix": (dict(n_q_heads=2, n_kv_heads=1, head_dim=64, dtype="f32", prefix=0), rnd(64)),
         "long_small_tree": (dict(n_q_heads=8, n_kv_heads=8, head_dim=64, dtype="bf16", prefix=60000), rnd(3)),
+        # one key in all: the tree's single node attends only to itself
+        "single_token_no_prefix": (dict(n_q_heads=4, n_kv_heads=2, head_dim=128, dtype="bf16", prefix=0), [-1]),
+        # the tree starts exactly at a stage boundary and fills two stages
+        "stage_aligned_prefix": (dict(n_q_heads=8, n_kv_heads=2, head_dim=128, dtype="bf16", prefix=64),
+                                 deep_tree(rng, 128)),
         # 45 units (15 splits): a row block's splits are not all on one XCD,
         # so the hand-off between them crosses L2 caches
         "cross_xcd_groups": (dict(n_q_heads=6, n_kv_heads=3, head_dim=128, dtype="bf16", prefix=4000), rnd(20)),
