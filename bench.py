@@ -165,19 +165,19 @@ def reroot_bytes(cfg, src_rows, prefix, n_layers=1):
     return 2 * moved * 2 * cfg["n_kv_heads"] * cfg["head_dim"] * es * n_layers
 
 
-def split_partial_bytes(cfg, splits):
+def split_partial_bytes(cfg, splits, block_rows):
     """Bytes of split partials one tree_attn launch writes (and the merge
     reads back once): per unit and written row, a (max, sum) fp32 pair and O
-    in fp32. A unit writes its block's 128 rows; the bf16 kernel skips the
-    32-row tiles that lie wholly past the head's last query row. Overhead,
-    not algorithmic."""
+    in fp32. A unit writes its block's rows (block_rows of them, 128 or 64);
+    the bf16 kernel skips the 32-row tiles that lie wholly past the head's
+    last query row. Overhead, not algorithmic."""
     if splits <= 1:
         return 0
     rows = cfg["n_q_heads"] // cfg["n_kv_heads"] * (cfg["n_tree"] - cfg.get("q_first", 0))
     written = 0
-    for rb in range(-(-rows // 128)):
-        block = min(128, rows - 128 * rb)
-        written += 128 if cfg["dtype"] == "f32" else 32 * -(-block // 32)
+    for rb in range(-(-rows // block_rows)):
+        block = min(block_rows, rows - block_rows * rb)
+        written += block_rows if cfg["dtype"] == "f32" else 32 * -(-block // 32)
     return cfg["n_kv_heads"] * splits * written * (8 + cfg["head_dim"] * 4)
 
 
@@ -822,6 +822,7 @@ def main():
 
     nbytes, flops, anc = tree_attn_work(cfg, parent)
     splits = ta.tree_attn_num_splits(sets[0]["k"], sets[0]["v"], cfg["n_q_heads"], P, cfg["n_tree"], qf)
+    block_rows = ta.tree_attn_block_rows(sets[0]["k"], sets[0]["v"], cfg["n_q_heads"], P, cfg["n_tree"], qf)
     rr_bytes = reroot_bytes(cfg, src_rows, P)
     attn_mean = statistics.fmean(attn_us)
     rr_mean = statistics.fmean(reroot_us)
@@ -854,14 +855,14 @@ def main():
         "config": {"workload": cfg["name"], "n_q_heads": cfg["n_q_heads"], "n_kv_heads": cfg["n_kv_heads"],
                    "head_dim": cfg["head_dim"], "prefix_len": P, "n_tree": cfg["n_tree"], "q_first": qf,
                    "visible_tree_pairs": anc, "accepted_path": len(path), "survivors": len(surv),
-                   "rotated_sets": rotate, "splits": splits},
+                   "rotated_sets": rotate, "splits": splits, "block_rows": block_rows},
         "tree_attn": {"us_mean": round(attn_mean, 2), "us_p10": round(pct(attn_us, 10), 2),
                       "us_p50": round(pct(attn_us, 50), 2), "us_p90": round(pct(attn_us, 90), 2),
                       "us_launch_period_back_to_back": round(attn_b2b / K, 2),
                       "hot_cache_us_p50": round(hot_us, 2),
                       "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
-                      "split_partial_bytes_written": split_partial_bytes(cfg, splits),
-                      "split_partial_bytes_read": split_partial_bytes(cfg, splits),
+                      "split_partial_bytes_written": split_partial_bytes(cfg, splits, block_rows),
+                      "split_partial_bytes_read": split_partial_bytes(cfg, splits, block_rows),
                       "hbm_GBs": round(hbm_gbs, 1), "hbm_frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
                       "TFLOPs": round(tflops, 1), "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4)},
         "kv_reroot": {"us_mean": round(rr_mean, 2), "us_p50": round(pct(reroot_us, 50), 2),

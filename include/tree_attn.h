@@ -138,6 +138,16 @@ size_t ta_tree_attn_rows_workspace_bytes(const ta_kv_cache* cache, int32_t n_q_h
                                          int32_t prefix_len, int32_t n_tree, int32_t q_first);
 int32_t ta_tree_attn_rows_num_splits(const ta_kv_cache* cache, int32_t n_q_heads,
                                      int32_t prefix_len, int32_t n_tree, int32_t q_first);
+/*
+ * Query rows per row block of this call's launch (host only, no device
+ * access): 128, or 64 for bf16 heads of at most 64 query rows and for bf16
+ * launches whose 128-row blocks would leave CUs idle. A row block is the
+ * G * (n_tree - q_first) rows of one KV head cut into pieces of this size;
+ * the launch has n_kv_heads * ceil(rows / block) * splits workgroups.
+ * 0 on an invalid shape (ta_last_error says why).
+ */
+int32_t ta_tree_attn_rows_block_rows(const ta_kv_cache* cache, int32_t n_q_heads,
+                                     int32_t prefix_len, int32_t n_tree, int32_t q_first);
 
 /*
  * For callers that cannot allocate device memory or pass a workspace (code

@@ -239,6 +239,10 @@ void fuzz_attn_plan() {
   const int64_t bytes = static_cast<int64_t>(p.total_keys) * c.head_dim * (c.dtype == TA_F32 ? 4 : 2);
   CHECK(bytes < 2147483647);  // the kernels' 32-bit buffer ranges
   if (p.rows_per_head == 0) return;
+  // 128-row blocks, or 64 (bf16 only: always for heads of at most 64 rows)
+  CHECK(p.block_rows == 128 || (p.block_rows == 64 && c.dtype == TA_BF16));
+  if (c.dtype == TA_BF16 && p.rows_per_head <= 64) CHECK(p.block_rows == 64);
+  CHECK(p.row_blocks == (p.rows_per_head + p.block_rows - 1) / p.block_rows);
   CHECK(p.splits >= 1 && p.splits <= kMaxSplits);
   CHECK(p.splits <= p.n_tiles);  // every split has at least one stage
   CHECK(p.n_units == c.n_kv_heads * p.row_blocks * p.splits && p.n_units < kMaxUnits);

@@ -108,13 +108,18 @@ def test_traffic_record_scales_counters_by_the_copy_calibration(tmp_path, monkey
 def test_split_partial_bytes_match_the_traffic_excess_model():
     cfg = W.config("llama3_70b_verify")
     # 8 KV heads x 4 row blocks x 8 splits = 256 units of 128 rows, fp32 O + fp32 (max, sum)
-    assert bench.split_partial_bytes(cfg, 8) == 256 * 128 * (8 + 128 * 4)
-    assert bench.split_partial_bytes(cfg, 1) == 0
+    assert bench.split_partial_bytes(cfg, 8, 128) == 256 * 128 * (8 + 128 * 4)
+    assert bench.split_partial_bytes(cfg, 1, 128) == 0
     tiny = W.config("tiny_fp32")
-    assert bench.split_partial_bytes(tiny, 2) == 1 * 1 * 2 * 128 * (8 + 64 * 4)
-    # bs = 8 verify: 64 query rows per KV head, so each unit writes two of its four tiles
+    assert bench.split_partial_bytes(tiny, 2, 128) == 1 * 1 * 2 * 128 * (8 + 64 * 4)
+    # bs = 8 verify: one 64-row block per KV head, both of its tiles written
     bs8 = W.config("llama3_70b_verify_bs8")
-    assert bench.split_partial_bytes(bs8, 16) == 8 * 16 * 64 * (8 + 128 * 4)
+    assert bench.split_partial_bytes(bs8, 16, 64) == 8 * 16 * 64 * (8 + 128 * 4)
+    # 8B verify in 64-row blocks: 8 KV heads x 4 blocks x 8 splits = 256 units of 64 rows
+    assert bench.split_partial_bytes(W.config("llama3_8b_verify"), 8, 64) == 256 * 64 * (8 + 128 * 4)
+    # 300 rows per KV head in 64-row blocks: the last block's 44 rows take two 32-row tiles
+    ragged = dict(n_q_heads=12, n_kv_heads=4, head_dim=128, dtype="bf16", n_tree=100)
+    assert bench.split_partial_bytes(ragged, 4, 64) == 4 * 4 * (4 * 64 + 64) * (8 + 128 * 4)
 
 
 def test_counter_summary_derives_rocprof_utilisations(tmp_path):

@@ -250,6 +250,11 @@ def edge_cases():
         # 45 units (15 splits): a row block's splits are not all on one XCD,
         # so the hand-off between them crosses L2 caches
         "cross_xcd_groups": (dict(n_q_heads=6, n_kv_heads=3, head_dim=128, dtype="bf16", prefix=4000), rnd(20)),
+        # 128-row blocks (64-row ones would exceed 256 units) with a ragged
+        # last block: 32 rows (the sparse mapping inside the dense instance)
+        # and 96 rows
+        "dense_last_block_32": (dict(n_q_heads=64, n_kv_heads=8, head_dim=128, dtype="bf16", prefix=2000), rnd(36)),
+        "dense_last_block_96": (dict(n_q_heads=64, n_kv_heads=8, head_dim=128, dtype="bf16", prefix=2000), rnd(60)),
     }
 
 

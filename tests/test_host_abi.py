@@ -164,6 +164,45 @@ def test_workspace_and_split_plan():
     assert lib.ta_tree_attn_num_splits(ctypes.byref(tiny), 2, 128, 15) == 1
     assert lib.ta_tree_attn_workspace_bytes(ctypes.byref(tiny), 2, 128, 15) == 0
     assert lib.ta_tree_attn_workspace_bytes(ctypes.byref(d), 60, 8192, 64) == 0  # invalid -> 0
+    assert lib.ta_tree_attn_rows_block_rows(ctypes.byref(d), 60, 8192, 64, 0) == 0
+    assert lib.ta_tree_attn_rows_block_rows(ctypes.byref(d), 64, 8192, 8, 0) == 64   # 64 rows per KV head
+    assert lib.ta_tree_attn_rows_block_rows(ctypes.byref(tiny), 2, 128, 15, 0) == 128  # fp32
+
+
+def _units_from_workspace(ws, head_dim):
+    """Work units (workgroups) of a split launch, read back from its workspace
+    size: 4096 x 16 B of counters, then (max, sum) and partial-output rows
+    for 128 rows per unit, each part 256-byte aligned."""
+    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    size = lambda u: up(up(4096 * 16 + u * 128 * 8) + u * 128 * head_dim * 4)  # noqa: E731
+    units = [u for u in range(1, 1 << 17) if size(u) == ws]
+    assert len(units) == 1
+    return units[0]
+
+
+@pytest.mark.parametrize("name,n_kv,group,prefix,n_tree,dtype,block", [
+    ("8B verify: 128-row blocks fill only 128 units", 8, 4, 2048, 64, ta.TA_BF16, 64),
+    ("70B verify, TP = 4 share", 2, 8, 8192, 64, ta.TA_BF16, 64),
+    ("ragged: 300 rows per KV head", 4, 3, 1000, 100, ta.TA_BF16, 64),
+    ("70B verify: 256 units at 128 rows already", 8, 8, 8192, 64, ta.TA_BF16, 128),
+    ("fp32 keeps 128-row blocks", 2, 8, 8192, 64, ta.TA_F32, 128),
+    ("64-row blocks would give 280 units (last block 32 rows)", 8, 8, 2000, 36, ta.TA_BF16, 128),
+    ("256 units at 128 rows (last block 96 rows)", 8, 8, 2000, 60, ta.TA_BF16, 128),
+])
+def test_row_block_choice(name, n_kv, group, prefix, n_tree, dtype, block):
+    """bf16 launches whose 128-row blocks leave CUs idle (fewer than 256
+    workgroups once the splits are capped at 4 stages each) take 64-row
+    blocks instead; the unit count read back from the workspace size is
+    KV heads x row blocks x splits for the block size chosen."""
+    lib = ta.lib()
+    d = _desc(H=n_kv, C=prefix + n_tree, dtype=dtype)
+    splits = lib.ta_tree_attn_num_splits(ctypes.byref(d), n_kv * group, prefix, n_tree)
+    ws = lib.ta_tree_attn_workspace_bytes(ctypes.byref(d), n_kv * group, prefix, n_tree)
+    assert splits > 1 and ws > 0
+    assert lib.ta_tree_attn_rows_block_rows(ctypes.byref(d), n_kv * group, prefix, n_tree, 0) == block
+    blocks = -(-group * n_tree // block)
+    assert _units_from_workspace(ws, 128) == n_kv * blocks * splits, name
+    assert n_kv * blocks * splits <= 256
 
 
 def test_kv_reroot_rejects_before_enqueueing():

@@ -10,7 +10,8 @@ library has not been built, importing works but every call raises.
     tree_verify(logits, tokens, parent) -> (choice, result) device tensors
     tree_expand(logits, path_scores, k) -> (leaf, token, score) device tensors
     kv_reroot(k_cache, v_cache, prefix_len, parent, accepted_path, surviving_nodes)
-    tree_attn_workspace_bytes / tree_attn_num_splits / tree_ancestor_bits / kv_reroot_plan
+    tree_attn_workspace_bytes / tree_attn_num_splits / tree_attn_block_rows /
+    tree_ancestor_bits / kv_reroot_plan
 
 Layouts: q and out ``[n_tree, n_q_heads, head_dim]``; caches
 ``[n_layers, n_kv_heads, capacity, head_dim]``; all contiguous, same dtype
@@ -84,6 +85,9 @@ def lib():
                                                             ctypes.c_int32]
             L.ta_tree_attn_rows_num_splits.restype = ctypes.c_int32
             L.ta_tree_attn_rows_num_splits.argtypes = [_CP, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                       ctypes.c_int32]
+            L.ta_tree_attn_rows_block_rows.restype = ctypes.c_int32
+            L.ta_tree_attn_rows_block_rows.argtypes = [_CP, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                        ctypes.c_int32]
             L.ta_tree_attn_rows_noalloc.restype = ctypes.c_int
             L.ta_tree_attn_rows_noalloc.argtypes = [ctypes.c_void_p, _CP, ctypes.c_int32, ctypes.c_int32, _I32P,
@@ -201,6 +205,11 @@ def tree_attn_workspace_bytes(k_cache, v_cache, n_q_heads, prefix_len, n_tree, q
 def tree_attn_num_splits(k_cache, v_cache, n_q_heads, prefix_len, n_tree, q_first=0):
     desc = _cache_desc(k_cache, v_cache, need_device=False)
     return lib().ta_tree_attn_rows_num_splits(ctypes.byref(desc), n_q_heads, prefix_len, n_tree, q_first)
+
+
+def tree_attn_block_rows(k_cache, v_cache, n_q_heads, prefix_len, n_tree, q_first=0):
+    desc = _cache_desc(k_cache, v_cache, need_device=False)
+    return lib().ta_tree_attn_rows_block_rows(ctypes.byref(desc), n_q_heads, prefix_len, n_tree, q_first)
 
 
 def tree_attn(q, k_cache, v_cache, prefix_len, parent, layer=0, out=None, workspace=None, q_first=0):

@@ -110,6 +110,14 @@ int32_t ta_tree_attn_rows_num_splits(const ta_kv_cache* cache, int32_t n_q_heads
   return p.splits > 0 ? p.splits : 1;
 }
 
+int32_t ta_tree_attn_rows_block_rows(const ta_kv_cache* cache, int32_t n_q_heads, int32_t prefix_len,
+                                     int32_t n_tree, int32_t q_first) {
+  clear_error();
+  AttnPlan p;
+  if (plan_tree_attn(cache, n_q_heads, prefix_len, n_tree, q_first, &p) != TA_OK) return 0;
+  return p.block_rows;
+}
+
 int32_t ta_tree_attn_num_splits(const ta_kv_cache* cache, int32_t n_q_heads, int32_t prefix_len,
                                 int32_t n_tree) {
   return ta_tree_attn_rows_num_splits(cache, n_q_heads, prefix_len, n_tree, 0);
@@ -179,6 +187,7 @@ ta_status tree_attn_rows_impl(const void* q, const ta_kv_cache* cache, int32_t l
   a.prefix_len = prefix_len;
   a.total_keys = plan.total_keys;
   a.rows_per_head = plan.rows_per_head;
+  a.block_rows = plan.block_rows;
   a.row_blocks = plan.row_blocks;
   a.splits = plan.splits;
   a.n_tiles = plan.n_tiles;

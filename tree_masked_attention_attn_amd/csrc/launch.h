@@ -29,6 +29,7 @@ struct TreeAttnArgs {
   int32_t prefix_len;
   int32_t total_keys;       // prefix_len + n_tree
   int32_t rows_per_head;    // group * (n_tree - q_first)
+  int32_t block_rows;       // query rows per row block: 128, or 64 (bf16, see the plan)
   int32_t row_blocks;
   int32_t splits;
   int32_t n_tiles;

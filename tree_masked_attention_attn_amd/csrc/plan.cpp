@@ -108,6 +108,10 @@ ta_status plan_tree_attn(const ta_kv_cache* cache, int32_t n_q_heads, int32_t pr
   p.head_dim = cache->head_dim;
   p.group = group;
   p.rows_per_head = group * (n_tree - q_first);
+  // bf16 heads of at most 64 rows run the sparse-block instance, whose blocks
+  // are 64 rows; 128 rows otherwise (64 below when CUs would stay idle)
+  const bool small = cache->dtype == TA_BF16 && p.rows_per_head <= kRowsPerBlock / 2;
+  p.block_rows = small ? kRowsPerBlock / 2 : kRowsPerBlock;
   p.row_blocks = (p.rows_per_head + kRowsPerBlock - 1) / kRowsPerBlock;
   p.total_keys = prefix_len + n_tree;
   p.n_tiles = (p.total_keys + kKeyTile - 1) / kKeyTile;
@@ -121,10 +125,29 @@ ta_status plan_tree_attn(const ta_kv_cache* cache, int32_t n_q_heads, int32_t pr
   // fp32 one two (one for head_dim 128).
   const bool one_per_cu = cache->dtype == TA_BF16 || cache->head_dim == 128;
   const int32_t target = one_per_cu ? kTargetUnits / 2 : kTargetUnits;
-  int32_t want = (target + base_units - 1) / base_units;
-  int32_t cap = std::max(1, p.n_tiles / kMinTilesPerSplit);
-  p.splits = std::max(1, std::min(std::min(want, cap), kMaxSplits));
+  const int32_t cap = std::max(1, p.n_tiles / kMinTilesPerSplit);
+  auto splits_for = [&](int32_t base) {
+    const int32_t want = (target + base - 1) / base;
+    return std::max(1, std::min(std::min(want, cap), kMaxSplits));
+  };
+  p.splits = splits_for(base_units);
   p.n_units = base_units * p.splits;
+  // bf16: when the split cap leaves CUs idle, blocks of 64 rows double the
+  // units without adding partial rows (each block's two real row tiles run
+  // one wave per SIMD, the other four waves only load); 128 rows otherwise.
+  if (cache->dtype == TA_BF16 && p.rows_per_head > kRowsPerBlock / 2 && p.n_units < target) {
+    const int32_t half = kRowsPerBlock / 2;
+    const int32_t blocks = (p.rows_per_head + half - 1) / half;
+    const int32_t splits = splits_for(cache->n_kv_heads * blocks);
+    if (static_cast<int64_t>(cache->n_kv_heads) * blocks * splits > p.n_units &&
+        static_cast<int64_t>(cache->n_kv_heads) * blocks * splits <= target) {
+      p.block_rows = half;
+      p.row_blocks = blocks;
+      p.splits = splits;
+      p.n_units = cache->n_kv_heads * blocks * splits;
+    }
+  }
+  const int32_t base_groups = cache->n_kv_heads * p.row_blocks;
   // The kernels split a workgroup id into (group, split) and a group into
   // (KV head, row block) with a multiply-high division that is exact for
   // dividends below 2^17.
@@ -132,7 +155,7 @@ ta_status plan_tree_attn(const ta_kv_cache* cache, int32_t n_q_heads, int32_t pr
     return fail(TA_ERR_UNSUPPORTED, std::to_string(p.n_units) + " work units (KV heads x row blocks x splits) "
                                     "exceed " + std::to_string(kMaxUnits - 1));
   if (p.splits > 1) {
-    if (base_units > kMaxGroups)
+    if (base_groups > kMaxGroups)
       return fail(TA_ERR_UNSUPPORTED, "more than " + std::to_string(kMaxGroups) +
                                           " (KV head, row block) groups need a split");
     const size_t units = static_cast<size_t>(p.n_units);

@@ -27,12 +27,13 @@ ta_status ancestor_bits(const int32_t* parent, int32_t n, uint64_t* lo, uint64_t
 ta_status check_cache(const ta_kv_cache* c, bool need_ptrs);
 
 // Tiling of one ta_tree_attn call. A "work unit" is one workgroup:
-// (KV head g, block of kRowsPerBlock query rows, prefix split s).
+// (KV head g, block of block_rows query rows, prefix split s).
 struct AttnPlan {
   int32_t head_dim = 0;
   int32_t group = 0;           // query heads per KV head
   int32_t rows_per_head = 0;   // group * (n_tree - q_first): query rows per KV head
-  int32_t row_blocks = 0;      // ceil(rows_per_head / kRowsPerBlock)
+  int32_t block_rows = 0;      // query rows per row block: kRowsPerBlock, or half of it (bf16)
+  int32_t row_blocks = 0;      // ceil(rows_per_head / block_rows)
   int32_t total_keys = 0;      // prefix_len + n_tree
   int32_t n_tiles = 0;         // ceil(total_keys / kKeyTile): key stages
   int32_t splits = 0;          // key-range splits per row block
@@ -42,8 +43,8 @@ struct AttnPlan {
   // that calls of different shapes share never finds partial data of an
   // earlier call where it expects a counter.
   size_t ws_cnt_offset = 0;    // int32 x4 per group: arrivals, pad, give-up bits, pad
-  size_t ws_ml_offset = 0;     // fp32 (max, sum) pairs [units][kRowsPerBlock][2]
-  size_t ws_o_offset = 0;      // partial outputs [units][kRowsPerBlock][head_dim], fp32
+  size_t ws_ml_offset = 0;     // fp32 (max, sum) pairs [units][kRowsPerBlock][2] (block_rows used)
+  size_t ws_o_offset = 0;      // partial outputs [units][kRowsPerBlock][head_dim], fp32 (block_rows used)
   size_t ws_bytes = 0;
 };
 

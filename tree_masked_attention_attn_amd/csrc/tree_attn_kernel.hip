@@ -359,8 +359,9 @@ __device__ __forceinline__ void put_ml(const PartialSink& k, int r, float m, flo
 //    or 4 groups of one (row, column) sit in adjacent lanes and are combined
 //    with lane exchanges, so a slice of 128/S rows still takes one batch of
 //    8 loads per thread instead of S/8 batches in a row.
-template <typename T, int D, int NTH>
+template <typename T, int D, int NTH, int BR>  // BR: rows per row block
 __device__ void merge_rows(const TreeAttnArgs& a, int grp, int g, int rb, int r0, int r1, int tid) {
+  constexpr int block = BR;
   constexpr int C4 = D / 4;  // chunks of 4 values per row
   constexpr int MB = 8;      // splits per load batch
   const int S = a.splits;
@@ -397,7 +398,7 @@ __device__ void merge_rows(const TreeAttnArgs& a, int grp, int g, int rb, int r0
     }
   };
   auto put = [&](int br, int c, float L, f32x4 acc) {
-    const int hrow = rb * kBlockRows + br;
+    const int hrow = rb * block + br;
     const int nd = div_small(hrow, a.group, a.group_rcp), hd = g * a.group + hrow - nd * a.group;
     store4<T>(static_cast<T*>(a.out) + ((size_t)nd * a.n_q_heads + hd) * D + 4 * c, acc * (1.f / L));
   };
@@ -406,7 +407,7 @@ __device__ void merge_rows(const TreeAttnArgs& a, int grp, int g, int rb, int r0
     static_assert(RPP * C4 == NTH && (RPP & (RPP - 1)) == 0, "threads per pass");
     const int c = tid / RPP;
     for (int br = r0 + tid % RPP; br < r1; br += RPP) {
-      if (rb * kBlockRows + br >= a.rows_per_head) continue;
+      if (rb * block + br >= a.rows_per_head) continue;
       float M = kNegInf, L = 0.f;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
       combine(br, c, 0, M, L, acc);
@@ -446,7 +447,7 @@ __device__ void merge_rows(const TreeAttnArgs& a, int grp, int g, int rb, int r0
       L = lower ? L * sa + L2 * sb : L2 * sb + L * sa;
       M = Mn;
     }
-    if (live && h == 0 && rb * kBlockRows + br < a.rows_per_head) put(br, c, L, acc);
+    if (live && h == 0 && rb * block + br < a.rows_per_head) put(br, c, L, acc);
   }
 }
 
@@ -478,9 +479,10 @@ __device__ void merge_rows(const TreeAttnArgs& a, int grp, int g, int rb, int r0
 //    twice is written twice with the same bytes, and a bit left set for a
 //    later call only makes that call's last arrival merge a slice that is
 //    already complete.
-template <typename T, int D, int NTH>
+template <typename T, int D, int NTH, int BR>  // BR as for merge_rows
 __device__ void split_handoff(const TreeAttnArgs& a, int* s_flags, int* s_mask, int grp, int g, int rb,
                               int split, int tid) {
+  constexpr int block = BR;
   // Every wave waits for its own partial stores to complete before the
   // barrier (a workgroup barrier does not wait for global stores by itself),
   // so the whole workgroup's partials have been performed once thread 0
@@ -521,16 +523,16 @@ __device__ void split_handoff(const TreeAttnArgs& a, int* s_flags, int* s_mask, 
   }
   __syncthreads();
   const int flag = *s_flags;
-  if (flag) merge_rows<T, D, NTH>(a, grp, g, rb, div_small(split * kBlockRows, a.splits, a.splits_rcp),
-                                      div_small((split + 1) * kBlockRows, a.splits, a.splits_rcp), tid);
+  if (flag) merge_rows<T, D, NTH, BR>(a, grp, g, rb, div_small(split * block, a.splits, a.splits_rcp),
+                                          div_small((split + 1) * block, a.splits, a.splits_rcp), tid);
   if (flag == 2) {
     if (tid == 0) *s_mask = static_cast<int>(others & ~(1u << split));
     __syncthreads();
     const unsigned marked = static_cast<unsigned>(*s_mask);
     for (int j = 0; j < a.splits; ++j)
       if ((marked >> j) & 1u)
-        merge_rows<T, D, NTH>(a, grp, g, rb, div_small(j * kBlockRows, a.splits, a.splits_rcp),
-                                  div_small((j + 1) * kBlockRows, a.splits, a.splits_rcp), tid);
+        merge_rows<T, D, NTH, BR>(a, grp, g, rb, div_small(j * block, a.splits, a.splits_rcp),
+                                      div_small((j + 1) * block, a.splits, a.splits_rcp), tid);
   }
 }
 
@@ -669,7 +671,7 @@ void tree_attn_kernel(const TreeAttnArgs a) {
                     f32x4{o[dt][4 * jq], o[dt][4 * jq + 1], o[dt][4 * jq + 2], o[dt][4 * jq + 3]});
     if (half == 0) put_ml(sink, rloc, m_ref, l_tot);
   }
-  split_handoff<T, D, kThreads>(a, &s_flags, &s_taken, grp, g, rb, split, tid);
+  split_handoff<T, D, kThreads, kBlockRows>(a, &s_flags, &s_taken, grp, g, rb, split, tid);
 }
 
 // ============================================================================
@@ -845,8 +847,8 @@ __device__ __forceinline__ void bf_dma_slot(unsigned slot, const __bf16* head, i
 // 64-127 into their own area; rows past the head's rows read as zeros) and,
 // from the kernel arguments, the ancestor table.
 template <int D, int NW>
-__device__ __forceinline__ void bf_dma_q_anc(unsigned lds, const TreeAttnArgs& a, int g, int rb, int wave,
-                                             int lane) {
+__device__ __forceinline__ void bf_dma_q_anc(unsigned lds, const TreeAttnArgs& a, int g, int rb, int brows,
+                                             int wave, int lane) {
   using G = BfGeo<D>;
   const int qbytes = (a.n_tree - a.q_first) * a.n_q_heads * G::ROWB;
   const i32x4 r = bf_rsrc(a.q, qbytes);
@@ -857,7 +859,7 @@ __device__ __forceinline__ void bf_dma_q_anc(unsigned lds, const TreeAttnArgs& a
       const int op = o * NW + wave;
       const int p = op * 64 + lane;
       const int row = p / G::CPR, ch = (p % G::CPR) ^ bf_ksw<D>(row);
-      const int hr = rb * kBlockRows + 64 * h + row;
+      const int hr = rb * brows + 64 * h + row;  // h = 1 of a 64-row block: the next block, unused
       int off = qbytes;  // out of range: zeros
       if (hr < a.rows_per_head) {
         const int nd = div_small(hr, a.group, a.group_rcp);
@@ -1271,7 +1273,9 @@ void tree_attn_bf16_kernel(const TreeAttnArgs a) {
   // pairs a wave of real rows with a padding wave, and padding waves only
   // load: every real wave then has its SIMD to itself. Otherwise a SIMD
   // holds the two key halves of one row group.
-  const int block_rows = min(a.rows_per_head - rb * kBlockRows, kBlockRows);
+  // rows per row block: 64 in the sparse-block instance, 128 otherwise
+  constexpr int brows = SPARSE ? kBlockRows / 2 : kBlockRows;
+  const int block_rows = min(a.rows_per_head - rb * brows, brows);
   const bool sparse = SPARSE || block_rows <= 64;
   const int rg = sparse ? 2 * (wave >> 2) + ((wave & 3) >> 1) : wave % RW;
   const int kh = sparse ? wave & 1 : wave / RW;
@@ -1305,7 +1309,7 @@ void tree_attn_bf16_kernel(const TreeAttnArgs a) {
   // The first burst carries only what the first two iterations read first
   // (Q, the ancestors, K0, K1, V0); K2, V1 and V2 follow once Q and K0 have
   // landed, so that those do not queue behind the whole chip's later stages.
-  bf_dma_q_anc<D, NW>(lds0, a, g, rb, wave, lane);
+  bf_dma_q_anc<D, NW>(lds0, a, g, rb, brows, wave, lane);
   dma_k(0);
   if (n > 1) dma_k(1);
   dma_v(0);
@@ -1321,8 +1325,9 @@ void tree_attn_bf16_kernel(const TreeAttnArgs a) {
   bool row_ok[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    const int row = rb * kBlockRows + 32 * (NT * rg + nt) + l32;
-    row_ok[nt] = row < a.rows_per_head;
+    const int row = rb * brows + 32 * (NT * rg + nt) + l32;
+    // a row of this block (a padding tile of a 64-row block would be the next block's rows)
+    row_ok[nt] = row < a.rows_per_head && (!SPARSE || 32 * (NT * rg + nt) + l32 < block_rows);
     node[nt] = row_ok[nt] ? div_small(row, a.group, a.group_rcp) : 0;
     head[nt] = g * a.group + (row_ok[nt] ? row - node[nt] * a.group : 0);
 #pragma unroll
@@ -1558,7 +1563,7 @@ void tree_attn_bf16_kernel(const TreeAttnArgs a) {
   if (kh == 0) merge_halves(std::integral_constant<int, 0>{});
   else merge_halves(std::integral_constant<int, 1>{});
   if (a.splits == 1) return;
-  split_handoff<__bf16, D, kBfThreads<NT>>(a, &s_flags, &s_taken, grp, g, rb, split, tid);
+  split_handoff<__bf16, D, kBfThreads<NT>, brows>(a, &s_flags, &s_taken, grp, g, rb, split, tid);
 }
 
 }  // namespace
@@ -1567,9 +1572,10 @@ hipError_t launch_tree_attn(const TreeAttnArgs& a, int32_t dtype, int32_t head_d
                             hipStream_t stream) {
   const dim3 grid(a.n_units), block(kThreads);
   if (dtype == 1) {
-    // one row block of at most 64 query rows per KV head: the instance
-    // built for sparse blocks only
-    const bool sparse = a.rows_per_head <= 64;
+    // 64-row blocks (every head of at most 64 query rows, and the plan's
+    // choice where 128-row blocks leave CUs idle): the sparse-block instance
+    if (a.block_rows != kBlockRows && a.block_rows != kBlockRows / 2) return hipErrorInvalidValue;
+    const bool sparse = a.block_rows == kBlockRows / 2;
     const dim3 bf(kBfThreads<TA_BF16_NT>);
     if (head_dim == 128) {
       if (sparse) hipLaunchKernelGGL((tree_attn_bf16_kernel<128, TA_BF16_NT, true>), grid, bf, 0, stream, a);
