@@ -254,7 +254,7 @@ def edge_cases():
         # last block: 32 rows (the sparse mapping inside the dense instance)
         # and 96 rows
         "dense_last_block_32": (dict(n_q_heads=64, n_kv_heads=8, head_dim=128, dtype="bf16", prefix=2000), rnd(36)),
-        "dense_last_block_96": (dict(n_q_heads=64, n_kv_heads=8, head_dim=128, dtype="bf16", prefix=2000), rnd(60)),
+        "dense_last_block_96": (dict(n_q_heads=64, n_kv_heads=8, head_dim=128, dtype="bf16", prefix=4000), rnd(60)),
     }
 
 

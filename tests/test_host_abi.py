@@ -185,15 +185,20 @@ def _units_from_workspace(ws, head_dim):
     ("70B verify, TP = 4 share", 2, 8, 8192, 64, ta.TA_BF16, 64),
     ("ragged: 300 rows per KV head", 4, 3, 1000, 100, ta.TA_BF16, 64),
     ("70B verify: 256 units at 128 rows already", 8, 8, 8192, 64, ta.TA_BF16, 128),
+    ("draft loop: 256 units either way, 64-row splits of 9 stages", 8, 4, 4096, 64, ta.TA_BF16, 64),
+    ("70B heads, P = 2048: 256 units either way, 9 stages", 8, 8, 2048, 64, ta.TA_BF16, 64),
+    ("70B heads, P = 4096: 256 units either way, 17 stages", 8, 8, 4096, 64, ta.TA_BF16, 128),
     ("fp32 keeps 128-row blocks", 2, 8, 8192, 64, ta.TA_F32, 128),
     ("64-row blocks would give 280 units (last block 32 rows)", 8, 8, 2000, 36, ta.TA_BF16, 128),
-    ("256 units at 128 rows (last block 96 rows)", 8, 8, 2000, 60, ta.TA_BF16, 128),
+    ("256 units either way, 64-row splits of 16 stages (last block 96 rows)", 8, 8, 4000, 60, ta.TA_BF16, 128),
 ])
 def test_row_block_choice(name, n_kv, group, prefix, n_tree, dtype, block):
     """bf16 launches whose 128-row blocks leave CUs idle (fewer than 256
     workgroups once the splits are capped at 4 stages each) take 64-row
-    blocks instead; the unit count read back from the workspace size is
-    KV heads x row blocks x splits for the block size chosen."""
+    blocks instead, and so do launches where both give 256 units and the
+    64-row splits carry at most 12 stages; the unit count read back from the
+    workspace size is KV heads x row blocks x splits for the block size
+    chosen."""
     lib = ta.lib()
     d = _desc(H=n_kv, C=prefix + n_tree, dtype=dtype)
     splits = lib.ta_tree_attn_num_splits(ctypes.byref(d), n_kv * group, prefix, n_tree)

@@ -132,19 +132,22 @@ ta_status plan_tree_attn(const ta_kv_cache* cache, int32_t n_q_heads, int32_t pr
   };
   p.splits = splits_for(base_units);
   p.n_units = base_units * p.splits;
-  // bf16: when the split cap leaves CUs idle, blocks of 64 rows double the
-  // units without adding partial rows (each block's two real row tiles run
-  // one wave per SIMD, the other four waves only load); 128 rows otherwise.
-  if (cache->dtype == TA_BF16 && p.rows_per_head > kRowsPerBlock / 2 && p.n_units < target) {
+  // bf16: 64-row blocks (each block's two real row tiles run one wave per
+  // SIMD, the other four waves only load) where they give more units than
+  // 128-row blocks without passing the target, or as many units with
+  // splits of at most kMaxStagesHalfBlocks stages: there half the partial
+  // rows and longer splits outweigh the slower loop of a one-wave SIMD.
+  if (cache->dtype == TA_BF16 && p.rows_per_head > kRowsPerBlock / 2 && p.n_units <= target) {
     const int32_t half = kRowsPerBlock / 2;
     const int32_t blocks = (p.rows_per_head + half - 1) / half;
     const int32_t splits = splits_for(cache->n_kv_heads * blocks);
-    if (static_cast<int64_t>(cache->n_kv_heads) * blocks * splits > p.n_units &&
-        static_cast<int64_t>(cache->n_kv_heads) * blocks * splits <= target) {
+    const int64_t units = static_cast<int64_t>(cache->n_kv_heads) * blocks * splits;
+    const bool short_splits = (p.n_tiles + splits - 1) / splits <= kMaxStagesHalfBlocks;
+    if ((units > p.n_units || (units == p.n_units && short_splits)) && units <= target) {
       p.block_rows = half;
       p.row_blocks = blocks;
       p.splits = splits;
-      p.n_units = cache->n_kv_heads * blocks * splits;
+      p.n_units = static_cast<int32_t>(units);
     }
   }
   const int32_t base_groups = cache->n_kv_heads * p.row_blocks;

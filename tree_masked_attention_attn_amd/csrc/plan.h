@@ -64,6 +64,11 @@ constexpr int32_t kMinTilesPerSplit = 4;
 // bs=8 verify step and a one-row-block draft expansion: 16 splits beat 32 by
 // 10 to 25 percent).
 constexpr int32_t kMaxSplits = 16;
+// 64-row blocks at the unit count of 128-row ones only while their splits
+// stay this short. Measured on MI355X, per-launch events, 64- against
+// 128-row blocks at 256 units: 9 stages per split -5 to -6% (head_dim 64
+// and 128), 17 stages +0% (128) and +4% (64), 25 to 33 stages +12%.
+constexpr int32_t kMaxStagesHalfBlocks = 12;
 constexpr int32_t kMaxGroups = 4096;   // (KV head, row block) groups with counters
 constexpr int32_t kMaxUnits = 1 << 17; // the kernels' index divisions are exact below this
 constexpr int32_t kGroupWords = 4;     // arrival count, unused, give-up bits, unused
