@@ -255,6 +255,9 @@ def edge_cases():
         # and 96 rows
         "dense_last_block_32": (dict(n_q_heads=64, n_kv_heads=8, head_dim=128, dtype="bf16", prefix=2000), rnd(36)),
         "dense_last_block_96": (dict(n_q_heads=64, n_kv_heads=8, head_dim=128, dtype="bf16", prefix=4000), rnd(60)),
+        # 256 units with either block size and 9 stages per 64-row split: 64-row blocks
+        "half_blocks_equal_units": (dict(n_q_heads=64, n_kv_heads=8, head_dim=128, dtype="bf16", prefix=2048),
+                                    rnd(64)),
     }
 
 
