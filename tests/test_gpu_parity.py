@@ -274,6 +274,43 @@ def test_edge_shapes(case):
     check_close(gpu_attn(x), ref_attn(x, shape["n_kv_heads"]), shape["dtype"], case)
 
 
+def random_shapes(count=24, seed=2026):
+    """Seeded bf16 shapes spanning the planner's choices: 64- and 128-row
+    blocks, 1 to 16 splits, ragged last blocks and stages, frontier rows,
+    random, deep and chain trees of 1 to 128 nodes."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(count):
+        hkv, g = int(rng.choice([1, 2, 4, 8])), int(rng.choice([1, 2, 3, 4, 8]))
+        n = int(rng.integers(1, 129))
+        shape = dict(n_q_heads=hkv * g, n_kv_heads=hkv, head_dim=int(rng.choice([64, 128])), dtype="bf16",
+                     prefix=int(rng.integers(0, 3000)) if rng.random() < 0.9 else 0,
+                     q_first=int(rng.integers(0, n)) if rng.random() < 0.3 else 0)
+        kind = str(rng.choice(["random", "deep", "chain"]))
+        if kind == "random":
+            parent = [-1] + [int(rng.integers(-1, i)) for i in range(1, n)]
+        elif kind == "deep":
+            parent = deep_tree(rng, n)
+        else:
+            parent = [-1] + list(range(n - 1))
+        cases.append((shape, parent, kind))
+    return cases
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_random_shapes(i):
+    shape, parent, kind = random_shapes()[i]
+    n = len(parent)
+    cfg = dict(shape, n_tree=n, capacity=shape["prefix"] + n + 8, seed=0, value_scale=0.5, tree="random")
+    x = W.make_inputs(cfg, np.random.default_rng(1000 + i))
+    x["parent"] = parent
+    qf = shape["q_first"]
+    block = ta.tree_attn_block_rows(x["k"], x["v"], shape["n_q_heads"], shape["prefix"], n, qf)
+    splits = ta.tree_attn_num_splits(x["k"], x["v"], shape["n_q_heads"], shape["prefix"], n, qf)
+    say(f"[random {i}] {shape} n={n} {kind}: {block}-row blocks, {splits} splits")
+    check_close(gpu_attn(x), ref_attn(x, shape["n_kv_heads"]), "bf16", f"random {i}")
+
+
 def test_layer_selection_in_multilayer_cache():
     cfg = W.config("llama3_8b_verify", prefix=700)
     say("[layers] 3-layer cache, layer 2")

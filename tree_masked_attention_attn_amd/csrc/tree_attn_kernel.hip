@@ -12,7 +12,9 @@
 // barrier.
 //
 // Work decomposition (both kernels). A work unit is one workgroup: one KV
-// head x one block of 128 of its query rows (row r of a head is frontier
+// head x one block of 128 of its query rows (64 in the bf16 sparse-block
+// instance, which the plan picks for heads of at most 64 rows and where
+// 128-row blocks would leave CUs idle; row r of a head is frontier
 // node q_first + r / G, query head g*G + r % G, so a GQA group's rows share
 // every K/V tile) x one contiguous range of 64-key stages (a "split" of
 // [0, prefix_len + n_tree)). Splits spread the few KV heads over the 256 CUs;
@@ -687,10 +689,11 @@ void tree_attn_kernel(const TreeAttnArgs a) {
 //    softmax of stage s, the other the softmax first. Between the workgroup
 //    barriers that start each iteration the matrix core works for one wave
 //    while the VALU works for the other.
-//  * A block of at most 64 query rows (the sparse instance) pairs each wave
-//    of real rows with a padding wave that only loads, so every real wave
-//    has its SIMD to itself; its softmax is then free to interleave with its
-//    MFMAs.
+//  * A block of at most 64 query rows (every block of the sparse instance,
+//    whose blocks are 64 rows, and the last block of a head in the dense
+//    one) pairs each wave of real rows with a padding wave that only loads,
+//    so every real wave has its SIMD to itself; its softmax is then free to
+//    interleave with its MFMAs.
 //  * NT (32-row tiles per wave) is 1. NT = 2, one wave per SIMD holding two
 //    row tiles so that each K or V fragment feeds two MFMAs, was measured as
 //    a variant of this kernel (its DMA split over four waves): same outputs,
@@ -710,9 +713,10 @@ typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-// NT: 32-row MFMA tiles per wave. A workgroup always covers 128 rows and both
-// 32-key halves of each stage: 8 / NT waves (NT = 1: two waves per SIMD;
-// NT = 2: one wave per SIMD, each K or V fragment feeding two MFMAs).
+// NT: 32-row MFMA tiles per wave. A workgroup's waves cover 128 rows (of
+// which a 64-row block uses two tiles) and both 32-key halves of each stage:
+// 8 / NT waves (NT = 1: two waves per SIMD; NT = 2: one wave per SIMD, each
+// K or V fragment feeding two MFMAs).
 #ifndef TA_BF16_NT
 #define TA_BF16_NT 1
 #endif
@@ -843,9 +847,10 @@ __device__ __forceinline__ void bf_dma_slot(unsigned slot, const __bf16* head, i
   for (int o = 0; o < G::KOPS; ++o) bf_dma16(r, slot + (o * NW + wave) * 1024, off, o * NW * 1024);
 }
 
-// DMA the block's 128 query rows (K layout; rows 0-63 into K slot 3, rows
-// 64-127 into their own area; rows past the head's rows read as zeros) and,
-// from the kernel arguments, the ancestor table.
+// DMA 128 query rows from the block's first (K layout; rows 0-63 into K
+// slot 3, rows 64-127 into their own area; rows past the head's rows read as
+// zeros; in a 64-row block rows 64-127 are the next block's and go unused)
+// and, from the kernel arguments, the ancestor table.
 template <int D, int NW>
 __device__ __forceinline__ void bf_dma_q_anc(unsigned lds, const TreeAttnArgs& a, int g, int rb, int brows,
                                              int wave, int lane) {
