@@ -2,6 +2,7 @@
 the rocprofv3 summary tools (on synthetic profiler output). No GPU needed."""
 
 import csv
+import ctypes
 import json
 import os
 import sqlite3
@@ -17,6 +18,7 @@ import workloads as W
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
 import bench  # noqa: E402
+import tree_masked_attention_attn_amd as ta  # noqa: E402
 
 
 def test_more_than_one_gpu_is_refused_before_touching_a_gpu():
@@ -120,6 +122,33 @@ def test_split_partial_bytes_match_the_traffic_excess_model():
     # 300 rows per KV head in 64-row blocks: the last block's 44 rows take two 32-row tiles
     ragged = dict(n_q_heads=12, n_kv_heads=4, head_dim=128, dtype="bf16", n_tree=100)
     assert bench.split_partial_bytes(ragged, 4, 64) == 4 * 4 * (4 * 64 + 64) * (8 + 128 * 4)
+
+
+@pytest.mark.parametrize("name", ["llama3_70b_verify", "qwen2_72b_32k_verify", "llama3_8b_verify",
+                                  "llama3_70b_verify_bs8"])
+def test_committed_traffic_is_the_algorithmic_bytes_plus_the_partials_both_ways(name):
+    """The FETCH_SIZE/WRITE_SIZE records in profiles/ against the traffic
+    model: q, out and every K/V byte once, the split partials written once
+    and read back once (within 5%). These shapes keep each KV head's row
+    blocks on one XCD; the TP = 4 share, whose heads span four XCDs, fetches
+    its K/V once per XCD and is not one of them."""
+    cfg = W.config(name)
+    path = bench.traffic_file(cfg)
+    if not os.path.exists(path):
+        pytest.skip(f"no traffic record for {name}")
+    with open(path) as f:
+        rec = json.loads(f.read().split("```json", 1)[1].split("```", 1)[0])
+    parent, _ = W.make_tree(cfg, np.random.default_rng(cfg["seed"]))
+    nbytes, _, _ = bench.tree_attn_work(cfg, parent)
+    es = 2 if cfg["dtype"] == "bf16" else 4
+    desc = ta.ta_kv_cache(1 << 40, 1 << 41, 1, cfg["n_kv_heads"], cfg["capacity"], cfg["head_dim"],
+                          ta.TA_BF16 if es == 2 else ta.TA_F32)
+    qf = cfg.get("q_first", 0)
+    lib = ta.lib()
+    splits = lib.ta_tree_attn_rows_num_splits(ctypes.byref(desc), cfg["n_q_heads"], cfg["prefix"], cfg["n_tree"], qf)
+    block = lib.ta_tree_attn_rows_block_rows(ctypes.byref(desc), cfg["n_q_heads"], cfg["prefix"], cfg["n_tree"], qf)
+    model = nbytes + 2 * bench.split_partial_bytes(cfg, splits, block)
+    assert abs(rec["traffic_bytes"] - model) <= 0.05 * model, (rec["traffic_bytes"], model)
 
 
 def test_counter_summary_derives_rocprof_utilisations(tmp_path):
